@@ -1,0 +1,74 @@
+"""Planted mistakes in a copy of the oracle (CPU only) must each fail a pin.
+
+Each mutant is the oracle's C source with one plausible slip (a wrong rounding
+tie, a leaked future row, a flipped tie-break, an off-by-one window, a dropped
+scale, a wrong sign ...).  The copy is compiled to a temporary library and the
+pin suite is run against it; at least one pin must fail.  This shows the pins
+are strong enough to notice such a slip in the real oracle.
+"""
+import inspect
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "csa2_oracle.c")
+
+MUTANTS = {
+    "rounding ties away from zero": ("return (q % 2 == 0) ? q : q + 1;", "return q + 1;"),
+    "rounding truncates": ("if (2 * r > n) return q + 1;", "if (2 * r > 2 * n) return q + 1;"),
+    "partial block reads future rows": ("if (last > t) last = t;", ""),
+    "tie goes to the higher id": ("return (a->id < b->id) ? -1 : (a->id > b->id);",
+                                  "return (a->id > b->id) ? -1 : (a->id < b->id);"),
+    "own block not eligible": ("int n_elig = t / B + 1;", "int n_elig = (t + 1) / B;"),
+    "query's own position excluded": ("if (p > t) break;", "if (p >= t) break;"),
+    "score sign flipped": ("s += (int64_t)a[c] * (int64_t)b[c];", "s -= (int64_t)a[c] * (int64_t)b[c];"),
+    "pool one short": ("n_pool = P;", "n_pool = P - 1;"),
+    "window one short": ("int nw = (W > 0) ? t - w0 + 1 : 0;", "int nw = (W > 0) ? t - w0 : 0;"),
+    "scale dropped on main logits": ("logit[i] = scale * acc;", "logit[i] = acc;"),
+    "window logits use main keys": ("load_elem(k_swa, elem, (size_t)r * D + c);",
+                                    "load_elem(k_main, elem, (size_t)(r + swa_first) * D + c);"),
+    "value index transposed": ("load_elem(v_main, elem, (size_t)topk[i] * D + c);",
+                               "load_elem(v_main, elem, (size_t)c * D + topk[i] % D);"),
+    "normaliser ignores the window": ("for (int i = 0; i < cnt + nw; i++) {\n            logit[i] = exp(logit[i] - m);    /* now the unnormalised weight */\n            z += logit[i];",
+                                      "for (int i = 0; i < cnt + nw; i++) {\n            logit[i] = exp(logit[i] - m);    /* now the unnormalised weight */\n            if (i < cnt) z += logit[i];"),
+    "lse drops the max": ("lse[h] = m + log(z);", "lse[h] = log(z);"),
+}
+
+
+def _pin_calls():
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        if params:
+            argnames, values = params[0].args
+            argnames = [a.strip() for a in argnames.split(",")]
+            for v in values:
+                yield name, (lambda fn=fn, v=v, a=argnames: fn(**dict(zip(a, v))))
+        else:
+            yield name, fn
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(mutant, tmp_path):
+    old, new = MUTANTS[mutant]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique/found: {old!r}"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O1", "-std=c11", "-shared", "-fPIC", "-o", str(so), str(path), "-lm"])
+    caught = []
+    with oracle.using(str(so)):
+        for name, call in _pin_calls():
+            try:
+                call()
+            except Exception:            # assertion or rejected input: the pin noticed
+                caught.append(name)
+                break
+    assert caught, f"no pin noticed the planted mistake: {mutant}"
