@@ -1,0 +1,204 @@
+/*
+ * csa2.h -- C ABI of the CSA2 sparse-attention library for MI355X (gfx950).
+ *
+ * The method (page "DeepSeek V4.1 Flash", k-a.in, and the forum summary on
+ * artofsm.art):
+ *   - "Hierarchical indexer" key fact, and the forum summary's description of
+ *     a hierarchical sparse indexer that narrows the attention candidates down
+ *     to blocks: an indexer first scores blocks of B tokens and keeps a pool of
+ *     at most P blocks, so at most P*B candidate tokens are scored;
+ *   - "Sparse attention" key fact: each query then attends to its Top-K
+ *     main-KV entries plus a sliding window of the W most recent tokens;
+ *   - "CSA2 with cross-layer reuse" mode table: a Full layer computes its own
+ *     keys and fresh indices, a Reindex layer reuses the keys but selects with
+ *     its own indexer query, a Reuse layer reuses keys and indices; every mode
+ *     has its own main query and its own sliding-window K/V.
+ * The pages leave the scores open; this library fixes them:
+ *   - token score  s_p = <q_idx, k_idx[p]>, int8 x int8 summed exactly in int32;
+ *   - block score  s_j = <q_idx, kb_j>, where kb_j is the per-dimension mean of
+ *     block j's k_idx rows that are visible to the query (positions <= t),
+ *     rounded to the nearest integer with ties to even;
+ *   - every selection ranks by score, higher first, and breaks ties by the
+ *     lower block id / lower position, so the selected set is unique;
+ *   - attention is one softmax per head over the selected main entries and the
+ *     window entries together, logits scale * <q, k>, scale = 1/sqrt(D) unless
+ *     given.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device data are device pointers (hipMalloc'd or from a
+ *     framework allocator) owned by the caller.  The library allocates nothing
+ *     and keeps no pointer after the call returns.
+ *   - Arrays are dense, row-major, with the shapes given; int32 indices.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; the call returns after the launches, without waiting.
+ *   - Arguments are checked before anything is launched; a bad argument
+ *     returns its status code and leaves every buffer untouched.  A failed
+ *     launch returns CSA2_E_HIP.  Faults inside a kernel surface at the
+ *     caller's next synchronisation.  Nothing is printed, nothing is thrown.
+ *   - Positions: sequence s holds positions 0..T-1 in every cache; a query row
+ *     i belongs to sequence q_seq[i] at position q_pos[i] (0 <= q_pos[i] < T)
+ *     and sees positions <= q_pos[i] only (the pages: both stacks are causal).
+ *     Device-side values of q_seq/q_pos are trusted: out-of-range values are
+ *     undefined behaviour, not an error code.
+ *   - Workspace: `ws` is device memory of at least csa2_workspace_bytes()
+ *     bytes that is zero-filled before its first use (csa2_workspace_init or
+ *     any zero fill).  Every call leaves its counters at zero again, so one
+ *     workspace serves any number of calls issued in order on one stream.
+ *     Calls that run concurrently need separate workspaces.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_E_NULL = 1,        /* a required pointer is NULL                        */
+    CSA2_E_SHAPE = 2,       /* a size is out of range or sizes disagree          */
+    CSA2_E_DTYPE = 3,       /* unknown element type                              */
+    CSA2_E_UNSUPPORTED = 4, /* valid but not built (e.g. head_dim not 64 or 128) */
+    CSA2_E_ALIGN = 5,       /* a device pointer is not 16-byte aligned           */
+    CSA2_E_WORKSPACE = 6,   /* workspace missing or smaller than required        */
+    CSA2_E_HIP = 7,         /* a HIP runtime call or kernel launch failed        */
+    CSA2_E_MODE = 8         /* unknown layer mode, or a mode/argument mismatch   */
+} csa2_status;
+
+typedef enum {
+    CSA2_FULL = 0,      /* own keys: update block keys, fresh pool + Top-K, attend */
+    CSA2_REINDEX = 1,   /* shared keys, own q_idx: fresh pool + Top-K, attend      */
+    CSA2_REUSE = 2,     /* shared keys and indices: attend only                    */
+    CSA2_SWA = 3        /* sliding-window-only layer: attend to the window alone   */
+} csa2_mode;
+
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
+
+/* Selection and attention sizes (one struct shared by every call). */
+typedef struct {
+    int32_t block;     /* B: tokens per block; 1..16                              */
+    int32_t pool;      /* P: blocks kept by the hierarchical pass; >= 1           */
+    int32_t top_k;     /* K: selected main-KV entries; 0 (window only) .. P*B     */
+    int32_t window;    /* W: sliding window length; 0 .. 1024; K + W >= 1         */
+    int32_t d_idx;     /* indexer dimension: 32 or 64                             */
+    int32_t n_heads;   /* H: query heads sharing one main-KV head; 1 .. 128       */
+    int32_t head_dim;  /* D: 64 or 128                                            */
+    int32_t dtype;     /* csa2_dtype of Q, K, V and the output                    */
+    float scale;       /* logit scale; 0 means 1/sqrt(head_dim)                  */
+} csa2_cfg;
+/* Limits: P*B <= 16384 candidates per query (the pages' cap on candidates
+ * scored by an indexer); T <= 2^24 positions. */
+
+int32_t csa2_abi_version(void);
+const char *csa2_status_str(int32_t status);
+
+/* Bytes of workspace needed by any call below for n_q query rows against
+ * caches of T positions and n_layers layers per group call.  Writes *bytes. */
+int32_t csa2_workspace_bytes(const csa2_cfg *cfg, int32_t n_q, int32_t T, int32_t n_layers,
+                             size_t *bytes);
+
+/* Zero-fills `bytes` of device memory at `ws` with a kernel (safe to record
+ * into a HIP graph). */
+int32_t csa2_workspace_init(void *ws, size_t bytes, void *stream);
+
+/* Block keys (the block-level indexer keys the hierarchical pass scores).
+ * For each sequence s < n_seq and each block j in [blk_begin, blk_end) that
+ * is complete ((j+1)*B <= T):
+ *     k_blk[s][j][c] = round_half_even(mean over p in [jB, jB+B) of k_idx[s][p][c])
+ *   k_idx : device int8 [n_seq][T][d_idx]
+ *   k_blk : device int8 [n_seq][T/B][d_idx]  (only blocks in range are written)
+ * A Full layer builds all blocks once (prefill) and, in decode, the block that
+ * the newest token completes.  Incomplete blocks are never stored: the
+ * selection calls compute the key of a query's own block from k_idx. */
+int32_t csa2_build_block_keys(const csa2_cfg *cfg, const int8_t *k_idx, int32_t n_seq, int32_t T,
+                              int32_t blk_begin, int32_t blk_end, int8_t *k_blk, void *stream);
+
+/* Hierarchical block pass.  For query row i at position t = q_pos[i] in
+ * sequence s = q_seq[i], the eligible blocks are j = 0 .. t/B (each holds at
+ * least one visible token).  If there are at most P of them, all are pooled;
+ * otherwise the P with the highest block score, ties to the lower block id.
+ * Blocks j < t/B take their key from k_blk; block t/B (the query's own, maybe
+ * incomplete) takes the rounded mean of its rows jB..t of k_idx.
+ *   q_idx   : device int8  [n_q][d_idx]
+ *   q_seq, q_pos : device int32 [n_q]
+ *   k_idx   : device int8  [n_seq][T][d_idx]
+ *   k_blk   : device int8  [n_seq][T/B][d_idx], blocks < t/B filled
+ *   blk_ids : device int32 [n_q][P] out: pooled block ids ascending, then -1
+ *   blk_cnt : device int32 [n_q]    out: number of pooled blocks           */
+int32_t csa2_index_blocks(const csa2_cfg *cfg, int32_t n_q, const int8_t *q_idx,
+                          const int32_t *q_seq, const int32_t *q_pos, const int8_t *k_idx,
+                          const int8_t *k_blk, int32_t n_seq, int32_t T, int32_t *blk_ids,
+                          int32_t *blk_cnt, void *ws, size_t ws_bytes, void *stream);
+
+/* Token Top-K.  The candidates of query row i are the visible positions
+ * (p <= t) of its pooled blocks.  If there are at most K, all are selected;
+ * otherwise the K with the highest token score, ties to the lower position.
+ *   blk_ids, blk_cnt : as written by csa2_index_blocks
+ *   topk     : device int32 [n_q][K] out: selected positions ascending, then -1
+ *   topk_cnt : device int32 [n_q]    out: number selected                   */
+int32_t csa2_topk_tokens(const csa2_cfg *cfg, int32_t n_q, const int8_t *q_idx,
+                         const int32_t *q_seq, const int32_t *q_pos, const int8_t *k_idx,
+                         int32_t n_seq, int32_t T, const int32_t *blk_ids, const int32_t *blk_cnt,
+                         int32_t *topk, int32_t *topk_cnt, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* Sparse attention for a group of n_layers layers that share one index set
+ * and one main K/V cache (the layer-group call; n_layers = 1 is one layer).
+ * For layer l, query row i, head h: one softmax over
+ *   - main entries p in topk[i][0 .. topk_cnt[i]) with k_main/v_main rows of
+ *     sequence q_seq[i] (skipped when topk is NULL: a window-only layer), and
+ *   - window positions max(0, t-W+1) .. t with this layer's own k_swa/v_swa,
+ *     whose row r holds position swa_first + r.
+ *   q      : device [n_layers][n_q][H][D]             (dtype)
+ *   k_main, v_main : device [n_seq][T][D]             (dtype)
+ *   k_swa, v_swa   : device [n_layers][n_seq][swa_len][D] (dtype)
+ *   topk, topk_cnt : device int32 [n_q][K], [n_q], or both NULL
+ *   out    : device [n_layers][n_q][H][D]             (dtype) out
+ *   lse    : device fp32 [n_layers][n_q][H] out (natural-log normaliser) or NULL
+ * Window positions outside [swa_first, swa_first + swa_len) are not attended:
+ * callers supply rows covering every query's window. */
+int32_t csa2_attend_group(const csa2_cfg *cfg, int32_t n_layers, int32_t n_q, const void *q,
+                          const int32_t *q_seq, const int32_t *q_pos, const void *k_main,
+                          const void *v_main, int32_t n_seq, int32_t T, const void *k_swa,
+                          const void *v_swa, int32_t swa_first, int32_t swa_len,
+                          const int32_t *topk, const int32_t *topk_cnt, void *out, float *lse,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* One layer: csa2_attend_group with n_layers = 1. */
+int32_t csa2_attend(const csa2_cfg *cfg, int32_t n_q, const void *q, const int32_t *q_seq,
+                    const int32_t *q_pos, const void *k_main, const void *v_main, int32_t n_seq,
+                    int32_t T, const void *k_swa, const void *v_swa, int32_t swa_first,
+                    int32_t swa_len, const int32_t *topk, const int32_t *topk_cnt, void *out,
+                    float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* A CSA2 layer group in one call: the first layer's mode decides the
+ * selection work, then all n_layers layers attend with the shared indices
+ * (the mode table of "CSA2 with cross-layer reuse": a Full or Reindex layer
+ * followed by the Reuse layers that take its indices).
+ *   CSA2_FULL    : csa2_build_block_keys over [blk_update_begin, T/B) (pass
+ *                  blk_update_begin >= T/B to skip), csa2_index_blocks,
+ *                  csa2_topk_tokens, csa2_attend_group
+ *   CSA2_REINDEX : csa2_index_blocks + csa2_topk_tokens with this layer's q_idx
+ *                  over the shared k_idx/k_blk (read only), csa2_attend_group
+ *   CSA2_REUSE   : csa2_attend_group with the given topk/topk_cnt (read only)
+ *   CSA2_SWA     : csa2_attend_group with no main entries (topk ignored)
+ * blk_ids/blk_cnt/topk/topk_cnt are outputs for FULL/REINDEX, inputs for
+ * REUSE.  Shapes as in the calls above. */
+int32_t csa2_layer_group(const csa2_cfg *cfg, int32_t mode, int32_t n_layers, int32_t n_q,
+                         const int8_t *q_idx, const int32_t *q_seq, const int32_t *q_pos,
+                         const int8_t *k_idx, int8_t *k_blk, int32_t blk_update_begin,
+                         int32_t n_seq, int32_t T, const void *q, const void *k_main,
+                         const void *v_main, const void *k_swa, const void *v_swa,
+                         int32_t swa_first, int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt,
+                         int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *ws,
+                         size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,230 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Indices must be identical and outputs within 2e-2 + 1e-2*|ref|.  Cases cover
+the five workload shapes (full size where the oracle can take every query,
+sampled rows for the 8K prefill), scaled versions that span several tiles with
+ragged tails, tie-heavy draws, and the edge cases of the method: the pool
+covering every block, fewer candidates than K, the query's own partial block,
+no window, window-only layers, several head groups, fp32 and bf16, d_idx 32.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import assert_close, assert_index_equal, compare_run
+from top_kv_selection_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "toy16.json")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from top_kv_selection_amd import binding, pipeline
+    return binding, pipeline
+
+
+def run_gpu(pipeline, wl):
+    dw = pipeline.upload(wl)
+    pipeline.build_cache(dw)
+    pipeline.run(dw)
+    torch.cuda.synchronize()
+    return pipeline.outputs(dw)
+
+
+def check(lib, cfg, seed=None, rows=None, int_range=(-127, 127)):
+    _, pipeline = lib
+    print(f"case {cfg.name} S={cfg.n_seq} T={cfg.ctx} P={cfg.pool} K={cfg.top_k} W={cfg.window} "
+          f"layers={cfg.layers} seed={seed} rows={'all' if rows is None else len(rows)}", flush=True)
+    wl = W.generate(cfg, seed=seed, int_range=int_range)
+    got = run_gpu(pipeline, wl)
+    ref = oracle.run_layers(wl, rows=rows)
+    return compare_run(got, ref, cfg, rows=rows, what=cfg.name)
+
+
+# ------------------------------------------------------------------ the five workloads
+def test_tiny_full_fp32_all_queries(lib):
+    check(lib, W.CONFIGS["tiny_full_fp32"])
+
+
+def test_decode_full_32k(lib):
+    check(lib, W.CONFIGS["decode_full_32k"])
+
+
+def test_decode_group_128k(lib):
+    check(lib, W.CONFIGS["decode_group_128k"])
+
+
+def test_decoder_pattern_64k(lib):
+    check(lib, W.CONFIGS["decoder_pattern_64k"])
+
+
+def test_prefill_8k_sampled_rows(lib):
+    cfg = W.CONFIGS["prefill_8k"]
+    rng = np.random.default_rng(4)
+    edges = [0, 1, 7, 8, 9, 63, 64, 127, 128, 129, 511, 512, 513, 1023, 4095, 8190, 8191]
+    rows = np.unique(np.concatenate([edges, rng.choice(cfg.n_q, 80, replace=False)]))
+    check(lib, cfg, rows=rows)
+
+
+# ------------------------------------------------------------------ scaled cases
+def test_decode_scaled_ragged_context(lib):
+    """Context not a multiple of the block: the own block is partial; several
+    workgroups per query, pool smaller than the eligible blocks."""
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=5, ctx=5003, pool=96, top_k=100, window=37)
+    check(lib, cfg, seed=21)
+
+
+def test_decode_scaled_tie_heavy(lib):
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=3, ctx=8192, pool=128, top_k=200, window=64,
+                   layers=("full", "reuse", "reuse"))
+    check(lib, cfg, seed=22, int_range=(-2, 2))
+
+
+def test_decode_pool_covers_everything(lib):
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=4, ctx=1000, pool=2048)
+    check(lib, cfg, seed=23)
+
+
+def test_decode_fewer_candidates_than_k(lib):
+    # 300 visible tokens < K = 512 <= P*B: every candidate is selected
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=4, ctx=300, pool=64, top_k=512)
+    check(lib, cfg, seed=24)
+
+
+def test_prefill_scaled_all_rows(lib):
+    """Every position of a 700-token prompt: own partial blocks, pool active
+    past 8*64 tokens, K larger than the prefix for early rows."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=700, pool=64, top_k=96, window=40,
+                   layers=("full", "reuse", "swa"))
+    check(lib, cfg, seed=25)
+
+
+def test_prefill_scaled_tie_heavy_d32(lib):
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=600, d_idx=32, pool=24, top_k=50, window=16,
+                   layers=("full", "reindex"))
+    check(lib, cfg, seed=26, int_range=(-1, 1))
+
+
+def test_no_window(lib):
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=4096, pool=64, top_k=128, window=0)
+    check(lib, cfg, seed=27)
+
+
+def test_two_head_groups_and_generic_kernels(lib):
+    # H = 32: two 16-head groups on the MFMA path
+    check(lib, W.scaled(W.CONFIGS["decode_full_32k"], n_seq=2, ctx=3000, pool=64, top_k=128, n_heads=32), seed=28)
+    # D = 64 bf16 and H = 8: the generic kernel
+    check(lib, W.scaled(W.CONFIGS["decode_full_32k"], n_seq=2, ctx=3000, pool=64, top_k=128, n_heads=8,
+                        head_dim=64), seed=29)
+
+
+def test_decoder_pattern_scaled(lib):
+    cfg = W.scaled(W.CONFIGS["decoder_pattern_64k"], n_seq=2, ctx=6000, pool=200)
+    check(lib, cfg, seed=30)
+
+
+def test_fp32_decode_long(lib):
+    cfg = W.scaled(W.CONFIGS["tiny_full_fp32"], n_seq=2, ctx=20000, decode=True, pool=300, top_k=128, window=64)
+    check(lib, cfg, seed=31)
+
+
+# ------------------------------------------------------------------ single calls
+def test_block_keys_bit_exact(lib):
+    B, _ = lib
+    rng = np.random.default_rng(32)
+    for blk, d in ((8, 64), (2, 32), (16, 64), (5, 32)):
+        k = rng.integers(-128, 128, size=(3, 203, d), dtype=np.int8)
+        T = k.shape[1]
+        cfg = B.Cfg(block=blk, pool=4, top_k=8, window=4, d_idx=d)
+        kd = torch.from_numpy(k).cuda()
+        kb = torch.full((3, T // blk, d), 77, dtype=torch.int8, device="cuda")
+        B.csa2_build_block_keys(cfg, kd, kb, 1, T // blk - 1)
+        got = kb.cpu().numpy()
+        for s in range(3):
+            for j in range(T // blk):
+                want = oracle.block_key(k[s], blk, j, T - 1) if 1 <= j < T // blk - 1 else np.full(d, 77, np.int8)
+                assert np.array_equal(got[s, j], want), (blk, d, s, j)
+
+
+def test_golden_toy_selection(lib):
+    B, _ = lib
+    g = json.load(open(GOLDEN))
+    k = np.zeros((1, g["T"], 32), np.int8)
+    k[0, :, 0] = g["k_idx"]
+    kd = torch.from_numpy(k).cuda()
+    for case in g["cases"]:
+        P = case.get("pool_override", g["pool"])
+        cfg = B.Cfg(block=g["block"], pool=P, top_k=g["top_k"], window=g["window"], d_idx=32)
+        q = np.zeros((1, 32), np.int8)
+        q[0, 0] = case["q_idx"]
+        qd = torch.from_numpy(q).cuda()
+        seq = torch.zeros(1, dtype=torch.int32, device="cuda")
+        pos = torch.full((1,), case["t"], dtype=torch.int32, device="cuda")
+        kb = torch.zeros((1, g["T"] // g["block"], 32), dtype=torch.int8, device="cuda")
+        B.csa2_build_block_keys(cfg, kd, kb)
+        ids = torch.empty((1, P), dtype=torch.int32, device="cuda")
+        cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+        tk = torch.empty((1, g["top_k"]), dtype=torch.int32, device="cuda")
+        tc = torch.empty(1, dtype=torch.int32, device="cuda")
+        ws = B.new_workspace(cfg, 1, g["T"])
+        B.csa2_index_blocks(cfg, qd, seq, pos, kd, kb, ids, cnt, ws)
+        B.csa2_topk_tokens(cfg, qd, seq, pos, kd, ids, cnt, tk, tc, ws)
+        torch.cuda.synchronize()
+        assert ids[0, :cnt.item()].tolist() == case["pool"], case["name"]
+        assert tk[0, :tc.item()].tolist() == case["topk"], case["name"]
+
+
+def test_reuse_equals_attend_with_full_indices(lib):
+    """The layer group's Reuse layers equal single attend calls that take the
+    Full layer's indices (and the group call equals per-layer calls)."""
+    B, pipeline = lib
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=4, ctx=9000, pool=256)
+    wl = W.generate(cfg, seed=33)
+    dw = pipeline.upload(wl)
+    pipeline.build_cache(dw)
+    pipeline.run(dw)
+    grp = dw.groups[0]
+    for j in range(len(grp.layers)):
+        out = torch.empty_like(grp.out[j])
+        lse = torch.empty_like(grp.lse[j])
+        B.csa2_attend(dw.lcfg, grp.q[j].contiguous(), dw.q_seq, dw.q_pos, dw.k_main, dw.v_main,
+                      grp.k_swa[j].contiguous(), grp.v_swa[j].contiguous(), cfg.swa_first, dw.topk[0],
+                      dw.topk_cnt[0], out, lse, dw.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, grp.out[j]), j
+        assert torch.equal(lse, grp.lse[j]), j
+
+
+def test_deterministic_bitwise(lib):
+    B, pipeline = lib
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=3, ctx=20000, pool=512)
+    wl = W.generate(cfg, seed=34)
+    dw = pipeline.upload(wl)
+    pipeline.build_cache(dw)
+    outs = []
+    for _ in range(3):
+        pipeline.run(dw)
+        torch.cuda.synchronize()
+        outs.append((dw.groups[0].out.clone(), dw.topk[0].clone(), dw.blk_ids[0].clone()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+
+
+def test_empty_query_batch_is_a_no_op(lib):
+    B, _ = lib
+    cfg = B.Cfg(pool=64)
+    e8 = torch.empty((0, 64), dtype=torch.int8, device="cuda")
+    e32 = torch.empty(0, dtype=torch.int32, device="cuda")
+    k = torch.zeros((1, 1024, 64), dtype=torch.int8, device="cuda")
+    kb = torch.zeros((1, 128, 64), dtype=torch.int8, device="cuda")
+    ids = torch.empty((0, 64), dtype=torch.int32, device="cuda")
+    B.csa2_index_blocks(cfg, e8, e32, e32, k, kb, ids, e32, None)
+    torch.cuda.synchronize()

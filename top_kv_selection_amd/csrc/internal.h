@@ -1,0 +1,87 @@
+// internal.h -- host-side declarations shared by the CSA2 translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kSelectThreads = 512;     // threads of a selection workgroup
+constexpr int kTargetWorkgroups = 512;  // ~2 per CU on a 256-CU MI355X
+constexpr int kAttendKeysPerIter = 128; // keys one attention workgroup takes per step
+constexpr int kMaxCandidates = 16384;   // P*B cap: candidates one query may score
+
+struct BlockKeysParams {
+    const int8_t *k_idx;
+    int8_t *k_blk;
+    int T, B, nblk, blk_begin, blk_end;
+};
+
+struct IndexParams {
+    const int8_t *q_idx;
+    const int32_t *q_seq, *q_pos;
+    const int8_t *k_idx, *k_blk;
+    int T, B, P, n_q, G, chunk, nblk;
+    uint32_t *ws_keys;
+    int64_t ws_stride;
+    uint32_t *ws_cnt;
+    int32_t *blk_ids, *blk_cnt;
+};
+
+struct TopkParams {
+    const int8_t *q_idx;
+    const int32_t *q_seq, *q_pos;
+    const int8_t *k_idx;
+    const int32_t *blk_ids, *blk_cnt;
+    int T, B, P, K, n_q, G, chunk;
+    uint32_t *ws_keys;
+    int64_t ws_stride;
+    uint32_t *ws_cnt;
+    int32_t *topk, *topk_cnt;
+};
+
+struct AttendParams {
+    const void *q;
+    const int32_t *q_seq, *q_pos;
+    const void *k_main, *v_main;
+    int n_seq, T;
+    const void *k_swa, *v_swa;
+    int swa_first, swa_len;
+    const int32_t *topk, *topk_cnt;
+    int K, W, n_q, n_layers, H;
+    float scale_log2;       // logit scale times log2(e)
+    void *out;
+    float *lse;
+    float *ws_part;         // split partials (MFMA path, n_splits > 1)
+    uint32_t *ws_cnt;
+    int n_splits, keys_per_split, n_q_pad;
+};
+
+// Work split of one selection launch: G workgroups per query, `chunk` items each.
+struct SelectPlan {
+    int G, chunk;
+    bool split;       // scores go through the workspace (G > 1 or too many for LDS)
+    size_t key_bytes; // workspace bytes for the scores
+};
+
+struct AttendPlan {
+    bool mfma;
+    int n_splits, keys_per_split;
+    size_t part_bytes;
+};
+
+SelectPlan plan_index(int n_q, int T, int B, int P, int d_idx);
+SelectPlan plan_topk(int n_q, int B, int P, int K, int d_idx);
+AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dtype);
+
+hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hipStream_t st);
+hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &plan, int d_idx,
+                               hipStream_t st);
+hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &plan, int d_idx,
+                              hipStream_t st);
+hipError_t launch_attend(const AttendParams &p, const AttendPlan &plan, int D, int dtype,
+                         hipStream_t st);
+hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t st);
+
+}  // namespace csa2

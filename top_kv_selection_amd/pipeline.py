@@ -1,0 +1,192 @@
+"""Runs a workload's CSA2 layers on the GPU through the C ABI.
+
+Host-side plumbing only: device buffers come from torch, and each layer group
+(an indexing or window-only layer plus the Reuse layers that share its indices)
+is one ``csa2_layer_group`` call, issued in model order on the current stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .workloads import Config, Workload
+
+
+def _dev(a: np.ndarray, device, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(device)
+
+
+def _real(a: np.ndarray, cfg: Config, device):
+    return _dev(a, device, torch.bfloat16 if cfg.dtype == "bf16" else None)
+
+
+@dataclass
+class Group:
+    mode: str
+    layers: list
+    q: torch.Tensor                 # [L][n_q][H][D]
+    k_swa: torch.Tensor             # [L][S][swa_len][D]
+    v_swa: torch.Tensor
+    out: torch.Tensor               # [L][n_q][H][D]
+    lse: torch.Tensor               # [L][n_q][H]
+    q_idx: torch.Tensor = None      # [n_q][d] for full/reindex
+    index_of: int = -1              # group whose indices a reuse group takes
+
+
+@dataclass
+class DeviceWorkload:
+    cfg: Config
+    lcfg: B.Cfg
+    q_seq: torch.Tensor
+    q_pos: torch.Tensor
+    k_idx: torch.Tensor
+    k_blk: torch.Tensor
+    k_main: torch.Tensor
+    v_main: torch.Tensor
+    groups: list
+    # one index set per indexing group
+    blk_ids: dict = field(default_factory=dict)
+    blk_cnt: dict = field(default_factory=dict)
+    topk: dict = field(default_factory=dict)
+    topk_cnt: dict = field(default_factory=dict)
+    ws: torch.Tensor = None
+
+
+def upload(wl: Workload, device="cuda", q_idx=None, q=None) -> DeviceWorkload:
+    """Copies a workload to the GPU, grouping per-layer tensors by layer group.
+    ``q_idx``/``q`` optionally replace the workload's queries (fresh replicas)."""
+    cfg = wl.cfg
+    q_idx = wl.q_idx if q_idx is None else q_idx
+    q = wl.q if q is None else q
+    lcfg = B.cfg_of(cfg)
+    S, T, d = wl.k_idx.shape
+    k_idx = _dev(wl.k_idx, device)
+    dw = DeviceWorkload(cfg, lcfg, _dev(wl.q_seq, device), _dev(wl.q_pos, device), k_idx,
+                        torch.zeros((S, T // cfg.block, d), dtype=torch.int8, device=device),
+                        _real(wl.k_main, cfg, device), _real(wl.v_main, cfg, device), [])
+    tdt = lcfg.torch_dtype
+    for mode, layers in cfg.groups():
+        grp = Group(mode, layers,
+                    _real(np.stack([q[l] for l in layers]), cfg, device),
+                    _real(np.stack([wl.k_swa[l] for l in layers]), cfg, device),
+                    _real(np.stack([wl.v_swa[l] for l in layers]), cfg, device),
+                    torch.empty((len(layers), cfg.n_q, cfg.n_heads, cfg.head_dim), dtype=tdt, device=device),
+                    torch.empty((len(layers), cfg.n_q, cfg.n_heads), dtype=torch.float32, device=device))
+        if mode in ("full", "reindex"):
+            grp.q_idx = _dev(q_idx[layers[0]], device)
+            g = len(dw.groups)
+            dw.blk_ids[g] = torch.empty((cfg.n_q, cfg.pool), dtype=torch.int32, device=device)
+            dw.blk_cnt[g] = torch.empty(cfg.n_q, dtype=torch.int32, device=device)
+            dw.topk[g] = torch.empty((cfg.n_q, cfg.top_k), dtype=torch.int32, device=device)
+            dw.topk_cnt[g] = torch.empty(cfg.n_q, dtype=torch.int32, device=device)
+        dw.groups.append(grp)
+    last = -1
+    for g, grp in enumerate(dw.groups):
+        if grp.mode in ("full", "reindex"):
+            last = g
+        grp.index_of = last if grp.mode != "swa" else -1
+    max_layers = max(len(g.layers) for g in dw.groups)
+    dw.ws = B.new_workspace(lcfg, cfg.n_q, T, max_layers, device)
+    return dw
+
+
+def build_cache(dw: DeviceWorkload, upto_block=None):
+    """Block keys of every complete block (the state of the cache before a step)."""
+    T = dw.k_idx.shape[1]
+    end = T // dw.cfg.block if upto_block is None else upto_block
+    B.csa2_build_block_keys(dw.lcfg, dw.k_idx, dw.k_blk, 0, end)
+
+
+def step_update_begin(dw: DeviceWorkload) -> int:
+    """First block a Full layer rebuilds inside a step: decode rebuilds the
+    block holding the newest token; prefill builds every block."""
+    T = dw.k_idx.shape[1]
+    return max(0, (T - 1) // dw.cfg.block) if dw.cfg.decode else 0
+
+
+def run(dw: DeviceWorkload):
+    """One pass of every layer group, in model order."""
+    begin = step_update_begin(dw)
+    for g, grp in enumerate(dw.groups):
+        src = grp.index_of
+        idx = src if src >= 0 else None
+        B.csa2_layer_group(
+            dw.lcfg, grp.mode, grp.q_idx, dw.q_seq, dw.q_pos, dw.k_idx, dw.k_blk, begin, grp.q,
+            dw.k_main, dw.v_main, grp.k_swa, grp.v_swa, dw.cfg.swa_first,
+            dw.blk_ids.get(idx), dw.blk_cnt.get(idx), dw.topk.get(idx), dw.topk_cnt.get(idx),
+            grp.out, grp.lse, dw.ws)
+
+
+def outputs(dw: DeviceWorkload):
+    """Host copies: per layer (out fp32, lse) and per indexing layer the index set."""
+    n_layers = dw.cfg.n_layers
+    out, lse = [None] * n_layers, [None] * n_layers
+    index = {}
+    for g, grp in enumerate(dw.groups):
+        o = grp.out.float().cpu().numpy()
+        l = grp.lse.cpu().numpy()
+        for j, layer in enumerate(grp.layers):
+            out[layer], lse[layer] = o[j], l[j]
+        if g in dw.topk:
+            index[grp.layers[0]] = {
+                "blk_ids": dw.blk_ids[g].cpu().numpy(), "blk_cnt": dw.blk_cnt[g].cpu().numpy(),
+                "topk": dw.topk[g].cpu().numpy(), "topk_cnt": dw.topk_cnt[g].cpu().numpy()}
+    return {"out": out, "lse": lse, "index": index}
+
+
+def replicate(dw: DeviceWorkload, q_idx=None, q=None) -> DeviceWorkload:
+    """A copy of ``dw`` with its own device caches (cloned on the GPU) and,
+    optionally, fresh queries from the host.  Rotating over several replicas
+    keeps one step's working set from being served by the last-level cache."""
+    cfg = dw.cfg
+    dev = dw.k_idx.device
+    new = DeviceWorkload(cfg, dw.lcfg, dw.q_seq.clone(), dw.q_pos.clone(), dw.k_idx.clone(),
+                         dw.k_blk.clone(), dw.k_main.clone(), dw.v_main.clone(), [])
+    for g, grp in enumerate(dw.groups):
+        ng = Group(grp.mode, list(grp.layers),
+                   grp.q.clone() if q is None else _real(np.stack([q[l] for l in grp.layers]), cfg, dev),
+                   grp.k_swa.clone(), grp.v_swa.clone(), torch.empty_like(grp.out), torch.empty_like(grp.lse),
+                   None, grp.index_of)
+        if grp.q_idx is not None:
+            ng.q_idx = grp.q_idx.clone() if q_idx is None else _dev(q_idx[grp.layers[0]], dev)
+            new.blk_ids[g] = torch.empty_like(dw.blk_ids[g])
+            new.blk_cnt[g] = torch.empty_like(dw.blk_cnt[g])
+            new.topk[g] = torch.empty_like(dw.topk[g])
+            new.topk_cnt[g] = torch.empty_like(dw.topk_cnt[g])
+        new.groups.append(ng)
+    new.ws = torch.zeros_like(dw.ws)
+    return new
+
+
+def algorithmic_bytes(cfg: Config) -> dict:
+    """Bytes each kernel of one step must move at minimum (every input read
+    once, every output written once), for decode workloads where every query
+    sits at t = T-1.  Per launch, summed over the step's queries."""
+    S, T, d, B, P, K, W_, H, D = (cfg.n_seq, cfg.ctx, cfg.d_idx, cfg.block, cfg.pool, cfg.top_k,
+                                  cfg.window, cfg.n_heads, cfg.head_dim)
+    esz = 4 if cfg.dtype == "f32" else 2
+    n_q = cfg.n_q
+    t = T - 1
+    n_elig = t // B + 1
+    own = t - (n_elig - 1) * B + 1
+    pool = min(P, n_elig)
+    n_cand = sum(min(B, t - j * B + 1) for j in range(n_elig - pool, n_elig)) if pool == n_elig else pool * B
+    sel = min(K, n_cand)
+    out = {}
+    out["block_keys"] = S * (B * d + d) if T % B == 0 else 0
+    out["index_blocks"] = n_q * ((n_elig - 1) * d + own * d + d + P * 4 + 4) if n_elig > P else n_q * (P * 4 + 4)
+    out["topk_tokens"] = n_q * (d + pool * 4 + 4 + n_cand * d + K * 4 + 4)
+    per_layer = min(W_, t + 1) * 2 * D * esz + 2 * H * D * esz + H * 4
+    groups = cfg.groups()
+    attend = 0
+    for mode, layers in groups:
+        main = 0 if mode == "swa" else K * 4 + 4 + sel * 2 * D * esz
+        attend += n_q * (main + len(layers) * per_layer)
+    out["attend"] = attend
+    return out
