@@ -42,8 +42,9 @@
  *     undefined behaviour, not an error code.
  *   - Workspace: `ws` is device memory of at least csa2_workspace_bytes()
  *     bytes that is zero-filled before its first use (csa2_workspace_init or
- *     any zero fill).  Every call leaves its counters at zero again, so one
- *     workspace serves any number of calls issued in order on one stream.
+ *     any zero fill).  It holds selection histograms that every call leaves
+ *     zeroed again, and scratch; one workspace serves any number of calls
+ *     issued in order on one stream when it is sized for the largest of them.
  *     Calls that run concurrently need separate workspaces.
  */
 #ifndef CSA2_H
@@ -182,7 +183,10 @@ int32_t csa2_attend(const csa2_cfg *cfg, int32_t n_q, const void *q, const int32
  * followed by the Reuse layers that take its indices).
  *   CSA2_FULL    : csa2_build_block_keys over [blk_update_begin, T/B) (pass
  *                  blk_update_begin >= T/B to skip), csa2_index_blocks,
- *                  csa2_topk_tokens, csa2_attend_group
+ *                  csa2_topk_tokens, csa2_attend_group; the block pass also
+ *                  stores into k_blk the key of every block that a query
+ *                  completes ((t+1) % B == 0), so a decode step keeps k_blk
+ *                  current without a separate launch
  *   CSA2_REINDEX : csa2_index_blocks + csa2_topk_tokens with this layer's q_idx
  *                  over the shared k_idx/k_blk (read only), csa2_attend_group
  *   CSA2_REUSE   : csa2_attend_group with the given topk/topk_cnt (read only)

@@ -228,3 +228,26 @@ def test_empty_query_batch_is_a_no_op(lib):
     ids = torch.empty((0, 64), dtype=torch.int32, device="cuda")
     B.csa2_index_blocks(cfg, e8, e32, e32, k, kb, ids, e32, None)
     torch.cuda.synchronize()
+
+
+def test_full_mode_stores_the_block_a_query_completes(lib):
+    """A decode step in Full mode writes the key of the block its newest token
+    completes (and only that block), so the next step finds k_blk current."""
+    B, pipeline = lib
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=4096, pool=64, top_k=128)
+    wl = W.generate(cfg, seed=35)
+    dw = pipeline.upload(wl)
+    nblk = cfg.ctx // cfg.block
+    pipeline.build_cache(dw, upto_block=nblk - 1)      # the last block's key is still zero
+    before = dw.k_blk.clone()
+    pipeline.run(dw)
+    torch.cuda.synchronize()
+    after = dw.k_blk.cpu().numpy()
+    for s in range(cfg.n_seq):
+        want = oracle.block_key(wl.k_idx[s], cfg.block, nblk - 1, cfg.ctx - 1)
+        assert np.array_equal(after[s, nblk - 1], want)
+    assert torch.equal(dw.k_blk[:, :nblk - 1], before[:, :nblk - 1])
+    # and the selection of that step already used the right key
+    ref = oracle.run_layers(wl)
+    got = pipeline.outputs(dw)
+    assert_index_equal(got["index"][0], ref["index"][0], what="completed block")

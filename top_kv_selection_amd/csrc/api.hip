@@ -1,10 +1,10 @@
 // api.hip -- the C ABI declared in include/csa2.h: argument checks, workspace
 // layout and the mode dispatch of a CSA2 layer group.
 //
-// Workspace layout: arrival counters at the head, scratch (scores or split
-// partials) at the tail.  Every call's counters return to zero when its
-// kernels finish, so a zero-filled workspace sized by csa2_workspace_bytes for
-// the largest call serves every call in stream order.
+// Workspace layout: state that must be zero between calls (the selection
+// histograms) at the head, scratch (scores, split records) at the tail.  The
+// kernels leave the head zeroed again, so a zero-filled workspace sized by
+// csa2_workspace_bytes for the largest call serves every call in stream order.
 #include <math.h>
 #include <algorithm>
 
@@ -42,17 +42,14 @@ int32_t check_sizes(int32_t n_q, int32_t n_seq, int32_t T)
     return CSA2_OK;
 }
 
-size_t attend_counters(const csa2_cfg *c, int n_q, int n_layers)
-{
-    return (size_t)n_q * n_layers * std::max(1, c->n_heads / 16) * sizeof(uint32_t);
-}
+
 
 struct Region {
-    uint32_t *ctr;
-    void *data;
+    uint32_t *ctr;     // head: zero between calls
+    void *data;        // tail: scratch
 };
 
-// Counters at the head, `data_bytes` at the tail of the workspace.
+// `ctr_bytes` at the head, `data_bytes` at the tail of the workspace.
 int32_t carve(void *ws, size_t ws_bytes, size_t ctr_bytes, size_t data_bytes, Region &r)
 {
     r = {nullptr, nullptr};
@@ -77,7 +74,7 @@ float scale_log2_of(const csa2_cfg *c)
 int32_t do_index(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32_t *q_seq,
                  const int32_t *q_pos, const int8_t *k_idx, const int8_t *k_blk, int32_t n_seq,
                  int32_t T, int32_t *blk_ids, int32_t *blk_cnt, void *ws, size_t ws_bytes,
-                 hipStream_t st, bool launch)
+                 hipStream_t st, bool launch, int8_t *k_blk_store = nullptr)
 {
     if (!q_idx || !q_seq || !q_pos || !k_idx || !k_blk || !blk_ids || !blk_cnt) return CSA2_E_NULL;
     if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(k_blk) || !aligned4(q_seq) ||
@@ -85,15 +82,16 @@ int32_t do_index(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int3
         return CSA2_E_ALIGN;
     const SelectPlan pl = plan_index(n_q, T, c->block, c->pool, c->d_idx);
     Region r;
-    if (int32_t e = carve(ws, ws_bytes, pl.split ? (size_t)n_q * 4 : 0, pl.key_bytes, r)) return e;
+    if (int32_t e = carve(ws, ws_bytes, select_head_bytes(n_q, pl.split), pl.key_bytes, r)) return e;
     if (!launch) return CSA2_OK;
     IndexParams p{};
     p.q_idx = q_idx; p.q_seq = q_seq; p.q_pos = q_pos; p.k_idx = k_idx; p.k_blk = k_blk;
+    p.k_blk_store = k_blk_store;
     p.T = T; p.B = c->block; p.P = c->pool; p.n_q = n_q; p.G = pl.G; p.chunk = pl.chunk;
     p.nblk = T / c->block;
     p.ws_keys = (uint32_t *)r.data;
-    p.ws_stride = (long long)(T - 1) / c->block + 1;
-    p.ws_cnt = r.ctr;
+    p.ws_stride = ((long long)(T - 1) / c->block + 1 + 3) / 4 * 4;   // rows 16-byte aligned
+    p.ws_hist = r.ctr;
     p.blk_ids = blk_ids; p.blk_cnt = blk_cnt;
     return hip_status(launch_index_blocks(p, pl, c->d_idx, st));
 }
@@ -111,7 +109,7 @@ int32_t do_topk(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32
         return CSA2_E_ALIGN;
     const SelectPlan pl = plan_topk(n_q, c->block, c->pool, c->top_k, c->d_idx);
     Region r;
-    if (int32_t e = carve(ws, ws_bytes, pl.split ? (size_t)n_q * 4 : 0, pl.key_bytes, r)) return e;
+    if (int32_t e = carve(ws, ws_bytes, select_head_bytes(n_q, pl.split), pl.key_bytes, r)) return e;
     if (!launch) return CSA2_OK;
     TopkParams p{};
     p.q_idx = q_idx; p.q_seq = q_seq; p.q_pos = q_pos; p.k_idx = k_idx;
@@ -119,8 +117,8 @@ int32_t do_topk(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32
     p.T = T; p.B = c->block; p.P = c->pool; p.K = c->top_k; p.n_q = n_q; p.G = pl.G;
     p.chunk = pl.chunk;
     p.ws_keys = (uint32_t *)r.data;
-    p.ws_stride = (long long)c->pool * c->block;
-    p.ws_cnt = r.ctr;
+    p.ws_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
+    p.ws_hist = r.ctr;
     p.topk = topk; p.topk_cnt = topk_cnt;
     return hip_status(launch_topk_tokens(p, pl, c->d_idx, st));
 }
@@ -151,8 +149,7 @@ int32_t do_attend(const csa2_cfg *c, int32_t n_layers, int32_t n_q, const void *
     const int K = has_main ? c->top_k : 0;
     const AttendPlan pl = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, K, W, c->dtype);
     Region r;
-    if (int32_t e = carve(ws, ws_bytes, pl.n_splits > 1 ? attend_counters(c, n_q, n_layers) : 0,
-                          pl.part_bytes, r))
+    if (int32_t e = carve(ws, ws_bytes, 0, pl.part_bytes, r))
         return e;
     if (!launch) return CSA2_OK;
     AttendParams p{};
@@ -166,7 +163,7 @@ int32_t do_attend(const csa2_cfg *c, int32_t n_layers, int32_t n_q, const void *
     p.n_q = n_q; p.n_layers = n_layers; p.H = c->n_heads;
     p.scale_log2 = scale_log2_of(c);
     p.out = out; p.lse = lse;
-    p.ws_part = (float *)r.data; p.ws_cnt = r.ctr;
+    p.ws_part = (float *)r.data;
     return hip_status(launch_attend(p, pl, c->head_dim, c->dtype, st));
 }
 
@@ -213,7 +210,7 @@ int32_t csa2_workspace_bytes(const csa2_cfg *c, int32_t n_q, int32_t T, int32_t 
     const SelectPlan pi = plan_index(n_q, T, c->block, c->pool, c->d_idx);
     const SelectPlan pt = plan_topk(n_q, c->block, c->pool, c->top_k, c->d_idx);
     const AttendPlan pa = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
-    const size_t ctr = std::max((size_t)n_q * 4, attend_counters(c, n_q, n_layers));
+    const size_t ctr = std::max(select_head_bytes(n_q, pi.split), select_head_bytes(n_q, pt.split));
     const size_t data = std::max({pi.key_bytes, pt.key_bytes, pa.part_bytes});
     *bytes = round_up(ctr) + round_up(data);
     return CSA2_OK;
@@ -314,7 +311,8 @@ int32_t csa2_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int3
         }
         if (selects) {
             if (int32_t e = do_index(c, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, n_seq, T, blk_ids,
-                                     blk_cnt, ws, ws_bytes, st, launch))
+                                     blk_cnt, ws, ws_bytes, st, launch,
+                                     mode == CSA2_FULL ? k_blk : nullptr))
                 return e;
             if (int32_t e = do_topk(c, n_q, q_idx, q_seq, q_pos, k_idx, T, blk_ids, blk_cnt, topk,
                                     topk_cnt, ws, ws_bytes, st, launch))

@@ -13,11 +13,10 @@
 //    online softmax in fp32 (one head per lane column), then O^T += V^T P^T.
 //    K rows go straight from HBM into MFMA operands (16 B per lane, each row
 //    read once); V rows are written transposed into LDS so that the PV operand
-//    is two 8-byte LDS reads per lane.  Decode splits a query's key list over
-//    workgroups; partial (max, sum, acc) records are merged by the last
-//    workgroup to arrive.  Workgroups of one query are numbered so that they
-//    land on one XCD (round-robin dispatch), so layers that share main rows
-//    re-read them from that XCD's L2.
+//    is two 8-byte LDS reads per lane.  One workgroup of 8 waves owns a
+//    (query, layer, head group) and a share of its key list; with few such
+//    triples (decode) the list is split over several workgroups that write
+//    (max, sum, acc) records, merged by k_attend_combine in a second launch.
 //  * k_attend_generic (fp32 or bf16, any H, D in {64, 128}): one wave per head,
 //    keys in sequence, fp32 online softmax on the vector ALU.
 #include <math.h>
@@ -121,19 +120,29 @@ __global__ __launch_bounds__(256) void k_attend_generic(AttendParams p)
 }
 
 // ============================================================ MFMA kernel
-constexpr int kVtStride = 40;                 // bf16 per V^T row in LDS (32 keys + pad)
-constexpr int kPartFloats = 16 * (2 + 128);   // one split record: 16 x (max, sum, acc[128])
+constexpr int kWaves = 8;                      // waves per workgroup, 32 keys each per step
+constexpr int kStepKeys = kWaves * 32;         // keys per workgroup step
+constexpr int kRowChunk = 2048;                // row codes staged in LDS at once
+constexpr int kVtStride = 40;                  // bf16 per V^T row in LDS (32 keys + pad)
+constexpr int kHeadRec = 4 + 128;              // split record per head: max, sum, 2 pad, acc[128]
+constexpr int kPartFloats = 16 * kHeadRec;     // one split record (16 heads), 16-byte aligned
+constexpr int kMergeBatch = 8;                 // split records loaded at once by the merge
 
 // Key slot e (0..7) of lane group g inside a 32-key step: the keys whose
 // scores this lane holds after the QK MFMA (rows 4g..4g+3 of tile 0 and of
 // tile 1).  Both PV operands use this same order along the contraction.
 __device__ __forceinline__ int slot_key(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
 
-__global__ __launch_bounds__(256) void k_attend_mfma(AttendParams p)
+// One workgroup per (query, head group of 16, layer): no split of the key
+// list, hence no cross-workgroup merge.  Workgroups are numbered query-fastest
+// with the query count padded to a multiple of 8, so with round-robin XCD
+// dispatch every layer of a query runs on one XCD and the shared main rows
+// are fetched from HBM once and then hit that XCD's L2.
+__global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[4][128 * kVtStride];
-    __shared__ float s_ml[4][16][2];
-    __shared__ uint32_t s_flag;
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[kWaves][128 * kVtStride];
+    __shared__ float s_ml[kWaves][16][2];
+    __shared__ int s_rows[kRowChunk];
 
     const int HG = p.H / 16;
     const int id = blockIdx.x;
@@ -150,6 +159,9 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendParams p)
     const int cnt = p.topk ? p.topk_cnt[i] : 0;
     const Window win = window_of(t, p.W, p.swa_first, p.swa_len);
     const int n_keys = cnt + win.nw;
+    // this workgroup's share of the key list (whole steps of kStepKeys keys)
+    const int k_begin = min(n_keys, split * p.keys_per_split);
+    const int k_end = min(n_keys, k_begin + p.keys_per_split);
 
     const uint16_t *qrow = (const uint16_t *)p.q + (((size_t)l * p.n_q + i) * p.H + hg * 16 + r16) * 128;
     const uint16_t *kmain = (const uint16_t *)p.k_main + (size_t)s * p.T * 128;
@@ -158,14 +170,17 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendParams p)
     const uint16_t *vswa = (const uint16_t *)p.v_swa + ((size_t)l * p.n_seq + s) * p.swa_len * 128;
     const int32_t *tk = p.topk ? p.topk + (size_t)i * p.K : nullptr;
 
-    // element offset of key kk's row and which cache it lives in; slots past
-    // the last key re-read the last key's row (always valid inside the loop,
-    // where n_keys >= 1) and are masked out of the softmax
-    auto key_off = [&](int kk, bool &main) -> size_t {
-        kk = min(kk, n_keys - 1);
-        main = kk < cnt;
-        if (main) return (size_t)tk[kk] * 128;
-        return (size_t)(win.w0 + (kk - cnt) - p.swa_first) * 128;
+    // Row code of key kk: main row r -> r, window row r -> -(r + 1).  Slots
+    // past the last key repeat the last key (read, then masked).
+    auto stage_rows = [&](int kc) {
+        for (int x = threadIdx.x; x < kRowChunk; x += kWaves * 64) {
+            const int kk = min(kc + x, k_end - 1);
+            s_rows[x] = (kk < cnt) ? tk[kk] : -(win.w0 + (kk - cnt) - p.swa_first) - 1;
+        }
+        __syncthreads();
+    };
+    auto row_ptr = [&](int code, const uint16_t *mbase, const uint16_t *wbase) -> const uint16_t * {
+        return code >= 0 ? mbase + (size_t)code * 128 : wbase + (size_t)(-code - 1) * 128;
     };
 
     bf16x8_t qb[4];
@@ -178,28 +193,28 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendParams p)
     for (int m = 0; m < 8; m++) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     uint16_t *vt = s_vt[w];
-    const int k_begin = split * p.keys_per_split;
-    const int k_stop = min(n_keys, k_begin + p.keys_per_split);
-    for (int kb = k_begin; kb < k_stop; kb += kAttendKeysPerIter) {
-        const int kw = kb + w * 32;
-        // K operand rows: keys kw + r16 (tile 0) and kw + 16 + r16 (tile 1)
-        bf16x8_t ka[2][4];
+
+    // K operand rows (keys kw + r16 and kw + 16 + r16) and this lane's 8 V
+    // slots (dims r16*8 .. r16*8+7) of one step, all issued back to back.
+    auto load_kv = [&](int kb, bf16x8_t (&ka)[2][4], uint4 (&vv)[8]) {
+        const int *rows = s_rows + ((kb - k_begin + w * 32) % kRowChunk);
 #pragma unroll
         for (int tau = 0; tau < 2; tau++) {
-            bool main;
-            const size_t off = key_off(kw + 16 * tau + r16, main);
-            const uint16_t *kr = (main ? kmain : kswa) + off;
+            const uint16_t *kr = row_ptr(rows[16 * tau + r16], kmain, kswa);
 #pragma unroll
             for (int kk = 0; kk < 4; kk++) ka[tau][kk] = *reinterpret_cast<const bf16x8_t *>(kr + kk * 32 + g * 8);
         }
-        // V rows of this lane's 8 key slots, dims r16*8 .. r16*8+7
-        uint4 vv[8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            bool main;
-            const size_t off = key_off(kw + slot_key(g, e), main);
-            vv[e] = *reinterpret_cast<const uint4 *>((main ? vmain : vswa) + off + r16 * 8);
-        }
+        for (int e = 0; e < 8; e++)
+            vv[e] = *reinterpret_cast<const uint4 *>(row_ptr(rows[slot_key(g, e)], vmain, vswa) + r16 * 8);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One step on the registers loaded for it; `next` runs once K and V have
+    // left the registers (after QK and the V^T write) and issues the following
+    // step's loads into the same registers, overlapping softmax and PV.
+    auto compute = [&](int kb, bf16x8_t (&ka)[2][4], uint4 (&vv)[8], auto &&next) {
+        const int kw = kb + w * 32;
         // S^T = K Q^T: lane holds keys 4g+ii (tile 0) and 16+4g+ii (tile 1) of head r16
         f32x4_t st[2];
 #pragma unroll
@@ -222,13 +237,14 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendParams p)
             *reinterpret_cast<uint2 *>(row + 4 * g) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             *reinterpret_cast<uint2 *>(row + 16 + 4 * g) = make_uint2(h[4] | (h[5] << 16), h[6] | (h[7] << 16));
         }
+        next();
         // online softmax over this step's 32 keys (log2 domain)
         float sc[8];
         float mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             const int key = kw + slot_key(g, e);
-            sc[e] = (key < k_stop) ? st[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+            sc[e] = (key < k_end) ? st[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
             mx = fmaxf(mx, sc[e]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -262,10 +278,33 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendParams p)
             acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), pb, acc[m], 0, 0, 0);
         }
         __syncthreads();
+    };
+
+    // Software pipeline: the loads of step s+1 are issued into the registers
+    // that step s has just consumed.  Row codes are staged per kRowChunk keys;
+    // a chunk boundary stages before the loads that need it (the barrier in
+    // stage_rows orders it after every wave's earlier reads of s_rows).
+    bf16x8_t ka[2][4];
+    uint4 vv[8];
+    if (k_begin < k_end) {
+        stage_rows(k_begin);
+        load_kv(k_begin, ka, vv);
+        for (int kb = k_begin; kb < k_end; kb += kStepKeys) {
+            const int kn = kb + kStepKeys;
+            const bool more = kn < k_end;
+            const bool restage = more && ((kn - k_begin) % kRowChunk == 0);
+            compute(kb, ka, vv, [&] {
+                if (more && !restage) load_kv(kn, ka, vv);
+            });
+            if (restage) {
+                stage_rows(kn);
+                load_kv(kn, ka, vv);
+            }
+        }
     }
 
-    // ---- merge the 4 waves (the V^T buffer is free now)
-    float *ob = reinterpret_cast<float *>(&s_vt[0][0]);   // [4][16][128]
+    // ---- merge the waves (the V^T buffer is free now)
+    float *ob = reinterpret_cast<float *>(&s_vt[0][0]);   // [kWaves][16][128]
 #pragma unroll
     for (int m = 0; m < 8; m++)
 #pragma unroll
@@ -275,60 +314,87 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendParams p)
         s_ml[w][r16][1] = l_run;
     }
     __syncthreads();
-    const int hh = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
+    // thread -> (head hh, dims d0 .. d0+3)
+    const int hh = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 4;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < 4; ww++) M = fmaxf(M, s_ml[ww][hh][0]);
+    for (int ww = 0; ww < kWaves; ww++) M = fmaxf(M, s_ml[ww][hh][0]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, o[8];
+    float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 8; j++) o[j] = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ww++) {
+    for (int ww = 0; ww < kWaves; ww++) {
         const float f = exp2f(s_ml[ww][hh][0] - Mu);
         L += f * s_ml[ww][hh][1];
-#pragma unroll
-        for (int j = 0; j < 8; j++) o[j] += f * ob[(ww * 16 + hh) * 128 + d0 + j];
+        const float4 v = *reinterpret_cast<const float4 *>(ob + (ww * 16 + hh) * 128 + d0);
+        o[0] += f * v.x; o[1] += f * v.y; o[2] += f * v.z; o[3] += f * v.w;
     }
-
     const size_t row_id = ((size_t)l * p.n_q + i) * p.H + hg * 16 + hh;
     if (p.n_splits > 1) {
+        // this split's (max, sum, acc) record; k_attend_combine merges them
         const size_t rec0 = (((size_t)l * p.n_q + i) * HG + hg) * p.n_splits;
-        float *rec = p.ws_part + (rec0 + split) * kPartFloats + hh * 130;
-        if ((threadIdx.x & 15) == 0) {
+        float *rec = p.ws_part + (rec0 + split) * kPartFloats + hh * kHeadRec;
+        if ((threadIdx.x & 31) == 0) {
             rec[0] = M;
             rec[1] = L;
         }
-#pragma unroll
-        for (int j = 0; j < 8; j++) rec[2 + d0 + j] = o[j];
-        const size_t ctr = ((size_t)l * p.n_q + i) * HG + hg;
-        if (!last_arrival(p.ws_cnt + ctr, (uint32_t)p.n_splits, &s_flag)) return;
-        // merge the split records of this (layer, query, head group)
-        M = -INFINITY;
-        for (int c = 0; c < p.n_splits; c++) {
-            const float *r = p.ws_part + (rec0 + c) * kPartFloats + hh * 130;
-            M = fmaxf(M, __hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        }
-        const float Mu2 = (M == -INFINITY) ? 0.f : M;
-        L = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; j++) o[j] = 0.f;
-        for (int c = 0; c < p.n_splits; c++) {
-            const float *r = p.ws_part + (rec0 + c) * kPartFloats + hh * 130;
-            const float f = exp2f(__hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - Mu2);
-            L += f * __hip_atomic_load(r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-                o[j] += f * __hip_atomic_load(r + 2 + d0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        *reinterpret_cast<float4 *>(rec + 4 + d0) = make_float4(o[0], o[1], o[2], o[3]);
+        return;
     }
     const float inv = 1.f / L;
-    uint32_t packed[4];
+    const uint32_t lo = (uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
+    *reinterpret_cast<uint2 *>((uint16_t *)p.out + row_id * 128 + d0) = make_uint2(lo, hi);
+    if (p.lse && (threadIdx.x & 31) == 0) p.lse[row_id] = (M + log2f(L)) * kLn2;
+}
+
+// Merge of the split records of one (query, layer, head group): thread ->
+// (head, 4 dims); all records' loads are issued before use.
+__global__ __launch_bounds__(512) void k_attend_combine(AttendParams p)
+{
+    const int HG = p.H / 16;
+    const int i = blockIdx.x % p.n_q;
+    const int rest = blockIdx.x / p.n_q;
+    const int hg = rest % HG, l = rest / HG;
+    const int hh = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 4;
+    const size_t rec0 = (((size_t)l * p.n_q + i) * HG + hg) * p.n_splits;
+    float M = -INFINITY, L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < p.n_splits; c0 += kMergeBatch) {
+        float mc[kMergeBatch], lc[kMergeBatch];
+        float4 a[kMergeBatch];
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-        packed[j] = (uint32_t)f32_to_bf16(o[2 * j] * inv) | ((uint32_t)f32_to_bf16(o[2 * j + 1] * inv) << 16);
-    *reinterpret_cast<uint4 *>((uint16_t *)p.out + row_id * 128 + d0) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    if (p.lse && (threadIdx.x & 15) == 0) p.lse[row_id] = (M + log2f(L)) * kLn2;
+        for (int u = 0; u < kMergeBatch; u++) {
+            if (c0 + u < p.n_splits) {
+                const float *r = p.ws_part + (rec0 + c0 + u) * kPartFloats + hh * kHeadRec;
+                mc[u] = r[0];
+                lc[u] = r[1];
+                a[u] = *reinterpret_cast<const float4 *>(r + 4 + d0);
+            } else {
+                mc[u] = -INFINITY;
+                lc[u] = 0.f;
+                a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; u++) Mn = fmaxf(Mn, mc[u]);
+        const float Mu = (Mn == -INFINITY) ? 0.f : Mn;
+        const float rescale = exp2f(M - Mu);
+        L *= rescale;
+        o[0] *= rescale; o[1] *= rescale; o[2] *= rescale; o[3] *= rescale;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; u++) {
+            const float f = exp2f(mc[u] - Mu);
+            L += f * lc[u];
+            o[0] += f * a[u].x; o[1] += f * a[u].y; o[2] += f * a[u].z; o[3] += f * a[u].w;
+        }
+        M = Mn;
+    }
+    const size_t row_id = ((size_t)l * p.n_q + i) * p.H + hg * 16 + hh;
+    const float inv = 1.f / L;
+    const uint32_t lo = (uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
+    *reinterpret_cast<uint2 *>((uint16_t *)p.out + row_id * 128 + d0) = make_uint2(lo, hi);
+    if (p.lse && (threadIdx.x & 31) == 0) p.lse[row_id] = (M + log2f(L)) * kLn2;
 }
 
 // ============================================================ planning / launch
@@ -336,19 +402,20 @@ static int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b);
 
 AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dtype)
 {
-    AttendPlan pl{false, 1, 0, 0};
-    pl.mfma = (dtype == 1) && (D == 128) && (H % 16 == 0);
+    AttendPlan pl{(dtype == 1) && (D == 128) && (H % 16 == 0), 1, 0, 0};
     if (!pl.mfma) return pl;
-    const int n_keys_max = K + W;
-    const int steps = std::max(1, ceil_div_i(n_keys_max, kAttendKeysPerIter));
+    // Split a key list over several workgroups only when there are too few
+    // (query, layer, head group) triples to spread the gather over the chip;
+    // each split then costs a device-scope merge.
+    const int steps = std::max(1, (K + W + kStepKeys - 1) / kStepKeys);
     const long long base = (long long)n_q * n_layers * (H / 16);
     int n_splits = 1;
-    if (base < kTargetWorkgroups) n_splits = std::min(steps, ceil_div_i(kTargetWorkgroups, base));
-    const int steps_per_split = ceil_div_i(steps, n_splits);
-    n_splits = ceil_div_i(steps, steps_per_split);
+    if (base < kTargetWorkgroups / 2) n_splits = (int)std::min<long long>(steps, (kTargetWorkgroups / 2 + base - 1) / base);
+    const int steps_per_split = (steps + n_splits - 1) / n_splits;
+    n_splits = (steps + steps_per_split - 1) / steps_per_split;
     pl.n_splits = n_splits;
-    pl.keys_per_split = steps_per_split * kAttendKeysPerIter;
-    pl.part_bytes = (n_splits > 1) ? (size_t)base * n_splits * kPartFloats * sizeof(float) : 0;
+    pl.keys_per_split = steps_per_split * kStepKeys;
+    pl.part_bytes = n_splits > 1 ? (size_t)base * n_splits * kPartFloats * sizeof(float) : 0;
     return pl;
 }
 
@@ -357,11 +424,15 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
     if (p0.n_q <= 0 || p0.n_layers <= 0) return hipSuccess;
     AttendParams p = p0;
     if (pl.mfma) {
+        p.n_q_pad = (p.n_q + 7) / 8 * 8;
         p.n_splits = pl.n_splits;
         p.keys_per_split = pl.keys_per_split;
-        p.n_q_pad = (p.n_q + 7) / 8 * 8;
         const long long n_wg = (long long)p.n_q_pad * pl.n_splits * (p.H / 16) * p.n_layers;
-        hipLaunchKernelGGL(k_attend_mfma, dim3((unsigned)n_wg), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(k_attend_mfma, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+        if (pl.n_splits > 1) {
+            const long long n_rows = (long long)p.n_q * (p.H / 16) * p.n_layers;
+            hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)n_rows), dim3(512), 0, st, p);
+        }
         return hipGetLastError();
     }
     dim3 grid((unsigned)p.n_q, (unsigned)p.n_layers, (unsigned)ceil_div_i(p.H, 4));

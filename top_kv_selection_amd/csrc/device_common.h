@@ -35,13 +35,10 @@ struct LdsKeys {
     __device__ __forceinline__ uint32_t operator()(int i) const { return p[lds_pad(i)]; }
 };
 
-// Keys written by other workgroups: loaded at device scope so that no stale
-// cache line of this CU can be returned.
+// Keys in global memory, written by an earlier launch.
 struct GlobalKeys {
     const uint32_t *p;
-    __device__ __forceinline__ uint32_t operator()(int i) const {
-        return __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    __device__ __forceinline__ uint32_t operator()(int i) const { return p[i]; }
 };
 
 // Exclusive prefix sum of one value per thread over a workgroup of NT threads
@@ -118,14 +115,17 @@ struct Threshold {
 
 // Threshold of the Top-n over keys(0..count-1) (key 0 = not a candidate).
 // With at most n candidates every candidate is taken (thr = 0, quota = 0).
+// With have_pass1, `hist` already holds the pass-1 histogram.
 template <int NT, class Keys>
 __device__ Threshold radix_threshold(const Keys &keys, int count, uint32_t n, uint32_t *hist,
-                                     uint32_t *sm)
+                                     uint32_t *sm, bool have_pass1 = false)
 {
     const int tid = threadIdx.x;
-    for (int b = tid; b < kRadixBins; b += NT) hist[b] = 0;
-    __syncthreads();
-    for (int i = tid; i < count; i += NT) atomicAdd(&hist[keys(i) >> kRadixBits], 1u);
+    if (!have_pass1) {
+        for (int b = tid; b < kRadixBins; b += NT) hist[b] = 0;
+        __syncthreads();
+        for (int i = tid; i < count; i += NT) atomicAdd(&hist[keys(i) >> kRadixBits], 1u);
+    }
     __syncthreads();
     // bin 0 holds only the zero keys (valid keys are >= 2^20)
     const uint32_t n_valid = (uint32_t)count - hist[0];
@@ -182,6 +182,115 @@ __device__ uint32_t ordered_compact(const Keys &keys, int count, Threshold th, E
     return total;
 }
 
+// ---- register-resident selection (at most NT * IPT items) -----------------
+// Thread t owns items [t*IPT, t*IPT + IPT) as keys k[0..IPT) (0 past the end).
+// The pass-1 histogram (bins of key >> 11 over all items) must already be in
+// `hist` (LDS).
+
+template <int NT, int IPT>
+__device__ Threshold threshold_regs(const uint32_t (&k)[IPT], int count, uint32_t n, uint32_t *hist,
+                                    uint32_t *sm)
+{
+    const int tid = threadIdx.x;
+    const uint32_t n_valid = (uint32_t)count - hist[0];
+    if (n_valid <= n) {
+        __syncthreads();
+        return {0u, 0u};
+    }
+    uint32_t b1, above1;
+    find_bin<NT>(hist, n, 0u, b1, above1, sm);
+    for (int b = tid; b < kRadixBins; b += NT) hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < IPT; j++)
+        if ((k[j] >> kRadixBits) == b1) atomicAdd(&hist[k[j] & kRadixMask], 1u);
+    __syncthreads();
+    uint32_t b2, above2;
+    find_bin<NT>(hist, n, above1, b2, above2, sm);
+    return {(b1 << kRadixBits) | b2, n - above2};
+}
+
+template <int NT, int IPT, class Emit>
+__device__ uint32_t compact_regs(const uint32_t (&k)[IPT], Threshold th, Emit emit, uint32_t *sm)
+{
+    const int lo = (int)threadIdx.x * IPT;
+    uint32_t ties = 0;
+#pragma unroll
+    for (int j = 0; j < IPT; j++) ties += (k[j] == th.thr);
+    uint32_t unused;
+    const uint32_t tie0 = block_excl_scan<NT>(ties, unused, sm);
+    uint32_t taken = 0;
+    uint32_t take_mask = 0;    // bit j: item lo + j is chosen (IPT <= 32)
+    {
+        uint32_t r = tie0;
+#pragma unroll
+        for (int j = 0; j < IPT; j++) {
+            const bool eq = k[j] == th.thr;
+            const bool take = (k[j] > th.thr) || (eq && r < th.quota);
+            take_mask |= (uint32_t)take << j;
+            taken += take;
+            r += eq;
+        }
+    }
+    uint32_t total;
+    uint32_t slot = block_excl_scan<NT>(taken, total, sm);
+    while (take_mask) {
+        const int j = __builtin_ctz(take_mask);
+        take_mask &= take_mask - 1;
+        emit(slot++, lo + j);
+    }
+    return total;
+}
+
+// Adds a workgroup's LDS histogram into a global one (non-zero bins only).
+template <int NT>
+__device__ __forceinline__ void flush_hist(const uint32_t *hist, uint32_t *ghist)
+{
+    for (int b = threadIdx.x; b < kRadixBins; b += NT) {
+        const uint32_t c = hist[b];
+        if (c) atomicAdd(&ghist[b], c);
+    }
+}
+
+// Moves a global histogram into LDS and leaves the global one zeroed.
+template <int NT>
+__device__ __forceinline__ void take_hist(uint32_t *ghist, uint32_t *hist)
+{
+    for (int b = threadIdx.x; b < kRadixBins; b += NT) {
+        hist[b] = ghist[b];
+        ghist[b] = 0u;
+    }
+    __syncthreads();
+}
+
+// Loads this thread's IPT keys of a global key row (16-byte aligned, `count`
+// valid entries) into registers, 0 past the end.
+template <int IPT>
+__device__ __forceinline__ void load_keys_global(const uint32_t *g, int count, uint32_t (&k)[IPT])
+{
+    const int lo = (int)threadIdx.x * IPT;
+    const uint4 *g4 = reinterpret_cast<const uint4 *>(g + lo);
+#pragma unroll
+    for (int u = 0; u < IPT / 4; u++) {
+        const int i = lo + 4 * u;
+        if (i + 4 <= count) {
+            const uint4 v = g4[u];
+            k[4 * u] = v.x; k[4 * u + 1] = v.y; k[4 * u + 2] = v.z; k[4 * u + 3] = v.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++) k[4 * u + e] = (i + e < count) ? g[i + e] : 0u;
+        }
+    }
+}
+
+template <int IPT>
+__device__ __forceinline__ void load_keys_lds(const uint32_t *lds, int count, uint32_t (&k)[IPT])
+{
+    const int lo = (int)threadIdx.x * IPT;
+#pragma unroll
+    for (int j = 0; j < IPT; j++) k[j] = (lo + j < count) ? lds[lds_pad(lo + j)] : 0u;
+}
+
 // Nearest integer to sum / n (n >= 1), exact ties to the even integer:
 // floor(sum/n + 1/2) computed as a floor division of 2*sum + n by 2n; an exact
 // tie leaves no remainder and then lands on the odd neighbour, which is moved
@@ -199,24 +308,6 @@ __device__ __forceinline__ int round_mean_half_even(int sum, int n)
 __device__ __forceinline__ int dot4_i8(int a, int b, int c)
 {
     return __builtin_amdgcn_sdot4(a, b, c, false);
-}
-
-// Device-scope "last one in" counter: each of `parties` workgroups calls this
-// once after its results are written; exactly one gets true, after all the
-// others have arrived, and the counter returns to zero.  Must be reached by
-// every thread of the workgroup.  `flag` is one LDS word.
-__device__ __forceinline__ bool last_arrival(uint32_t *counter, uint32_t parties, uint32_t *flag)
-{
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = atomicInc(counter, parties - 1);
-        *flag = (prev == parties - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    const bool last = *flag != 0;
-    if (last) __threadfence();
-    return last;
 }
 
 }  // namespace csa2

@@ -9,7 +9,6 @@ namespace csa2 {
 
 constexpr int kSelectThreads = 512;     // threads of a selection workgroup
 constexpr int kTargetWorkgroups = 512;  // ~2 per CU on a 256-CU MI355X
-constexpr int kAttendKeysPerIter = 128; // keys one attention workgroup takes per step
 constexpr int kMaxCandidates = 16384;   // P*B cap: candidates one query may score
 
 struct BlockKeysParams {
@@ -22,10 +21,11 @@ struct IndexParams {
     const int8_t *q_idx;
     const int32_t *q_seq, *q_pos;
     const int8_t *k_idx, *k_blk;
+    int8_t *k_blk_store;    // non-null: store each query's own block key when the query completes it
     int T, B, P, n_q, G, chunk, nblk;
     uint32_t *ws_keys;
     int64_t ws_stride;
-    uint32_t *ws_cnt;
+    uint32_t *ws_hist;      // [n_q][2048] top-11-bit histograms (split launches)
     int32_t *blk_ids, *blk_cnt;
 };
 
@@ -37,7 +37,7 @@ struct TopkParams {
     int T, B, P, K, n_q, G, chunk;
     uint32_t *ws_keys;
     int64_t ws_stride;
-    uint32_t *ws_cnt;
+    uint32_t *ws_hist;
     int32_t *topk, *topk_cnt;
 };
 
@@ -53,9 +53,9 @@ struct AttendParams {
     float scale_log2;       // logit scale times log2(e)
     void *out;
     float *lse;
-    float *ws_part;         // split partials (MFMA path, n_splits > 1)
-    uint32_t *ws_cnt;
-    int n_splits, keys_per_split, n_q_pad;
+    float *ws_part;         // split records (n_splits > 1)
+    int n_splits, keys_per_split;
+    int n_q_pad;            // n_q rounded up to a multiple of 8 (XCD-aware numbering)
 };
 
 // Work split of one selection launch: G workgroups per query, `chunk` items each.
@@ -66,10 +66,14 @@ struct SelectPlan {
 };
 
 struct AttendPlan {
-    bool mfma;
+    bool mfma;    // bf16, D = 128, H a multiple of 16: the MFMA kernel; else the generic one
     int n_splits, keys_per_split;
     size_t part_bytes;
 };
+
+// Workspace head bytes of a selection launch: one 2048-bin histogram per
+// query (split launches only); zero between calls.
+size_t select_head_bytes(int n_q, bool split);
 
 SelectPlan plan_index(int n_q, int T, int B, int P, int d_idx);
 SelectPlan plan_topk(int n_q, int B, int P, int K, int d_idx);

@@ -10,8 +10,11 @@
 //
 // Decode has one query per sequence, so a query's scan (up to 1 MiB of block
 // keys or candidate rows at 128K context) is split over G workgroups that
-// write keys to the workspace; the last workgroup to arrive selects.  With many
-// queries (prefill) each workgroup owns one query and keeps its keys in LDS.
+// write keys and a histogram to the workspace; a second launch with one
+// workgroup per query then selects.  (A last-arriving-workgroup hand-off was
+// measured at ~6 us on MI355X -- an L2 writeback plus a device-scope atomic
+// round trip -- against ~2.5 us for a kernel boundary.)  With many queries
+// (prefill) each workgroup owns one query and keeps its keys in LDS.
 // Loads are 16-byte per lane with DIDX/16 lanes per row, so a wave reads
 // 1 KiB of consecutive rows per instruction.
 #include "device_common.h"
@@ -78,13 +81,20 @@ __global__ __launch_bounds__(256) void k_block_keys(BlockKeysParams p)
 }
 
 // ---------------------------------------------------------------- block pass
+// Scoring: thread group (DIDX/16 lanes) per block, U rows in flight per lane.
+// Every key also lands in a per-workgroup histogram of its top 11 bits; split
+// launches add it into the query's global histogram, so the last workgroup
+// starts the selection with pass 1 already done.
+constexpr int kUnroll = 4;
+constexpr int kPoolLds = 4096;      // pooled block ids staged in LDS for the emit
+
 template <int NT, int DIDX, bool SPLIT>
 __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
 {
-    __shared__ uint32_t s_keys[kLdsKeysPadded];
+    constexpr int LPR = DIDX / 16, RPP = NT / LPR, IPT = kLdsKeys / NT;
+    __shared__ uint32_t s_keys[SPLIT ? 4 : kLdsKeysPadded];
     __shared__ uint32_t s_hist[kRadixBins];
     __shared__ uint32_t s_sm[NT / 64 + 4];
-    constexpr int LPR = DIDX / 16;
     const int q = blockIdx.x % p.n_q;
     const int g = blockIdx.x / p.n_q;
     const int tid = threadIdx.x, part = tid % LPR;
@@ -92,56 +102,98 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     const int jt = t / p.B, n_elig = jt + 1;
     int32_t *ids = p.blk_ids + (size_t)q * p.P;
 
+    // A Full layer stores the key of a block its query has just completed
+    // (the query's own block, when t is the block's last position).
+    const bool store_own = p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk;
+    int8_t *own_store = store_own ? p.k_blk_store + ((size_t)s * p.nblk + jt) * DIDX + part * 16 : nullptr;
+    const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX + part * 16;
+
     if (n_elig <= p.P) {   // the pool is every eligible block
         for (int j = g * NT + tid; j < p.P; j += p.G * NT) ids[j] = (j < n_elig) ? j : -1;
         if (g == 0 && tid == 0) p.blk_cnt[q] = n_elig;
+        if (store_own && g == 0 && tid < LPR)
+            *reinterpret_cast<int4 *>(own_store) = block_key_part<DIDX>(own_rows, p.B);
         return;
     }
+    for (int b = tid; b < kRadixBins; b += NT) s_hist[b] = 0;
+    __syncthreads();
 
     const int4 qv = *reinterpret_cast<const int4 *>(p.q_idx + (size_t)q * DIDX + part * 16);
     const int lo = SPLIT ? min(n_elig, g * p.chunk) : 0;
     const int hi = SPLIT ? min(n_elig, lo + p.chunk) : n_elig;
     uint32_t *gkeys = p.ws_keys + (size_t)q * p.ws_stride;
+    uint32_t *ghist = p.ws_hist + (size_t)q * kRadixBins;
     const int8_t *blk_rows = p.k_blk + (size_t)s * p.nblk * DIDX + part * 16;
-    const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX + part * 16;
 
-    for (int base = lo; base < hi; base += NT / LPR) {
-        const int j = base + tid / LPR;
-        int acc = 0;
-        if (j < hi) {
-            const int4 kv = (j < jt) ? *reinterpret_cast<const int4 *>(blk_rows + (size_t)j * DIDX)
-                                     : block_key_part<DIDX>(own_rows, t - jt * p.B + 1);
-            acc = dot16_i8(kv, qv);
+    for (int base = lo; base < hi; base += RPP * kUnroll) {
+        int4 kv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int j = base + u * RPP + tid / LPR;
+            kv[u] = make_int4(0, 0, 0, 0);
+            if (j < hi && j < jt) kv[u] = *reinterpret_cast<const int4 *>(blk_rows + (size_t)j * DIDX);
         }
-        acc = row_reduce<LPR>(acc);
-        if (j < hi && part == 0) {
-            const uint32_t key = (uint32_t)(acc + (int)kKeyBias);
-            if (SPLIT) gkeys[j] = key;
-            else s_keys[lds_pad(j)] = key;
-        }
-    }
-
-    bool in_lds = true;
-    if (SPLIT) {
-        if (!last_arrival(p.ws_cnt + q, (uint32_t)p.G, &s_sm[NT / 64 + 3])) return;
-        in_lds = n_elig <= kLdsKeys;
-        if (in_lds) {
-            const GlobalKeys src{gkeys};
-            for (int i = tid; i < n_elig; i += NT) s_keys[lds_pad(i)] = src(i);
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int j = base + u * RPP + tid / LPR;
+            if (j == jt && j < hi) {
+                kv[u] = block_key_part<DIDX>(own_rows, t - jt * p.B + 1);
+                if (store_own) *reinterpret_cast<int4 *>(own_store) = kv[u];
+            }
+            int acc = (j < hi) ? dot16_i8(kv[u], qv) : 0;
+            acc = row_reduce<LPR>(acc);
+            if (j < hi && part == 0) {
+                const uint32_t key = (uint32_t)(acc + (int)kKeyBias);
+                if (SPLIT) gkeys[j] = key;
+                else s_keys[lds_pad(j)] = key;
+                atomicAdd(&s_hist[key >> kRadixBits], 1u);
+            }
         }
     }
     __syncthreads();
+    if (SPLIT) {   // the selection runs in k_index_select, after this launch
+        flush_hist<NT>(s_hist, ghist);
+        return;
+    }
+    const uint32_t cap = (uint32_t)p.P;
+    auto emit = [&](uint32_t slot, int i) { if (slot < cap) ids[slot] = i; };
+    uint32_t k[IPT];
+    load_keys_lds<IPT>(s_keys, n_elig, k);
+    const Threshold th = threshold_regs<NT, IPT>(k, n_elig, cap, s_hist, s_sm);
+    const uint32_t chosen = compact_regs<NT, IPT>(k, th, emit, s_sm);
+    for (int o = (int)chosen + tid; o < p.P; o += NT) ids[o] = -1;
+    if (tid == 0) p.blk_cnt[q] = (int32_t)min(chosen, cap);
+}
 
+// Pool selection of a split launch: one workgroup per query, after every
+// scoring workgroup of k_index_blocks<.., true> has finished (kernel order).
+// The histogram (pass 1) and the keys are loaded together.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_index_select(IndexParams p)
+{
+    constexpr int IPT = kLdsKeys / NT;
+    __shared__ uint32_t s_hist[kRadixBins];
+    __shared__ uint32_t s_sm[NT / 64 + 4];
+    const int q = blockIdx.x, tid = threadIdx.x;
+    const int t = p.q_pos[q];
+    const int n_elig = t / p.B + 1;
+    if (n_elig <= p.P) return;   // handled by the scoring launch
+    int32_t *ids = p.blk_ids + (size_t)q * p.P;
+    uint32_t *gkeys = p.ws_keys + (size_t)q * p.ws_stride;
+    uint32_t *ghist = p.ws_hist + (size_t)q * kRadixBins;
     const uint32_t cap = (uint32_t)p.P;
     auto emit = [&](uint32_t slot, int i) { if (slot < cap) ids[slot] = i; };
     uint32_t chosen;
-    if (in_lds) {
-        const LdsKeys keys{s_keys};
-        const Threshold th = radix_threshold<NT>(keys, n_elig, (uint32_t)p.P, s_hist, s_sm);
-        chosen = ordered_compact<NT>(keys, n_elig, th, emit, s_sm);
-    } else {
+    if (n_elig <= NT * IPT) {
+        uint32_t k[IPT];
+        load_keys_global<IPT>(gkeys, n_elig, k);
+        take_hist<NT>(ghist, s_hist);
+        const Threshold th = threshold_regs<NT, IPT>(k, n_elig, cap, s_hist, s_sm);
+        chosen = compact_regs<NT, IPT>(k, th, emit, s_sm);
+    } else {   // more blocks than one workgroup holds in registers
+        take_hist<NT>(ghist, s_hist);
         const GlobalKeys keys{gkeys};
-        const Threshold th = radix_threshold<NT>(keys, n_elig, (uint32_t)p.P, s_hist, s_sm);
+        const Threshold th = radix_threshold<NT>(keys, n_elig, cap, s_hist, s_sm, true);
         chosen = ordered_compact<NT>(keys, n_elig, th, emit, s_sm);
     }
     for (int o = (int)chosen + tid; o < p.P; o += NT) ids[o] = -1;
@@ -149,63 +201,110 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
 }
 
 // ---------------------------------------------------------------- token Top-K
+// Threshold and ordered emit of a query's Top-K from its keys in registers and
+// its pass-1 histogram in LDS; writes topk/topk_cnt.
+template <int NT, int IPT>
+__device__ void topk_finish(const TopkParams &p, int q, const uint32_t (&k)[IPT], int n_cand,
+                            uint32_t *s_hist, int32_t *s_pool, uint32_t *s_sm)
+{
+    const int tid = threadIdx.x, B = p.B;
+    const int n_pool = p.blk_cnt[q];
+    const int32_t *pool = p.blk_ids + (size_t)q * p.P;
+    const bool pool_in_lds = n_pool <= kPoolLds;
+    if (pool_in_lds)
+        for (int r = tid; r < n_pool; r += NT) s_pool[r] = pool[r];
+    const Threshold th = threshold_regs<NT, IPT>(k, n_cand, (uint32_t)p.K, s_hist, s_sm);
+    int32_t *out = p.topk + (size_t)q * p.K;
+    const uint32_t cap = (uint32_t)p.K;
+    auto emit = [&](uint32_t slot, int i) {
+        const int r = i / B;
+        const int blk = pool_in_lds ? s_pool[r] : pool[r];
+        if (slot < cap) out[slot] = blk * B + (i - r * B);
+    };
+    const uint32_t chosen = compact_regs<NT, IPT>(k, th, emit, s_sm);
+    for (int o = (int)chosen + tid; o < p.K; o += NT) out[o] = -1;
+    if (tid == 0) p.topk_cnt[q] = (int32_t)min(chosen, cap);
+}
+
 template <int NT, int DIDX, bool SPLIT>
 __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
 {
-    __shared__ uint32_t s_keys[kLdsKeysPadded];
+    constexpr int LPR = DIDX / 16, RPP = NT / LPR, IPT = kLdsKeys / NT;
+    __shared__ uint32_t s_keys[SPLIT ? 4 : kLdsKeysPadded];
     __shared__ uint32_t s_hist[kRadixBins];
+    __shared__ int32_t s_pool[SPLIT ? 4 : kPoolLds];
     __shared__ uint32_t s_sm[NT / 64 + 4];
-    constexpr int LPR = DIDX / 16;
     const int q = blockIdx.x % p.n_q;
     const int g = blockIdx.x / p.n_q;
     const int tid = threadIdx.x, part = tid % LPR;
     const int s = p.q_seq[q], t = p.q_pos[q];
-    const int n_cand = p.blk_cnt[q] * p.B;            // <= P*B <= kLdsKeys
+    const int B = p.B;
+    const int n_pool = p.blk_cnt[q];
+    const int n_cand = n_pool * B;                    // <= P*B <= kLdsKeys
     const int32_t *pool = p.blk_ids + (size_t)q * p.P;
+    for (int b = tid; b < kRadixBins; b += NT) s_hist[b] = 0;
+    __syncthreads();
 
     const int4 qv = *reinterpret_cast<const int4 *>(p.q_idx + (size_t)q * DIDX + part * 16);
     const int lo = SPLIT ? min(n_cand, g * p.chunk) : 0;
     const int hi = SPLIT ? min(n_cand, lo + p.chunk) : n_cand;
     uint32_t *gkeys = p.ws_keys + (size_t)q * p.ws_stride;
+    uint32_t *ghist = p.ws_hist + (size_t)q * kRadixBins;
     const int8_t *seq_rows = p.k_idx + (size_t)s * p.T * DIDX + part * 16;
 
-    for (int base = lo; base < hi; base += NT / LPR) {
-        const int c = base + tid / LPR;
-        int acc = 0;
-        bool valid = false;
-        if (c < hi) {
-            const int r = c / p.B;
-            const int pos = pool[r] * p.B + (c - r * p.B);
-            valid = pos <= t;
-            if (valid) acc = dot16_i8(*reinterpret_cast<const int4 *>(seq_rows + (size_t)pos * DIDX), qv);
+    for (int base = lo; base < hi; base += RPP * kUnroll) {
+        int pos[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int c = base + u * RPP + tid / LPR;
+            pos[u] = INT32_MAX;
+            if (c < hi) {
+                const int r = c / B;
+                pos[u] = pool[r] * B + (c - r * B);
+            }
         }
-        acc = row_reduce<LPR>(acc);
-        if (c < hi && part == 0) {
-            const uint32_t key = valid ? (uint32_t)(acc + (int)kKeyBias) : 0u;
-            if (SPLIT) gkeys[c] = key;
-            else s_keys[lds_pad(c)] = key;
+        int4 kv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            kv[u] = make_int4(0, 0, 0, 0);
+            if (pos[u] <= t) kv[u] = *reinterpret_cast<const int4 *>(seq_rows + (size_t)pos[u] * DIDX);
         }
-    }
-
-    if (SPLIT) {
-        if (!last_arrival(p.ws_cnt + q, (uint32_t)p.G, &s_sm[NT / 64 + 3])) return;
-        const GlobalKeys src{gkeys};
-        for (int i = tid; i < n_cand; i += NT) s_keys[lds_pad(i)] = src(i);
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int c = base + u * RPP + tid / LPR;
+            int acc = dot16_i8(kv[u], qv);
+            acc = row_reduce<LPR>(acc);
+            if (c < hi && part == 0) {
+                const uint32_t key = (pos[u] <= t) ? (uint32_t)(acc + (int)kKeyBias) : 0u;
+                if (SPLIT) gkeys[c] = key;
+                else s_keys[lds_pad(c)] = key;
+                atomicAdd(&s_hist[key >> kRadixBits], 1u);
+            }
+        }
     }
     __syncthreads();
+    if (SPLIT) {   // the selection runs in k_topk_select, after this launch
+        flush_hist<NT>(s_hist, ghist);
+        return;
+    }
+    uint32_t k[IPT];
+    load_keys_lds<IPT>(s_keys, n_cand, k);
+    topk_finish<NT, IPT>(p, q, k, n_cand, s_hist, s_pool, s_sm);
+}
 
-    int32_t *out = p.topk + (size_t)q * p.K;
-    const int B = p.B;
-    const uint32_t cap = (uint32_t)p.K;
-    auto emit = [&](uint32_t slot, int i) {
-        const int r = i / B;
-        if (slot < cap) out[slot] = pool[r] * B + (i - r * B);
-    };
-    const LdsKeys keys{s_keys};
-    const Threshold th = radix_threshold<NT>(keys, n_cand, (uint32_t)p.K, s_hist, s_sm);
-    const uint32_t chosen = ordered_compact<NT>(keys, n_cand, th, emit, s_sm);
-    for (int o = (int)chosen + tid; o < p.K; o += NT) out[o] = -1;
-    if (tid == 0) p.topk_cnt[q] = (int32_t)min(chosen, cap);
+template <int NT>
+__global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
+{
+    constexpr int IPT = kLdsKeys / NT;
+    __shared__ uint32_t s_hist[kRadixBins];
+    __shared__ int32_t s_pool[kPoolLds];
+    __shared__ uint32_t s_sm[NT / 64 + 4];
+    const int q = blockIdx.x;
+    const int n_cand = p.blk_cnt[q] * p.B;
+    uint32_t k[IPT];
+    load_keys_global<IPT>(p.ws_keys + (size_t)q * p.ws_stride, n_cand, k);
+    take_hist<NT>(p.ws_hist + (size_t)q * kRadixBins, s_hist);
+    topk_finish<NT, IPT>(p, q, k, n_cand, s_hist, s_pool, s_sm);
 }
 
 __global__ void k_fill_zero(uint32_t *p, size_t n)
@@ -231,9 +330,14 @@ static SelectPlan plan_scan(int n_q, long long n_items, int d_idx, bool must_spl
         pl.G = ceil_div(n_items, chunk);
         pl.chunk = chunk;
         pl.split = true;
-        pl.key_bytes = (size_t)n_q * (size_t)n_items * sizeof(uint32_t);
+        pl.key_bytes = (size_t)n_q * (size_t)((n_items + 3) / 4 * 4) * sizeof(uint32_t);
     }
     return pl;
+}
+
+size_t select_head_bytes(int n_q, bool split)
+{
+    return split ? (size_t)n_q * kRadixBins * sizeof(uint32_t) : 0;
 }
 
 SelectPlan plan_index(int n_q, int T, int B, int P, int d_idx)
@@ -264,8 +368,12 @@ template <int DIDX>
 static void launch_index_t(const IndexParams &p, const SelectPlan &pl, hipStream_t st)
 {
     dim3 grid((unsigned)(p.n_q * pl.G));
-    if (pl.split) hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
-    else hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
+    if (pl.split) {
+        hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
+        hipLaunchKernelGGL((k_index_select<kSelectThreads>), dim3((unsigned)p.n_q), dim3(kSelectThreads), 0, st, p);
+    } else {
+        hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
+    }
 }
 
 hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &pl, int d_idx, hipStream_t st)
@@ -280,8 +388,12 @@ template <int DIDX>
 static void launch_topk_t(const TopkParams &p, const SelectPlan &pl, hipStream_t st)
 {
     dim3 grid((unsigned)(p.n_q * pl.G));
-    if (pl.split) hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
-    else hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
+    if (pl.split) {
+        hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
+        hipLaunchKernelGGL((k_topk_select<kSelectThreads>), dim3((unsigned)p.n_q), dim3(kSelectThreads), 0, st, p);
+    } else {
+        hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
+    }
 }
 
 hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &pl, int d_idx, hipStream_t st)

@@ -104,10 +104,11 @@ def build_cache(dw: DeviceWorkload, upto_block=None):
 
 
 def step_update_begin(dw: DeviceWorkload) -> int:
-    """First block a Full layer rebuilds inside a step: decode rebuilds the
-    block holding the newest token; prefill builds every block."""
+    """First block a Full layer rebuilds in bulk inside a step: prefill builds
+    every block; decode builds none in bulk (the block pass stores the block
+    the newest token completes)."""
     T = dw.k_idx.shape[1]
-    return max(0, (T - 1) // dw.cfg.block) if dw.cfg.decode else 0
+    return T // dw.cfg.block if dw.cfg.decode else 0
 
 
 def run(dw: DeviceWorkload):
@@ -165,28 +166,29 @@ def replicate(dw: DeviceWorkload, q_idx=None, q=None) -> DeviceWorkload:
 
 
 def algorithmic_bytes(cfg: Config) -> dict:
-    """Bytes each kernel of one step must move at minimum (every input read
-    once, every output written once), for decode workloads where every query
-    sits at t = T-1.  Per launch, summed over the step's queries."""
+    """Bytes each kernel launch of one decode step must move at minimum (every
+    input read once, every output written once; every query at t = T-1).
+    Returns kernel -> list of per-launch byte counts, in launch order."""
     S, T, d, B, P, K, W_, H, D = (cfg.n_seq, cfg.ctx, cfg.d_idx, cfg.block, cfg.pool, cfg.top_k,
                                   cfg.window, cfg.n_heads, cfg.head_dim)
     esz = 4 if cfg.dtype == "f32" else 2
     n_q = cfg.n_q
     t = T - 1
     n_elig = t // B + 1
-    own = t - (n_elig - 1) * B + 1
+    own = t - (n_elig - 1) * B + 1                  # visible rows of the query's own block
     pool = min(P, n_elig)
-    n_cand = sum(min(B, t - j * B + 1) for j in range(n_elig - pool, n_elig)) if pool == n_elig else pool * B
+    n_cand = pool * B - (B - own)                   # the own block is pooled at most once
     sel = min(K, n_cand)
-    out = {}
-    out["block_keys"] = S * (B * d + d) if T % B == 0 else 0
-    out["index_blocks"] = n_q * ((n_elig - 1) * d + own * d + d + P * 4 + 4) if n_elig > P else n_q * (P * 4 + 4)
-    out["topk_tokens"] = n_q * (d + pool * 4 + 4 + n_cand * d + K * 4 + 4)
     per_layer = min(W_, t + 1) * 2 * D * esz + 2 * H * D * esz + H * 4
-    groups = cfg.groups()
-    attend = 0
-    for mode, layers in groups:
+    out = {"index_blocks": [], "topk_tokens": [], "attend": []}
+    for mode, layers in cfg.groups():
+        if mode in ("full", "reindex"):
+            store = n_q * d if (mode == "full" and own == B) else 0   # completed block key written back
+            if n_elig > P:
+                out["index_blocks"].append(n_q * ((n_elig - 1) * d + own * d + d + P * 4 + 4) + store)
+            else:
+                out["index_blocks"].append(n_q * (own * d + P * 4 + 4) + store)
+            out["topk_tokens"].append(n_q * (d + pool * 4 + 4 + n_cand * d + K * 4 + 4))
         main = 0 if mode == "swa" else K * 4 + 4 + sel * 2 * D * esz
-        attend += n_q * (main + len(layers) * per_layer)
-    out["attend"] = attend
+        out["attend"].append(n_q * (main + len(layers) * per_layer))
     return out
