@@ -74,7 +74,21 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run one plain 1 GiB device-to-device copy (calibrates rocprofv3 "
+                         "FETCH_SIZE/WRITE_SIZE against a known byte count) and exit")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

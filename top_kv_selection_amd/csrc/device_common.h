@@ -182,6 +182,48 @@ __device__ uint32_t ordered_compact(const Keys &keys, int count, Threshold th, E
     return total;
 }
 
+// find_bin done by wave 0 alone: lane l owns 32 bins walked from the top, so
+// one wave scan replaces the workgroup-wide scans (one barrier in total).
+// `res` is 2 LDS words.  Must be reached by every thread.
+template <int NT>
+__device__ __forceinline__ void find_bin_wave(const uint32_t *hist, uint32_t n, uint32_t base,
+                                              uint32_t &bin, uint32_t &above, uint32_t *res)
+{
+    static_assert(kRadixBins == 64 * 32, "one wave covers the bins, 32 per lane");
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        // bins of lane l: 2047 - 32l - j, j = 0..31 (descending)
+        uint32_t h[32];
+        const uint4 *src = reinterpret_cast<const uint4 *>(hist + kRadixBins - 32 * (lane + 1));
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const uint4 v = src[u];      // ascending bins; h[] is filled descending
+            h[31 - 4 * u] = v.x; h[30 - 4 * u] = v.y; h[29 - 4 * u] = v.z; h[28 - 4 * u] = v.w;
+        }
+        uint32_t local = 0;
+#pragma unroll
+        for (int j = 0; j < 32; j++) local += h[j];
+        uint32_t incl = local;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        uint32_t a = base + incl - local;
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            if (a < n && a + h[j] >= n) {
+                res[0] = (uint32_t)(kRadixBins - 1 - (32 * lane + j));
+                res[1] = a;
+            }
+            a += h[j];
+        }
+    }
+    __syncthreads();
+    bin = res[0];
+    above = res[1];
+}
+
 // ---- register-resident selection (at most NT * IPT items) -----------------
 // Thread t owns items [t*IPT, t*IPT + IPT) as keys k[0..IPT) (0 past the end).
 // The pass-1 histogram (bins of key >> 11 over all items) must already be in
@@ -198,46 +240,59 @@ __device__ Threshold threshold_regs(const uint32_t (&k)[IPT], int count, uint32_
         return {0u, 0u};
     }
     uint32_t b1, above1;
-    find_bin<NT>(hist, n, 0u, b1, above1, sm);
-    for (int b = tid; b < kRadixBins; b += NT) hist[b] = 0;
-    __syncthreads();
+    find_bin_wave<NT>(hist, n, 0u, b1, above1, sm + NT / 64 + 1);
+    // pass 2 into a second histogram (the barrier in find_bin_wave has
+    // ordered every read of the first); the first is zeroed for reuse later
+    uint32_t *hist2 = hist + kRadixBins;
 #pragma unroll
     for (int j = 0; j < IPT; j++)
-        if ((k[j] >> kRadixBits) == b1) atomicAdd(&hist[k[j] & kRadixMask], 1u);
+        if ((k[j] >> kRadixBits) == b1) atomicAdd(&hist2[k[j] & kRadixMask], 1u);
     __syncthreads();
     uint32_t b2, above2;
-    find_bin<NT>(hist, n, above1, b2, above2, sm);
+    find_bin_wave<NT>(hist2, n, above1, b2, above2, sm + NT / 64 + 1);
     return {(b1 << kRadixBits) | b2, n - above2};
 }
 
+// One scan of packed (ties << 16 | greater) counts gives both the rank of a
+// thread's first tie and the number of greater items before it; the slot of a
+// chosen item is (greater items before it) + min(quota, ties before it).
 template <int NT, int IPT, class Emit>
 __device__ uint32_t compact_regs(const uint32_t (&k)[IPT], Threshold th, Emit emit, uint32_t *sm)
 {
+    static_assert(NT * IPT < 65536, "packed counts are 16-bit");
     const int lo = (int)threadIdx.x * IPT;
-    uint32_t ties = 0;
+    uint32_t ties = 0, gt = 0;
 #pragma unroll
-    for (int j = 0; j < IPT; j++) ties += (k[j] == th.thr);
-    uint32_t unused;
-    const uint32_t tie0 = block_excl_scan<NT>(ties, unused, sm);
-    uint32_t taken = 0;
-    uint32_t take_mask = 0;    // bit j: item lo + j is chosen (IPT <= 32)
-    {
-        uint32_t r = tie0;
+    for (int j = 0; j < IPT; j++) {
+        ties += (k[j] == th.thr);
+        gt += (k[j] > th.thr);
+    }
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan<NT>((ties << 16) | gt, tot, sm);
+    const uint32_t tie0 = pre >> 16, gt0 = pre & 0xffffu;
+    const uint32_t total = (tot & 0xffffu) + min(tot >> 16, th.quota);
+    static_assert(IPT <= 32, "one bit per item");
+    uint32_t gt_mask = 0, tie_mask = 0;
 #pragma unroll
-        for (int j = 0; j < IPT; j++) {
-            const bool eq = k[j] == th.thr;
-            const bool take = (k[j] > th.thr) || (eq && r < th.quota);
-            take_mask |= (uint32_t)take << j;
-            taken += take;
-            r += eq;
+    for (int j = 0; j < IPT; j++) {
+        gt_mask |= (uint32_t)(k[j] > th.thr) << j;
+        tie_mask |= (uint32_t)(k[j] == th.thr) << j;
+    }
+    // ties whose rank is at least quota are dropped
+    uint32_t take = gt_mask;
+    if (tie0 < th.quota) {
+        uint32_t tm = tie_mask;
+        for (uint32_t r = tie0; tm && r < th.quota; r++) {
+            take |= tm & (0u - tm);      // lowest remaining tie
+            tm &= tm - 1;
         }
     }
-    uint32_t total;
-    uint32_t slot = block_excl_scan<NT>(taken, total, sm);
-    while (take_mask) {
-        const int j = __builtin_ctz(take_mask);
-        take_mask &= take_mask - 1;
-        emit(slot++, lo + j);
+    while (take) {
+        const int j = __builtin_ctz(take);
+        take &= take - 1;
+        const uint32_t below = (1u << j) - 1u;
+        emit(gt0 + __builtin_popcount(gt_mask & below) + min(tie0 + __builtin_popcount(tie_mask & below), th.quota),
+             lo + j);
     }
     return total;
 }
@@ -252,13 +307,15 @@ __device__ __forceinline__ void flush_hist(const uint32_t *hist, uint32_t *ghist
     }
 }
 
-// Moves a global histogram into LDS and leaves the global one zeroed.
+// Moves a global histogram into LDS hist[0..2048), leaves the global one
+// zeroed and clears the pass-2 histogram hist[2048..4096).
 template <int NT>
 __device__ __forceinline__ void take_hist(uint32_t *ghist, uint32_t *hist)
 {
     for (int b = threadIdx.x; b < kRadixBins; b += NT) {
         hist[b] = ghist[b];
         ghist[b] = 0u;
+        hist[kRadixBins + b] = 0u;
     }
     __syncthreads();
 }

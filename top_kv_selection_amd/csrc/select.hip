@@ -24,15 +24,22 @@ namespace csa2 {
 
 // One lane's 16 dimensions of a block key: the rounded mean of `n` rows that
 // start at `rows` (row stride DIDX bytes).
+// All (at most kMaxBlock) row loads are issued before the first is summed.
+constexpr int kMaxBlock = 16;
+
 template <int DIDX>
 __device__ __forceinline__ int4 block_key_part(const int8_t *rows, int n)
 {
+    int4 v[kMaxBlock];
+#pragma unroll
+    for (int r = 0; r < kMaxBlock; r++)
+        v[r] = (r < n) ? *reinterpret_cast<const int4 *>(rows + (size_t)r * DIDX) : make_int4(0, 0, 0, 0);
     int sum[16];
 #pragma unroll
     for (int b = 0; b < 16; b++) sum[b] = 0;
-    for (int r = 0; r < n; r++) {
-        const int4 v = *reinterpret_cast<const int4 *>(rows + (size_t)r * DIDX);
-        const int w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int r = 0; r < kMaxBlock; r++) {
+        const int w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
 #pragma unroll
         for (int a = 0; a < 4; a++)
 #pragma unroll
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
 {
     constexpr int LPR = DIDX / 16, RPP = NT / LPR, IPT = kLdsKeys / NT;
     __shared__ uint32_t s_keys[SPLIT ? 4 : kLdsKeysPadded];
-    __shared__ uint32_t s_hist[kRadixBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2 * kRadixBins];
     __shared__ uint32_t s_sm[NT / 64 + 4];
     const int q = blockIdx.x % p.n_q;
     const int g = blockIdx.x / p.n_q;
@@ -115,7 +122,7 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
             *reinterpret_cast<int4 *>(own_store) = block_key_part<DIDX>(own_rows, p.B);
         return;
     }
-    for (int b = tid; b < kRadixBins; b += NT) s_hist[b] = 0;
+    for (int b = tid; b < 2 * kRadixBins; b += NT) s_hist[b] = 0;
     __syncthreads();
 
     const int4 qv = *reinterpret_cast<const int4 *>(p.q_idx + (size_t)q * DIDX + part * 16);
@@ -172,7 +179,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void k_index_select(IndexParams p)
 {
     constexpr int IPT = kLdsKeys / NT;
-    __shared__ uint32_t s_hist[kRadixBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2 * kRadixBins];
     __shared__ uint32_t s_sm[NT / 64 + 4];
     const int q = blockIdx.x, tid = threadIdx.x;
     const int t = p.q_pos[q];
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
 {
     constexpr int LPR = DIDX / 16, RPP = NT / LPR, IPT = kLdsKeys / NT;
     __shared__ uint32_t s_keys[SPLIT ? 4 : kLdsKeysPadded];
-    __shared__ uint32_t s_hist[kRadixBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2 * kRadixBins];
     __shared__ int32_t s_pool[SPLIT ? 4 : kPoolLds];
     __shared__ uint32_t s_sm[NT / 64 + 4];
     const int q = blockIdx.x % p.n_q;
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
     const int n_pool = p.blk_cnt[q];
     const int n_cand = n_pool * B;                    // <= P*B <= kLdsKeys
     const int32_t *pool = p.blk_ids + (size_t)q * p.P;
-    for (int b = tid; b < kRadixBins; b += NT) s_hist[b] = 0;
+    for (int b = tid; b < 2 * kRadixBins; b += NT) s_hist[b] = 0;
     __syncthreads();
 
     const int4 qv = *reinterpret_cast<const int4 *>(p.q_idx + (size_t)q * DIDX + part * 16);
@@ -296,7 +303,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
 {
     constexpr int IPT = kLdsKeys / NT;
-    __shared__ uint32_t s_hist[kRadixBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2 * kRadixBins];
     __shared__ int32_t s_pool[kPoolLds];
     __shared__ uint32_t s_sm[NT / 64 + 4];
     const int q = blockIdx.x;
