@@ -251,3 +251,36 @@ def test_full_mode_stores_the_block_a_query_completes(lib):
     ref = oracle.run_layers(wl)
     got = pipeline.outputs(dw)
     assert_index_equal(got["index"][0], ref["index"][0], what="completed block")
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("decode_group_128k", dict(n_seq=4, ctx=40000, layers=("full", "reuse", "reuse"))),
+    ("decode_full_32k", dict(n_seq=3, ctx=5001, pool=300, top_k=700, window=100)),
+    ("decode_full_32k", dict(n_seq=2, ctx=900, pool=2048)),            # pool covers every block
+    ("decode_group_128k", dict(n_seq=3, ctx=12000, pool=256, layers=("reindex", "reuse"))),
+])
+def test_fused_layer_group_equals_separate_calls(lib, name, kw):
+    """The layer-group call (fused decode launches) and the separate calls
+    (block pass, token Top-K, attention) give identical indices and outputs."""
+    B, pipeline = lib
+    cfg = W.scaled(W.CONFIGS[name], **kw)
+    wl = W.generate(cfg, seed=36)
+    dw = pipeline.upload(wl)
+    pipeline.build_cache(dw)
+    pipeline.run(dw)                    # csa2_layer_group
+    torch.cuda.synchronize()
+    grp = dw.groups[0]
+    lc = dw.lcfg
+    ids = torch.empty_like(dw.blk_ids[0]); cnt = torch.empty_like(dw.blk_cnt[0])
+    tk = torch.empty_like(dw.topk[0]); tc = torch.empty_like(dw.topk_cnt[0])
+    out = torch.empty_like(grp.out); lse = torch.empty_like(grp.lse)
+    B.csa2_index_blocks(lc, grp.q_idx, dw.q_seq, dw.q_pos, dw.k_idx, dw.k_blk, ids, cnt, dw.ws)
+    B.csa2_topk_tokens(lc, grp.q_idx, dw.q_seq, dw.q_pos, dw.k_idx, ids, cnt, tk, tc, dw.ws)
+    B.csa2_attend_group(lc, grp.q, dw.q_seq, dw.q_pos, dw.k_main, dw.v_main, grp.k_swa, grp.v_swa,
+                        cfg.swa_first, tk, tc, out, lse, dw.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt, dw.blk_cnt[0]) and torch.equal(ids, dw.blk_ids[0])
+    assert torch.equal(tc, dw.topk_cnt[0]) and torch.equal(tk, dw.topk[0])
+    assert torch.equal(out, grp.out) and torch.equal(lse, grp.lse)
+    ref = oracle.run_layers(wl)
+    compare_run(pipeline.outputs(dw), ref, cfg, what="fused")

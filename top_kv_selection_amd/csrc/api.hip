@@ -167,6 +167,39 @@ int32_t do_attend(const csa2_cfg *c, int32_t n_layers, int32_t n_q, const void *
     return hip_status(launch_attend(p, pl, c->head_dim, c->dtype, st));
 }
 
+// ---- fused decode layer group: block scoring -> pool + token scoring ->
+// token Top-K + attention -> combine (4 launches instead of 6).  Used when the
+// block pass is split over workgroups (few queries), the keys of a query fit
+// one workgroup's registers, and the attention takes the MFMA path.
+struct FusedPlan {
+    bool ok;
+    SelectPlan idx;
+    AttendPlan att;
+    int64_t blk_stride, tok_stride;
+    size_t head, blk_off, tok_off, tok_hist_off, part_off, tail;
+};
+
+FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
+{
+    FusedPlan f{};
+    const long long n_elig_max = (long long)(T - 1) / c->block + 1;
+    f.idx = plan_index(n_q, T, c->block, c->pool, c->d_idx);
+    f.att = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
+    f.ok = c->top_k >= 1 && f.idx.split && n_elig_max <= kMaxCandidates && f.att.mfma &&
+           f.att.keys_per_split <= kAttendRowChunk && f.idx.chunk <= kFusedMaxChunk &&
+           c->pool <= kFusedPoolLds;
+    f.blk_stride = (n_elig_max + 3) / 4 * 4;
+    f.tok_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
+    f.head = (size_t)n_q * 2048 * sizeof(uint32_t);
+    size_t off = 0;
+    f.blk_off = off;      off += round_up((size_t)n_q * f.blk_stride * 4);
+    f.tok_off = off;      off += round_up((size_t)n_q * f.tok_stride * 4);
+    f.tok_hist_off = off; off += round_up((size_t)n_q * 2048 * 4);
+    f.part_off = off;     off += round_up(f.att.part_bytes);
+    f.tail = off;
+    return f;
+}
+
 int32_t do_block_keys(const csa2_cfg *c, const int8_t *k_idx, int32_t n_seq, int32_t T,
                       int32_t blk_begin, int32_t blk_end, int8_t *k_blk, hipStream_t st, bool launch)
 {
@@ -178,6 +211,71 @@ int32_t do_block_keys(const csa2_cfg *c, const int8_t *k_idx, int32_t n_seq, int
     if (!launch || blk_begin >= blk_end) return CSA2_OK;
     BlockKeysParams p{k_idx, k_blk, T, c->block, nblk, blk_begin, blk_end};
     return hip_status(launch_block_keys(p, n_seq, c->d_idx, st));
+}
+
+int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int32_t n_q,
+                          const int8_t *q_idx, const int32_t *q_seq, const int32_t *q_pos,
+                          const int8_t *k_idx, int8_t *k_blk, int32_t blk_update_begin,
+                          int32_t n_seq, int32_t T, const void *q, const void *k_main,
+                          const void *v_main, const void *k_swa, const void *v_swa,
+                          int32_t swa_first, int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt,
+                          int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *ws,
+                          size_t ws_bytes, hipStream_t st, const FusedPlan &f)
+{
+    // the argument checks of the separate stages (nothing launched)
+    if (int32_t e = do_index(c, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, n_seq, T, blk_ids, blk_cnt,
+                             ws, ws_bytes, st, false))
+        return e;
+    if (int32_t e = do_topk(c, n_q, q_idx, q_seq, q_pos, k_idx, T, blk_ids, blk_cnt, topk, topk_cnt,
+                            ws, ws_bytes, st, false))
+        return e;
+    if (int32_t e = do_attend(c, n_layers, n_q, q, q_seq, q_pos, k_main, v_main, n_seq, T, k_swa, v_swa,
+                              swa_first, swa_len, topk, topk_cnt, out, lse, ws, ws_bytes, st, false))
+        return e;
+    if (mode == CSA2_FULL)
+        if (int32_t e = do_block_keys(c, k_idx, n_seq, T, blk_update_begin, T / c->block, k_blk, st, false))
+            return e;
+    if (!aligned16(ws)) return CSA2_E_ALIGN;
+    uint32_t *head = (uint32_t *)ws;
+    char *tail = (char *)ws + round_up(f.head);
+    uint32_t *blk_keys = (uint32_t *)(tail + f.blk_off);
+    uint32_t *tok_keys = (uint32_t *)(tail + f.tok_off);
+    uint32_t *tok_hist = (uint32_t *)(tail + f.tok_hist_off);
+    float *part = (float *)(tail + f.part_off);
+
+    if (mode == CSA2_FULL)
+        if (int32_t e = do_block_keys(c, k_idx, n_seq, T, blk_update_begin, T / c->block, k_blk, st, true))
+            return e;
+    IndexParams ip{};
+    ip.q_idx = q_idx; ip.q_seq = q_seq; ip.q_pos = q_pos; ip.k_idx = k_idx; ip.k_blk = k_blk;
+    ip.k_blk_store = mode == CSA2_FULL ? k_blk : nullptr;
+    ip.tok_hist_clear = tok_hist;
+    ip.T = T; ip.B = c->block; ip.P = c->pool; ip.n_q = n_q; ip.G = f.idx.G; ip.chunk = f.idx.chunk;
+    ip.nblk = T / c->block;
+    ip.ws_keys = blk_keys; ip.ws_stride = f.blk_stride; ip.ws_hist = head;
+    ip.blk_ids = blk_ids; ip.blk_cnt = blk_cnt;
+    if (int32_t e = hip_status(launch_index_blocks(ip, f.idx, c->d_idx, st, false))) return e;
+
+    PoolTokensParams pp{};
+    pp.q_idx = q_idx; pp.q_seq = q_seq; pp.q_pos = q_pos; pp.k_idx = k_idx;
+    pp.T = T; pp.B = c->block; pp.P = c->pool; pp.n_q = n_q; pp.G = f.idx.G; pp.chunk = f.idx.chunk;
+    pp.blk_keys = blk_keys; pp.blk_stride = f.blk_stride; pp.blk_hist = head;
+    pp.blk_ids = blk_ids; pp.blk_cnt = blk_cnt;
+    pp.tok_keys = tok_keys; pp.tok_stride = f.tok_stride; pp.tok_hist = tok_hist;
+    if (int32_t e = hip_status(launch_pool_tokens(pp, c->d_idx, st))) return e;
+
+    AttendParams ap{};
+    ap.q = q; ap.q_seq = q_seq; ap.q_pos = q_pos; ap.k_main = k_main; ap.v_main = v_main;
+    ap.n_seq = n_seq; ap.T = T;
+    ap.k_swa = k_swa; ap.v_swa = v_swa; ap.swa_first = swa_first; ap.swa_len = std::max(swa_len, 1);
+    ap.topk = topk; ap.topk_cnt = topk_cnt; ap.K = c->top_k; ap.W = c->window;
+    ap.n_q = n_q; ap.n_layers = n_layers; ap.H = c->n_heads;
+    ap.scale_log2 = scale_log2_of(c);
+    ap.out = out; ap.lse = lse; ap.ws_part = part;
+    ap.sel_keys = tok_keys; ap.sel_stride = f.tok_stride; ap.sel_hist = tok_hist;
+    ap.sel_pool = blk_ids; ap.sel_pool_cnt = blk_cnt; ap.sel_B = c->block; ap.sel_P = c->pool;
+    ap.topk_out = topk; ap.topk_cnt_out = topk_cnt; ap.blk_hist_clear = head;
+    return hip_status(launch_attend(ap, f.att, c->head_dim, c->dtype, st, true));
 }
 
 }  // namespace
@@ -212,7 +310,10 @@ int32_t csa2_workspace_bytes(const csa2_cfg *c, int32_t n_q, int32_t T, int32_t 
     const AttendPlan pa = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
     const size_t ctr = std::max(select_head_bytes(n_q, pi.split), select_head_bytes(n_q, pt.split));
     const size_t data = std::max({pi.key_bytes, pt.key_bytes, pa.part_bytes});
-    *bytes = round_up(ctr) + round_up(data);
+    size_t need = round_up(ctr) + round_up(data);
+    const FusedPlan f = plan_fused(c, n_q, T, n_layers);
+    if (f.ok) need = std::max(need, round_up(f.head) + f.tail);
+    *bytes = need;
     return CSA2_OK;
 }
 
@@ -301,6 +402,14 @@ int32_t csa2_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int3
     const bool selects = mode == CSA2_FULL || mode == CSA2_REINDEX;
     const bool window_only = mode == CSA2_SWA;
     if (mode == CSA2_REUSE && (!topk || !topk_cnt)) return CSA2_E_NULL;
+    if (selects) {
+        const FusedPlan f = plan_fused(c, n_q, T, n_layers);
+        if (f.ok && ws && ws_bytes >= round_up(f.head) + f.tail)
+            return fused_layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk,
+                                     blk_update_begin, n_seq, T, q, k_main, v_main, k_swa, v_swa,
+                                     swa_first, swa_len, blk_ids, blk_cnt, topk, topk_cnt, out, lse,
+                                     ws, ws_bytes, st, f);
+    }
     // every stage is checked before the first launch, then all are launched
     for (int pass = 0; pass < 2; pass++) {
         const bool launch = pass == 1;

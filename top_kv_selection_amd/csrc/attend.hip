@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void k_attend_generic(AttendParams p)
 // ============================================================ MFMA kernel
 constexpr int kWaves = 8;                      // waves per workgroup, 32 keys each per step
 constexpr int kStepKeys = kWaves * 32;         // keys per workgroup step
-constexpr int kRowChunk = 2048;                // row codes staged in LDS at once
+constexpr int kRowChunk = kAttendRowChunk;     // row codes staged in LDS at once
 constexpr int kVtStride = 40;                  // bf16 per V^T row in LDS (32 keys + pad)
 constexpr int kHeadRec = 4 + 128;              // split record per head: max, sum, 2 pad, acc[128]
 constexpr int kPartFloats = 16 * kHeadRec;     // one split record (16 heads), 16-byte aligned
@@ -138,11 +138,16 @@ __device__ __forceinline__ int slot_key(int g, int e) { return (e < 4) ? 4 * g +
 // with the query count padded to a multiple of 8, so with round-robin XCD
 // dispatch every layer of a query runs on one XCD and the shared main rows
 // are fetched from HBM once and then hit that XCD's L2.
+template <bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
 {
+    constexpr int NT = kWaves * 64, IPT = kLdsKeys / NT;
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[kWaves][128 * kVtStride];
     __shared__ float s_ml[kWaves][16][2];
     __shared__ int s_rows[kRowChunk];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[FUSED ? kHist2Words : 4];
+    __shared__ int32_t s_pool[FUSED ? kFusedPoolLds : 4];
+    __shared__ uint32_t s_sm[NT / 64 + 4];
 
     const int HG = p.H / 16;
     const int id = blockIdx.x;
@@ -156,8 +161,42 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
 
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
     const int s = p.q_seq[i], t = p.q_pos[i];
-    const int cnt = p.topk ? p.topk_cnt[i] : 0;
     const Window win = window_of(t, p.W, p.swa_first, p.swa_len);
+    int cnt;
+    if constexpr (FUSED) {
+        // Exact token Top-K from the token keys (same selection as the
+        // standalone Top-K call); selected slots in this workgroup's share of
+        // the key list go straight into s_rows.
+        HistRegs<NT> hr;
+        load_hist<NT>(p.sel_hist + (size_t)i * kRadixBins, hr);
+        uint32_t k[IPT];
+        load_keys_global<IPT>(p.sel_keys + (size_t)i * p.sel_stride, (int)p.sel_stride, k);
+        const int n_pool = p.sel_pool_cnt[i];
+        const int B = p.sel_B;
+        for (int r = threadIdx.x; r < n_pool; r += NT) s_pool[r] = p.sel_pool[(size_t)i * p.sel_P + r];
+        hist_to_lds<NT>(hr, s_hist);
+        const int n_cand = n_pool * B;
+        mask_keys<IPT>(n_cand, k);
+        const Threshold th = threshold_regs<NT, IPT>(k, n_cand, (uint32_t)p.K, s_hist, s_sm);
+        const bool writer = (l == 0 && hg == 0 && split == 0);
+        int32_t *out_tk = p.topk_out + (size_t)i * p.K;
+        const int kb0 = split * p.keys_per_split;
+        auto emit = [&](uint32_t slot, int c) {
+            const int r = c / B;
+            const int pos = s_pool[r] * B + (c - r * B);
+            const int x = (int)slot - kb0;
+            if (x >= 0 && x < p.keys_per_split) s_rows[x] = pos;
+            if (writer && (int)slot < p.K) out_tk[slot] = pos;
+        };
+        cnt = (int)compact_regs<NT, IPT>(k, th, emit, s_sm);
+        if (writer) {
+            for (int o = cnt + (int)threadIdx.x; o < p.K; o += NT) out_tk[o] = -1;
+            if (threadIdx.x == 0) p.topk_cnt_out[i] = cnt;
+            for (int b = threadIdx.x; b < kRadixBins; b += NT) p.blk_hist_clear[(size_t)i * kRadixBins + b] = 0u;
+        }
+    } else {
+        cnt = p.topk ? p.topk_cnt[i] : 0;
+    }
     const int n_keys = cnt + win.nw;
     // this workgroup's share of the key list (whole steps of kStepKeys keys)
     const int k_begin = min(n_keys, split * p.keys_per_split);
@@ -177,7 +216,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
             const int kk = min(kc + x, k_end - 1);
             s_rows[x] = (kk < cnt) ? tk[kk] : -(win.w0 + (kk - cnt) - p.swa_first) - 1;
         }
-        __syncthreads();
+        lds_barrier();
     };
     auto row_ptr = [&](int code, const uint16_t *mbase, const uint16_t *wbase) -> const uint16_t * {
         return code >= 0 ? mbase + (size_t)code * 128 : wbase + (size_t)(-code - 1) * 128;
@@ -267,7 +306,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         for (int e = 0; e < 8; e++) pb[e] = __builtin_bit_cast(__bf16, f32_to_bf16(pr[e]));
 #pragma unroll
         for (int m = 0; m < 8; m++) acc[m] *= alpha;
-        __syncthreads();
+        lds_barrier();
         // O^T += V^T P^T over the 8 dim tiles
 #pragma unroll
         for (int m = 0; m < 8; m++) {
@@ -277,7 +316,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
             const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
             acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), pb, acc[m], 0, 0, 0);
         }
-        __syncthreads();
+        lds_barrier();
     };
 
     // Software pipeline: the loads of step s+1 are issued into the registers
@@ -287,7 +326,22 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
     bf16x8_t ka[2][4];
     uint4 vv[8];
     if (k_begin < k_end) {
-        stage_rows(k_begin);
+        if constexpr (FUSED) {
+            // main slots were written by the selection; add the window and
+            // repeat the last key in the slots past the end
+            lds_barrier();
+            const int kps = p.keys_per_split;
+            for (int x = threadIdx.x; x < kps; x += NT) {
+                const int kk = k_begin + x;
+                if (kk >= cnt && kk < k_end) s_rows[x] = -(win.w0 + (kk - cnt) - p.swa_first) - 1;
+            }
+            lds_barrier();
+            const int last = s_rows[k_end - 1 - k_begin];
+            for (int x = k_end - k_begin + (int)threadIdx.x; x < kps; x += NT) s_rows[x] = last;
+            lds_barrier();
+        } else {
+            stage_rows(k_begin);
+        }
         load_kv(k_begin, ka, vv);
         for (int kb = k_begin; kb < k_end; kb += kStepKeys) {
             const int kn = kb + kStepKeys;
@@ -313,7 +367,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         s_ml[w][r16][0] = m_run;
         s_ml[w][r16][1] = l_run;
     }
-    __syncthreads();
+    lds_barrier();
     // thread -> (head hh, dims d0 .. d0+3)
     const int hh = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 4;
     float M = -INFINITY;
@@ -419,7 +473,8 @@ AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dt
     return pl;
 }
 
-hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, int dtype, hipStream_t st)
+hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, int dtype, hipStream_t st,
+                         bool fused_select)
 {
     if (p0.n_q <= 0 || p0.n_layers <= 0) return hipSuccess;
     AttendParams p = p0;
@@ -428,7 +483,8 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
         p.n_splits = pl.n_splits;
         p.keys_per_split = pl.keys_per_split;
         const long long n_wg = (long long)p.n_q_pad * pl.n_splits * (p.H / 16) * p.n_layers;
-        hipLaunchKernelGGL(k_attend_mfma, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+        if (fused_select) hipLaunchKernelGGL(k_attend_mfma<true>, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+        else hipLaunchKernelGGL(k_attend_mfma<false>, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
         if (pl.n_splits > 1) {
             const long long n_rows = (long long)p.n_q * (p.H / 16) * p.n_layers;
             hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)n_rows), dim3(512), 0, st, p);

@@ -25,6 +25,24 @@ constexpr uint32_t kRadixMask = kRadixBins - 1;
 constexpr uint32_t kKeyBias = 1u << 21;
 constexpr int kLdsKeys = 16384;            // keys held in LDS by one workgroup
 constexpr int kLdsKeysPadded = kLdsKeys + kLdsKeys / 32;
+// Histograms in LDS also carry one pad word per 32 bins, so that the wave that
+// walks them (32 consecutive bins per lane) reads without bank conflicts.  A
+// pass-2 histogram is followed by 64 trash words (see threshold_regs); LDS
+// arrays holding two histograms are 2 * kHistWords + 64 words.
+constexpr int kHistWords = kRadixBins + kRadixBins / 32;
+constexpr int kHist2Words = 2 * kHistWords + 64;
+__device__ __forceinline__ int hist_pad(int b) { return b + (b >> 5); }
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits
+// for every outstanding global store of the wave (a full memory round trip);
+// no kernel here has one wave read another wave's global writes within a
+// launch (that data goes through LDS), so LDS ordering is all they need.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // LDS index with one pad word per 32 keys: thread-contiguous ranges of 32
 // keys then fall into different banks.
@@ -41,6 +59,20 @@ struct GlobalKeys {
     __device__ __forceinline__ uint32_t operator()(int i) const { return p[i]; }
 };
 
+// Inclusive prefix sum across the 64 lanes of a wave with DPP moves (row
+// shifts, then row broadcasts), which stay in the VALU instead of the LDS
+// crossbar that __shfl_up uses.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
+{
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
 // Exclusive prefix sum of one value per thread over a workgroup of NT threads
 // (NT a multiple of 64).  `sm` holds NT/64 + 1 words; the workgroup total is
 // returned in `total`.  Must be reached by every thread.
@@ -49,29 +81,19 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t &total,
 {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) sm[wid] = x;
-    __syncthreads();
+    lds_barrier();
     if (wid == 0) {
-        uint32_t w = (lane < NW) ? sm[lane] : 0u;
-        uint32_t s = w;
-#pragma unroll
-        for (int o = 1; o < NW; o <<= 1) {
-            uint32_t y = __shfl_up(s, o, 64);
-            if (lane >= o) s += y;
-        }
+        const uint32_t w = (lane < NW) ? sm[lane] : 0u;
+        const uint32_t s = wave_incl_scan(w);
         if (lane < NW) sm[lane] = s - w;
         if (lane == NW - 1) sm[NW] = s;
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t r = sm[wid] + x - v;
     total = sm[NW];
-    __syncthreads();
+    lds_barrier();
     return r;
 }
 
@@ -87,23 +109,23 @@ __device__ __forceinline__ void find_bin(const uint32_t *hist, uint32_t n, uint3
     const int tid = threadIdx.x;
     uint32_t local = 0;
 #pragma unroll
-    for (int j = 0; j < BPT; j++) local += hist[kRadixBins - 1 - (tid * BPT + j)];
+    for (int j = 0; j < BPT; j++) local += hist[hist_pad(kRadixBins - 1 - (tid * BPT + j))];
     uint32_t total;
     uint32_t a = base + block_excl_scan<NT>(local, total, sm);
 #pragma unroll
     for (int j = 0; j < BPT; j++) {
         const int b = kRadixBins - 1 - (tid * BPT + j);
-        const uint32_t h = hist[b];
+        const uint32_t h = hist[hist_pad(b)];
         if (a < n && a + h >= n) {
             sm[NT / 64 + 1] = (uint32_t)b;
             sm[NT / 64 + 2] = a;
         }
         a += h;
     }
-    __syncthreads();
+    lds_barrier();
     bin = sm[NT / 64 + 1];
     above = sm[NT / 64 + 2];
-    __syncthreads();
+    lds_barrier();
 }
 
 // Selection rule: take key > thr, and keys == thr while their rank among the
@@ -122,26 +144,26 @@ __device__ Threshold radix_threshold(const Keys &keys, int count, uint32_t n, ui
 {
     const int tid = threadIdx.x;
     if (!have_pass1) {
-        for (int b = tid; b < kRadixBins; b += NT) hist[b] = 0;
-        __syncthreads();
-        for (int i = tid; i < count; i += NT) atomicAdd(&hist[keys(i) >> kRadixBits], 1u);
+        for (int b = tid; b < kHistWords; b += NT) hist[b] = 0;
+        lds_barrier();
+        for (int i = tid; i < count; i += NT) atomicAdd(&hist[hist_pad(keys(i) >> kRadixBits)], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     // bin 0 holds only the zero keys (valid keys are >= 2^20)
     const uint32_t n_valid = (uint32_t)count - hist[0];
     if (n_valid <= n) {
-        __syncthreads();
+        lds_barrier();
         return {0u, 0u};
     }
     uint32_t b1, above1;
     find_bin<NT>(hist, n, 0u, b1, above1, sm);
-    for (int b = tid; b < kRadixBins; b += NT) hist[b] = 0;
-    __syncthreads();
+    for (int b = tid; b < kHistWords; b += NT) hist[b] = 0;
+    lds_barrier();
     for (int i = tid; i < count; i += NT) {
         const uint32_t k = keys(i);
-        if ((k >> kRadixBits) == b1) atomicAdd(&hist[k & kRadixMask], 1u);
+        if ((k >> kRadixBits) == b1) atomicAdd(&hist[hist_pad(k & kRadixMask)], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t b2, above2;
     find_bin<NT>(hist, n, above1, b2, above2, sm);
     return {(b1 << kRadixBits) | b2, n - above2};
@@ -182,9 +204,11 @@ __device__ uint32_t ordered_compact(const Keys &keys, int count, Threshold th, E
     return total;
 }
 
-// find_bin done by wave 0 alone: lane l owns 32 bins walked from the top, so
-// one wave scan replaces the workgroup-wide scans (one barrier in total).
-// `res` is 2 LDS words.  Must be reached by every thread.
+// find_bin done by wave 0 alone, in two levels: lane l sums 32 bins (walked
+// from the top), a wave scan and a ballot find the one lane whose bins hold the
+// crossing, then that lane's 32 bins are spread over 32 lanes for a second
+// scan and ballot.  No per-bin loop; one barrier.  `res` is 2 LDS words.
+// Requires base < n <= base + (total count).  Must be reached by every thread.
 template <int NT>
 __device__ __forceinline__ void find_bin_wave(const uint32_t *hist, uint32_t n, uint32_t base,
                                               uint32_t &bin, uint32_t &above, uint32_t *res)
@@ -192,34 +216,25 @@ __device__ __forceinline__ void find_bin_wave(const uint32_t *hist, uint32_t n, 
     static_assert(kRadixBins == 64 * 32, "one wave covers the bins, 32 per lane");
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
-        // bins of lane l: 2047 - 32l - j, j = 0..31 (descending)
-        uint32_t h[32];
-        const uint4 *src = reinterpret_cast<const uint4 *>(hist + kRadixBins - 32 * (lane + 1));
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const uint4 v = src[u];      // ascending bins; h[] is filled descending
-            h[31 - 4 * u] = v.x; h[30 - 4 * u] = v.y; h[29 - 4 * u] = v.z; h[28 - 4 * u] = v.w;
-        }
+        const uint32_t *src = hist + hist_pad(kRadixBins - 32 * (lane + 1));   // conflict-free
         uint32_t local = 0;
 #pragma unroll
-        for (int j = 0; j < 32; j++) local += h[j];
-        uint32_t incl = local;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-        }
-        uint32_t a = base + incl - local;
-#pragma unroll
-        for (int j = 0; j < 32; j++) {
-            if (a < n && a + h[j] >= n) {
-                res[0] = (uint32_t)(kRadixBins - 1 - (32 * lane + j));
-                res[1] = a;
-            }
-            a += h[j];
+        for (int j = 0; j < 32; j++) local += src[j];
+        const uint32_t a0 = base + wave_incl_scan(local) - local;   // count above this lane's bins
+        const unsigned long long hit = __ballot(a0 < n && a0 + local >= n);
+        const int L = __builtin_ctzll(hit);
+        const uint32_t aL = (uint32_t)__builtin_amdgcn_readlane((int)a0, L);
+        // bin of lane j (< 32): 2047 - 32L - j, descending
+        const int b = kRadixBins - 1 - 32 * L - lane;
+        const uint32_t h = (lane < 32) ? hist[hist_pad(b)] : 0u;
+        const uint32_t ab = aL + wave_incl_scan(h) - h;
+        const unsigned long long hit2 = __ballot(lane < 32 && ab < n && ab + h >= n);
+        if (lane == __builtin_ctzll(hit2)) {
+            res[0] = (uint32_t)b;
+            res[1] = ab;
         }
     }
-    __syncthreads();
+    lds_barrier();
     bin = res[0];
     above = res[1];
 }
@@ -236,18 +251,23 @@ __device__ Threshold threshold_regs(const uint32_t (&k)[IPT], int count, uint32_
     const int tid = threadIdx.x;
     const uint32_t n_valid = (uint32_t)count - hist[0];
     if (n_valid <= n) {
-        __syncthreads();
+        lds_barrier();
         return {0u, 0u};
     }
     uint32_t b1, above1;
     find_bin_wave<NT>(hist, n, 0u, b1, above1, sm + NT / 64 + 1);
     // pass 2 into a second histogram (the barrier in find_bin_wave has
-    // ordered every read of the first); the first is zeroed for reuse later
-    uint32_t *hist2 = hist + kRadixBins;
+    // ordered every read of the first).  Branch-free: a key outside bin b1
+    // counts into a trash word of its own lane (past the histogram), so every
+    // key costs one LDS atomic and no divergent branch.
+    uint32_t *hist2 = hist + kHistWords;
+    const int trash = kHistWords + (threadIdx.x & 63);
 #pragma unroll
-    for (int j = 0; j < IPT; j++)
-        if ((k[j] >> kRadixBits) == b1) atomicAdd(&hist2[k[j] & kRadixMask], 1u);
-    __syncthreads();
+    for (int j = 0; j < IPT; j++) {
+        const int slot = ((k[j] >> kRadixBits) == b1) ? hist_pad(k[j] & kRadixMask) : trash;
+        atomicAdd(&hist2[slot], 1u);
+    }
+    lds_barrier();
     uint32_t b2, above2;
     find_bin_wave<NT>(hist2, n, above1, b2, above2, sm + NT / 64 + 1);
     return {(b1 << kRadixBits) | b2, n - above2};
@@ -302,42 +322,75 @@ template <int NT>
 __device__ __forceinline__ void flush_hist(const uint32_t *hist, uint32_t *ghist)
 {
     for (int b = threadIdx.x; b < kRadixBins; b += NT) {
-        const uint32_t c = hist[b];
+        const uint32_t c = hist[hist_pad(b)];
         if (c) atomicAdd(&ghist[b], c);
     }
 }
 
-// Moves a global histogram into LDS hist[0..2048), leaves the global one
-// zeroed and clears the pass-2 histogram hist[2048..4096).
+// Global histogram -> registers (issue only; pair with store_hist after other
+// loads have been issued), so its round trip overlaps the key loads.
 template <int NT>
-__device__ __forceinline__ void take_hist(uint32_t *ghist, uint32_t *hist)
+struct HistRegs {
+    uint32_t v[kRadixBins / NT];
+};
+template <int NT>
+__device__ __forceinline__ void load_hist(const uint32_t *ghist, HistRegs<NT> &h)
 {
-    for (int b = threadIdx.x; b < kRadixBins; b += NT) {
-        hist[b] = ghist[b];
+#pragma unroll
+    for (int u = 0; u < kRadixBins / NT; u++) h.v[u] = ghist[u * NT + threadIdx.x];
+}
+// Writes the loaded counts into LDS hist[0..) (padded) and clears the pass-2
+// histogram, leaving the global one as it is (other workgroups still read it);
+// ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void hist_to_lds(const HistRegs<NT> &h, uint32_t *hist)
+{
+#pragma unroll
+    for (int u = 0; u < kRadixBins / NT; u++) hist[hist_pad(u * NT + threadIdx.x)] = h.v[u];
+    for (int b = threadIdx.x; b < kHistWords; b += NT) hist[kHistWords + b] = 0u;
+    lds_barrier();
+}
+
+// Writes the loaded counts into LDS hist[0..) (padded), clears the pass-2
+// histogram, leaves the global one zeroed, and ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void store_hist(const HistRegs<NT> &h, uint32_t *ghist, uint32_t *hist)
+{
+#pragma unroll
+    for (int u = 0; u < kRadixBins / NT; u++) {
+        const int b = u * NT + threadIdx.x;
+        hist[hist_pad(b)] = h.v[u];
         ghist[b] = 0u;
-        hist[kRadixBins + b] = 0u;
     }
-    __syncthreads();
+    for (int b = threadIdx.x; b < kHistWords; b += NT) hist[kHistWords + b] = 0u;
+    lds_barrier();
 }
 
 // Loads this thread's IPT keys of a global key row (16-byte aligned, `count`
 // valid entries) into registers, 0 past the end.
+// Issues the loads of this thread's IPT keys of a global key row that holds
+// `row_len` words (a multiple of 4, 16-byte aligned); entries past the row are
+// 0.  The count of valid keys is applied later by mask_keys, so the loads do
+// not wait for it.
 template <int IPT>
-__device__ __forceinline__ void load_keys_global(const uint32_t *g, int count, uint32_t (&k)[IPT])
+__device__ __forceinline__ void load_keys_global(const uint32_t *g, int row_len, uint32_t (&k)[IPT])
 {
     const int lo = (int)threadIdx.x * IPT;
     const uint4 *g4 = reinterpret_cast<const uint4 *>(g + lo);
 #pragma unroll
     for (int u = 0; u < IPT / 4; u++) {
-        const int i = lo + 4 * u;
-        if (i + 4 <= count) {
-            const uint4 v = g4[u];
-            k[4 * u] = v.x; k[4 * u + 1] = v.y; k[4 * u + 2] = v.z; k[4 * u + 3] = v.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++) k[4 * u + e] = (i + e < count) ? g[i + e] : 0u;
-        }
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (lo + 4 * u < row_len) v = g4[u];
+        k[4 * u] = v.x; k[4 * u + 1] = v.y; k[4 * u + 2] = v.z; k[4 * u + 3] = v.w;
     }
+}
+template <int IPT>
+__device__ __forceinline__ void mask_keys(int count, uint32_t (&k)[IPT])
+{
+    const int lo = (int)threadIdx.x * IPT;
+#pragma unroll
+    for (int j = 0; j < IPT; j++)
+        if (lo + j >= count) k[j] = 0u;
 }
 
 template <int IPT>

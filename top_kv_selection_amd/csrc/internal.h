@@ -22,11 +22,29 @@ struct IndexParams {
     const int32_t *q_seq, *q_pos;
     const int8_t *k_idx, *k_blk;
     int8_t *k_blk_store;    // non-null: store each query's own block key when the query completes it
+    uint32_t *tok_hist_clear;   // non-null (fused layer group): zero [n_q][2048] token histograms
     int T, B, P, n_q, G, chunk, nblk;
     uint32_t *ws_keys;
     int64_t ws_stride;
     uint32_t *ws_hist;      // [n_q][2048] top-11-bit histograms (split launches)
     int32_t *blk_ids, *blk_cnt;
+};
+
+// Fused decode stage after the block scoring launch: every workgroup derives
+// the exact pool from the block keys and histogram, writes the pooled ids of
+// its own block range and scores their tokens.
+struct PoolTokensParams {
+    const int8_t *q_idx;
+    const int32_t *q_seq, *q_pos;
+    const int8_t *k_idx;
+    int T, B, P, n_q, G, chunk;     // G, chunk: the block partition of the scoring launch
+    const uint32_t *blk_keys;       // [n_q][blk_stride] from the scoring launch
+    int64_t blk_stride;
+    const uint32_t *blk_hist;       // [n_q][2048] from the scoring launch (read only)
+    int32_t *blk_ids, *blk_cnt;
+    uint32_t *tok_keys;             // [n_q][tok_stride]
+    int64_t tok_stride;
+    uint32_t *tok_hist;             // [n_q][2048], zeroed by the scoring launch
 };
 
 struct TopkParams {
@@ -54,6 +72,16 @@ struct AttendParams {
     void *out;
     float *lse;
     float *ws_part;         // split records (n_splits > 1)
+    // fused token selection (layer-group decode path): the key list comes from
+    // the token keys instead of topk, and topk/topk_cnt are written
+    const uint32_t *sel_keys;   // [n_q][sel_stride] token keys
+    int64_t sel_stride;
+    const uint32_t *sel_hist;   // [n_q][2048] their top-11-bit histogram
+    const int32_t *sel_pool;    // [n_q][sel_P] pooled block ids
+    const int32_t *sel_pool_cnt;
+    int sel_B, sel_P;
+    int32_t *topk_out, *topk_cnt_out;
+    uint32_t *blk_hist_clear;   // [n_q][2048] block histograms to zero once read
     int n_splits, keys_per_split;
     int n_q_pad;            // n_q rounded up to a multiple of 8 (XCD-aware numbering)
 };
@@ -81,11 +109,16 @@ AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dt
 
 hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hipStream_t st);
 hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &plan, int d_idx,
-                               hipStream_t st);
+                               hipStream_t st, bool with_select = true);
 hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &plan, int d_idx,
                               hipStream_t st);
 hipError_t launch_attend(const AttendParams &p, const AttendPlan &plan, int D, int dtype,
-                         hipStream_t st);
+                         hipStream_t st, bool fused_select = false);
+hipError_t launch_pool_tokens(const PoolTokensParams &p, int d_idx, hipStream_t st);
+
+constexpr int kAttendRowChunk = 2048;   // key-list entries one attention workgroup stages at once
+constexpr int kFusedPoolLds = 2048;     // pooled block ids the fused attention keeps in LDS
+constexpr int kFusedMaxChunk = 1024;    // blocks per workgroup of the fused pool stage
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t st);
 
 }  // namespace csa2

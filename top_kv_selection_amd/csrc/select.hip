@@ -100,7 +100,7 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
 {
     constexpr int LPR = DIDX / 16, RPP = NT / LPR, IPT = kLdsKeys / NT;
     __shared__ uint32_t s_keys[SPLIT ? 4 : kLdsKeysPadded];
-    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2 * kRadixBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
     __shared__ uint32_t s_sm[NT / 64 + 4];
     const int q = blockIdx.x % p.n_q;
     const int g = blockIdx.x / p.n_q;
@@ -115,6 +115,9 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     int8_t *own_store = store_own ? p.k_blk_store + ((size_t)s * p.nblk + jt) * DIDX + part * 16 : nullptr;
     const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX + part * 16;
 
+    if (p.tok_hist_clear != nullptr && g == 0)
+        for (int b = tid; b < kRadixBins; b += NT) p.tok_hist_clear[(size_t)q * kRadixBins + b] = 0u;
+
     if (n_elig <= p.P) {   // the pool is every eligible block
         for (int j = g * NT + tid; j < p.P; j += p.G * NT) ids[j] = (j < n_elig) ? j : -1;
         if (g == 0 && tid == 0) p.blk_cnt[q] = n_elig;
@@ -122,8 +125,8 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
             *reinterpret_cast<int4 *>(own_store) = block_key_part<DIDX>(own_rows, p.B);
         return;
     }
-    for (int b = tid; b < 2 * kRadixBins; b += NT) s_hist[b] = 0;
-    __syncthreads();
+    for (int b = tid; b < kHist2Words; b += NT) s_hist[b] = 0;
+    lds_barrier();
 
     const int4 qv = *reinterpret_cast<const int4 *>(p.q_idx + (size_t)q * DIDX + part * 16);
     const int lo = SPLIT ? min(n_elig, g * p.chunk) : 0;
@@ -153,11 +156,11 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
                 const uint32_t key = (uint32_t)(acc + (int)kKeyBias);
                 if (SPLIT) gkeys[j] = key;
                 else s_keys[lds_pad(j)] = key;
-                atomicAdd(&s_hist[key >> kRadixBits], 1u);
+                atomicAdd(&s_hist[hist_pad(key >> kRadixBits)], 1u);
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (SPLIT) {   // the selection runs in k_index_select, after this launch
         flush_hist<NT>(s_hist, ghist);
         return;
@@ -179,26 +182,30 @@ template <int NT>
 __global__ __launch_bounds__(NT) void k_index_select(IndexParams p)
 {
     constexpr int IPT = kLdsKeys / NT;
-    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2 * kRadixBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
     __shared__ uint32_t s_sm[NT / 64 + 4];
     const int q = blockIdx.x, tid = threadIdx.x;
-    const int t = p.q_pos[q];
-    const int n_elig = t / p.B + 1;
-    if (n_elig <= p.P) return;   // handled by the scoring launch
     int32_t *ids = p.blk_ids + (size_t)q * p.P;
     uint32_t *gkeys = p.ws_keys + (size_t)q * p.ws_stride;
     uint32_t *ghist = p.ws_hist + (size_t)q * kRadixBins;
     const uint32_t cap = (uint32_t)p.P;
     auto emit = [&](uint32_t slot, int i) { if (slot < cap) ids[slot] = i; };
+    // every global load of the selection is issued before the first is used
+    HistRegs<NT> hr;
+    load_hist<NT>(ghist, hr);
+    uint32_t k[IPT];
+    const bool fits = p.ws_stride <= NT * IPT;
+    if (fits) load_keys_global<IPT>(gkeys, (int)p.ws_stride, k);
+    const int t = p.q_pos[q];
+    const int n_elig = t / p.B + 1;
+    if (n_elig <= p.P) return;   // handled by the scoring launch (nothing was stored)
+    store_hist<NT>(hr, ghist, s_hist);
     uint32_t chosen;
-    if (n_elig <= NT * IPT) {
-        uint32_t k[IPT];
-        load_keys_global<IPT>(gkeys, n_elig, k);
-        take_hist<NT>(ghist, s_hist);
+    if (fits) {
+        mask_keys<IPT>(n_elig, k);
         const Threshold th = threshold_regs<NT, IPT>(k, n_elig, cap, s_hist, s_sm);
         chosen = compact_regs<NT, IPT>(k, th, emit, s_sm);
     } else {   // more blocks than one workgroup holds in registers
-        take_hist<NT>(ghist, s_hist);
         const GlobalKeys keys{gkeys};
         const Threshold th = radix_threshold<NT>(keys, n_elig, cap, s_hist, s_sm, true);
         chosen = ordered_compact<NT>(keys, n_elig, th, emit, s_sm);
@@ -208,6 +215,99 @@ __global__ __launch_bounds__(NT) void k_index_select(IndexParams p)
 }
 
 // ---------------------------------------------------------------- token Top-K
+// ---------------------------------------------------------------- fused pool + token scoring
+constexpr int kMaxChunk = 1024;     // blocks per workgroup in the fused stage
+
+template <int NT, int DIDX>
+__global__ __launch_bounds__(NT) void k_pool_tokens(PoolTokensParams p)
+{
+    constexpr int LPR = DIDX / 16, RPP = NT / LPR, IPT = kLdsKeys / NT;
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
+    __shared__ uint32_t s_sm[NT / 64 + 4];
+    __shared__ int32_t s_blk[kMaxChunk];    // pooled blocks of this range ...
+    __shared__ int32_t s_rank[kMaxChunk];   // ... and their ranks in the pool
+    __shared__ uint32_t s_count;
+    const int q = blockIdx.x % p.n_q;
+    const int g = blockIdx.x / p.n_q;
+    const int tid = threadIdx.x, part = tid % LPR;
+
+    // all global loads of the pool selection go out before the first use
+    HistRegs<NT> hr;
+    load_hist<NT>(p.blk_hist + (size_t)q * kRadixBins, hr);
+    uint32_t k[IPT];
+    load_keys_global<IPT>(p.blk_keys + (size_t)q * p.blk_stride, (int)p.blk_stride, k);
+    const int s = p.q_seq[q], t = p.q_pos[q];
+    const int B = p.B;
+    const int n_elig = t / B + 1;
+    const int lo = min(n_elig, g * p.chunk), hi = min(n_elig, lo + p.chunk);
+    if (tid == 0) s_count = 0u;
+
+    if (n_elig <= p.P) {
+        // the pool is every eligible block, rank = id (ids already written)
+        lds_barrier();
+        for (int j = lo + tid; j < hi; j += NT) {
+            s_blk[j - lo] = j;
+            s_rank[j - lo] = j;
+        }
+        if (tid == 0) s_count = (uint32_t)(hi - lo);
+    } else {
+        hist_to_lds<NT>(hr, s_hist);
+        mask_keys<IPT>(n_elig, k);
+        const Threshold th = threshold_regs<NT, IPT>(k, n_elig, (uint32_t)p.P, s_hist, s_sm);
+        int32_t *ids = p.blk_ids + (size_t)q * p.P;
+        auto emit = [&](uint32_t rank, int j) {
+            if (j >= lo && j < hi) {
+                const uint32_t e = atomicAdd(&s_count, 1u);
+                s_blk[e] = j;
+                s_rank[e] = (int)rank;
+                ids[rank] = j;
+            }
+        };
+        compact_regs<NT, IPT>(k, th, emit, s_sm);
+        if (g == 0 && tid == 0) p.blk_cnt[q] = p.P;
+    }
+    for (int b = tid; b < kHistWords; b += NT) s_hist[b] = 0u;
+    lds_barrier();
+
+    // token scores of the pooled blocks in this range; candidate c = rank*B + w
+    const int m = (int)s_count;
+    const int4 qv = *reinterpret_cast<const int4 *>(p.q_idx + (size_t)q * DIDX + part * 16);
+    const int8_t *seq_rows = p.k_idx + (size_t)s * p.T * DIDX + part * 16;
+    uint32_t *tkeys = p.tok_keys + (size_t)q * p.tok_stride;
+    for (int base = 0; base < m * B; base += RPP * kUnroll) {
+        int pos[kUnroll], cidx[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int r = base + u * RPP + tid / LPR;
+            pos[u] = INT32_MAX;
+            cidx[u] = -1;
+            if (r < m * B) {
+                const int e = r / B, w = r - e * B;
+                pos[u] = s_blk[e] * B + w;
+                cidx[u] = s_rank[e] * B + w;
+            }
+        }
+        int4 kv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            kv[u] = make_int4(0, 0, 0, 0);
+            if (pos[u] <= t) kv[u] = *reinterpret_cast<const int4 *>(seq_rows + (size_t)pos[u] * DIDX);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            int acc = dot16_i8(kv[u], qv);
+            acc = row_reduce<LPR>(acc);
+            if (cidx[u] >= 0 && part == 0) {
+                const uint32_t key = (pos[u] <= t) ? (uint32_t)(acc + (int)kKeyBias) : 0u;
+                tkeys[cidx[u]] = key;
+                atomicAdd(&s_hist[hist_pad(key >> kRadixBits)], 1u);
+            }
+        }
+    }
+    lds_barrier();
+    flush_hist<NT>(s_hist, p.tok_hist + (size_t)q * kRadixBins);
+}
+
 // Threshold and ordered emit of a query's Top-K from its keys in registers and
 // its pass-1 histogram in LDS; writes topk/topk_cnt.
 template <int NT, int IPT>
@@ -238,7 +338,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
 {
     constexpr int LPR = DIDX / 16, RPP = NT / LPR, IPT = kLdsKeys / NT;
     __shared__ uint32_t s_keys[SPLIT ? 4 : kLdsKeysPadded];
-    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2 * kRadixBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
     __shared__ int32_t s_pool[SPLIT ? 4 : kPoolLds];
     __shared__ uint32_t s_sm[NT / 64 + 4];
     const int q = blockIdx.x % p.n_q;
@@ -249,8 +349,8 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
     const int n_pool = p.blk_cnt[q];
     const int n_cand = n_pool * B;                    // <= P*B <= kLdsKeys
     const int32_t *pool = p.blk_ids + (size_t)q * p.P;
-    for (int b = tid; b < 2 * kRadixBins; b += NT) s_hist[b] = 0;
-    __syncthreads();
+    for (int b = tid; b < kHist2Words; b += NT) s_hist[b] = 0;
+    lds_barrier();
 
     const int4 qv = *reinterpret_cast<const int4 *>(p.q_idx + (size_t)q * DIDX + part * 16);
     const int lo = SPLIT ? min(n_cand, g * p.chunk) : 0;
@@ -285,11 +385,11 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
                 const uint32_t key = (pos[u] <= t) ? (uint32_t)(acc + (int)kKeyBias) : 0u;
                 if (SPLIT) gkeys[c] = key;
                 else s_keys[lds_pad(c)] = key;
-                atomicAdd(&s_hist[key >> kRadixBits], 1u);
+                atomicAdd(&s_hist[hist_pad(key >> kRadixBits)], 1u);
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (SPLIT) {   // the selection runs in k_topk_select, after this launch
         flush_hist<NT>(s_hist, ghist);
         return;
@@ -303,14 +403,18 @@ template <int NT>
 __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
 {
     constexpr int IPT = kLdsKeys / NT;
-    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2 * kRadixBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
     __shared__ int32_t s_pool[kPoolLds];
     __shared__ uint32_t s_sm[NT / 64 + 4];
     const int q = blockIdx.x;
-    const int n_cand = p.blk_cnt[q] * p.B;
+    uint32_t *ghist = p.ws_hist + (size_t)q * kRadixBins;
+    HistRegs<NT> hr;
+    load_hist<NT>(ghist, hr);
     uint32_t k[IPT];
-    load_keys_global<IPT>(p.ws_keys + (size_t)q * p.ws_stride, n_cand, k);
-    take_hist<NT>(p.ws_hist + (size_t)q * kRadixBins, s_hist);
+    load_keys_global<IPT>(p.ws_keys + (size_t)q * p.ws_stride, (int)p.ws_stride, k);
+    const int n_cand = p.blk_cnt[q] * p.B;
+    store_hist<NT>(hr, ghist, s_hist);
+    mask_keys<IPT>(n_cand, k);
     topk_finish<NT, IPT>(p, q, k, n_cand, s_hist, s_pool, s_sm);
 }
 
@@ -372,22 +476,24 @@ hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hip
 }
 
 template <int DIDX>
-static void launch_index_t(const IndexParams &p, const SelectPlan &pl, hipStream_t st)
+static void launch_index_t(const IndexParams &p, const SelectPlan &pl, hipStream_t st, bool with_select)
 {
     dim3 grid((unsigned)(p.n_q * pl.G));
     if (pl.split) {
         hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
-        hipLaunchKernelGGL((k_index_select<kSelectThreads>), dim3((unsigned)p.n_q), dim3(kSelectThreads), 0, st, p);
+        if (with_select)
+            hipLaunchKernelGGL((k_index_select<kSelectThreads>), dim3((unsigned)p.n_q), dim3(kSelectThreads), 0, st, p);
     } else {
         hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
     }
 }
 
-hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &pl, int d_idx, hipStream_t st)
+hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &pl, int d_idx, hipStream_t st,
+                               bool with_select)
 {
     if (p.n_q <= 0) return hipSuccess;
-    if (d_idx == 64) launch_index_t<64>(p, pl, st);
-    else launch_index_t<32>(p, pl, st);
+    if (d_idx == 64) launch_index_t<64>(p, pl, st, with_select);
+    else launch_index_t<32>(p, pl, st, with_select);
     return hipGetLastError();
 }
 
@@ -408,6 +514,21 @@ hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &pl, int d_i
     if (p.n_q <= 0) return hipSuccess;
     if (d_idx == 64) launch_topk_t<64>(p, pl, st);
     else launch_topk_t<32>(p, pl, st);
+    return hipGetLastError();
+}
+
+template <int DIDX>
+static void launch_pool_tokens_t(const PoolTokensParams &p, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_pool_tokens<kSelectThreads, DIDX>), dim3((unsigned)(p.n_q * p.G)),
+                       dim3(kSelectThreads), 0, st, p);
+}
+
+hipError_t launch_pool_tokens(const PoolTokensParams &p, int d_idx, hipStream_t st)
+{
+    if (p.n_q <= 0) return hipSuccess;
+    if (d_idx == 64) launch_pool_tokens_t<64>(p, st);
+    else launch_pool_tokens_t<32>(p, st);
     return hipGetLastError();
 }
 
