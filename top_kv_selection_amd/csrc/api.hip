@@ -167,13 +167,14 @@ int32_t do_attend(const csa2_cfg *c, int32_t n_layers, int32_t n_q, const void *
     return hip_status(launch_attend(p, pl, c->head_dim, c->dtype, st));
 }
 
-// ---- fused decode layer group: block scoring -> pool + token scoring ->
-// token Top-K + attention -> combine (4 launches instead of 6).  Used when the
-// block pass is split over workgroups (few queries), the keys of a query fit
-// one workgroup's registers, and the attention takes the MFMA path.
+// ---- fused decode layer group: block scoring -> pool selection -> token
+// scoring -> token Top-K inside the attention launch -> combine (5 launches
+// instead of 6, and no standalone Top-K pass).  Used when the selections are
+// split over workgroups (few queries), the keys of a query fit one
+// workgroup's registers, and the attention takes the MFMA path.
 struct FusedPlan {
     bool ok;
-    SelectPlan idx;
+    SelectPlan idx, tok;
     AttendPlan att;
     int64_t blk_stride, tok_stride;
     size_t head, blk_off, tok_off, tok_hist_off, part_off, tail;
@@ -184,10 +185,10 @@ FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
     FusedPlan f{};
     const long long n_elig_max = (long long)(T - 1) / c->block + 1;
     f.idx = plan_index(n_q, T, c->block, c->pool, c->d_idx);
+    f.tok = plan_topk(n_q, c->block, c->pool, c->top_k, c->d_idx);
     f.att = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
-    f.ok = c->top_k >= 1 && f.idx.split && n_elig_max <= kMaxCandidates && f.att.mfma &&
-           f.att.keys_per_split <= kAttendRowChunk && f.idx.chunk <= kFusedMaxChunk &&
-           c->pool <= kFusedPoolLds;
+    f.ok = c->top_k >= 1 && f.idx.split && f.tok.split && n_elig_max <= kMaxCandidates && f.att.mfma &&
+           f.att.keys_per_split <= kAttendRowChunk && c->pool <= kFusedPoolLds;
     f.blk_stride = (n_elig_max + 3) / 4 * 4;
     f.tok_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
     f.head = (size_t)n_q * 2048 * sizeof(uint32_t);
@@ -254,15 +255,20 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     ip.nblk = T / c->block;
     ip.ws_keys = blk_keys; ip.ws_stride = f.blk_stride; ip.ws_hist = head;
     ip.blk_ids = blk_ids; ip.blk_cnt = blk_cnt;
-    if (int32_t e = hip_status(launch_index_blocks(ip, f.idx, c->d_idx, st, false))) return e;
+    // block scoring + pool selection (one workgroup per query): a pool stage
+    // fused into the token scoring would redo the pool selection in each of a
+    // query's scoring workgroups, which was measured slower on MI355X
+    if (int32_t e = hip_status(launch_index_blocks(ip, f.idx, c->d_idx, st, true))) return e;
 
-    PoolTokensParams pp{};
-    pp.q_idx = q_idx; pp.q_seq = q_seq; pp.q_pos = q_pos; pp.k_idx = k_idx;
-    pp.T = T; pp.B = c->block; pp.P = c->pool; pp.n_q = n_q; pp.G = f.idx.G; pp.chunk = f.idx.chunk;
-    pp.blk_keys = blk_keys; pp.blk_stride = f.blk_stride; pp.blk_hist = head;
-    pp.blk_ids = blk_ids; pp.blk_cnt = blk_cnt;
-    pp.tok_keys = tok_keys; pp.tok_stride = f.tok_stride; pp.tok_hist = tok_hist;
-    if (int32_t e = hip_status(launch_pool_tokens(pp, c->d_idx, st))) return e;
+    TopkParams tp{};
+    tp.q_idx = q_idx; tp.q_seq = q_seq; tp.q_pos = q_pos; tp.k_idx = k_idx;
+    tp.blk_ids = blk_ids; tp.blk_cnt = blk_cnt;
+    tp.T = T; tp.B = c->block; tp.P = c->pool; tp.K = c->top_k; tp.n_q = n_q;
+    tp.G = f.tok.G; tp.chunk = f.tok.chunk;
+    tp.ws_keys = tok_keys; tp.ws_stride = f.tok_stride; tp.ws_hist = tok_hist;
+    tp.topk = topk; tp.topk_cnt = topk_cnt;
+    // token scoring only; the Top-K is taken inside the attention launch
+    if (int32_t e = hip_status(launch_topk_tokens(tp, f.tok, c->d_idx, st, false))) return e;
 
     AttendParams ap{};
     ap.q = q; ap.q_seq = q_seq; ap.q_pos = q_pos; ap.k_main = k_main; ap.v_main = v_main;
@@ -274,7 +280,7 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     ap.out = out; ap.lse = lse; ap.ws_part = part;
     ap.sel_keys = tok_keys; ap.sel_stride = f.tok_stride; ap.sel_hist = tok_hist;
     ap.sel_pool = blk_ids; ap.sel_pool_cnt = blk_cnt; ap.sel_B = c->block; ap.sel_P = c->pool;
-    ap.topk_out = topk; ap.topk_cnt_out = topk_cnt; ap.blk_hist_clear = head;
+    ap.topk_out = topk; ap.topk_cnt_out = topk_cnt; ap.blk_hist_clear = nullptr;
     return hip_status(launch_attend(ap, f.att, c->head_dim, c->dtype, st, true));
 }
 

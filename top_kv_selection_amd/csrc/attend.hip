@@ -192,7 +192,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         if (writer) {
             for (int o = cnt + (int)threadIdx.x; o < p.K; o += NT) out_tk[o] = -1;
             if (threadIdx.x == 0) p.topk_cnt_out[i] = cnt;
-            for (int b = threadIdx.x; b < kRadixBins; b += NT) p.blk_hist_clear[(size_t)i * kRadixBins + b] = 0u;
+            if (p.blk_hist_clear)
+                for (int b = threadIdx.x; b < kRadixBins; b += NT) p.blk_hist_clear[(size_t)i * kRadixBins + b] = 0u;
         }
     } else {
         cnt = p.topk ? p.topk_cnt[i] : 0;

@@ -30,23 +30,6 @@ struct IndexParams {
     int32_t *blk_ids, *blk_cnt;
 };
 
-// Fused decode stage after the block scoring launch: every workgroup derives
-// the exact pool from the block keys and histogram, writes the pooled ids of
-// its own block range and scores their tokens.
-struct PoolTokensParams {
-    const int8_t *q_idx;
-    const int32_t *q_seq, *q_pos;
-    const int8_t *k_idx;
-    int T, B, P, n_q, G, chunk;     // G, chunk: the block partition of the scoring launch
-    const uint32_t *blk_keys;       // [n_q][blk_stride] from the scoring launch
-    int64_t blk_stride;
-    const uint32_t *blk_hist;       // [n_q][2048] from the scoring launch (read only)
-    int32_t *blk_ids, *blk_cnt;
-    uint32_t *tok_keys;             // [n_q][tok_stride]
-    int64_t tok_stride;
-    uint32_t *tok_hist;             // [n_q][2048], zeroed by the scoring launch
-};
-
 struct TopkParams {
     const int8_t *q_idx;
     const int32_t *q_seq, *q_pos;
@@ -81,7 +64,7 @@ struct AttendParams {
     const int32_t *sel_pool_cnt;
     int sel_B, sel_P;
     int32_t *topk_out, *topk_cnt_out;
-    uint32_t *blk_hist_clear;   // [n_q][2048] block histograms to zero once read
+    uint32_t *blk_hist_clear;   // optional: [n_q][2048] histograms to zero once read
     int n_splits, keys_per_split;
     int n_q_pad;            // n_q rounded up to a multiple of 8 (XCD-aware numbering)
 };
@@ -111,14 +94,12 @@ hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hip
 hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &plan, int d_idx,
                                hipStream_t st, bool with_select = true);
 hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &plan, int d_idx,
-                              hipStream_t st);
+                              hipStream_t st, bool with_select = true);
 hipError_t launch_attend(const AttendParams &p, const AttendPlan &plan, int D, int dtype,
                          hipStream_t st, bool fused_select = false);
-hipError_t launch_pool_tokens(const PoolTokensParams &p, int d_idx, hipStream_t st);
 
 constexpr int kAttendRowChunk = 2048;   // key-list entries one attention workgroup stages at once
 constexpr int kFusedPoolLds = 2048;     // pooled block ids the fused attention keeps in LDS
-constexpr int kFusedMaxChunk = 1024;    // blocks per workgroup of the fused pool stage
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t st);
 
 }  // namespace csa2

@@ -135,6 +135,13 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     uint32_t *ghist = p.ws_hist + (size_t)q * kRadixBins;
     const int8_t *blk_rows = p.k_blk + (size_t)s * p.nblk * DIDX + part * 16;
 
+    // the query's own block (computed from its visible rows) belongs to the
+    // workgroup whose range holds it; computed once, outside the unrolled loop
+    int4 own_key = make_int4(0, 0, 0, 0);
+    if (jt >= lo && jt < hi) {
+        own_key = block_key_part<DIDX>(own_rows, t - jt * p.B + 1);
+        if (store_own && (tid / LPR) == 0) *reinterpret_cast<int4 *>(own_store) = own_key;
+    }
     for (int base = lo; base < hi; base += RPP * kUnroll) {
         int4 kv[kUnroll];
 #pragma unroll
@@ -146,10 +153,7 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             const int j = base + u * RPP + tid / LPR;
-            if (j == jt && j < hi) {
-                kv[u] = block_key_part<DIDX>(own_rows, t - jt * p.B + 1);
-                if (store_own) *reinterpret_cast<int4 *>(own_store) = kv[u];
-            }
+            if (j == jt) kv[u] = own_key;
             int acc = (j < hi) ? dot16_i8(kv[u], qv) : 0;
             acc = row_reduce<LPR>(acc);
             if (j < hi && part == 0) {
@@ -215,99 +219,6 @@ __global__ __launch_bounds__(NT) void k_index_select(IndexParams p)
 }
 
 // ---------------------------------------------------------------- token Top-K
-// ---------------------------------------------------------------- fused pool + token scoring
-constexpr int kMaxChunk = 1024;     // blocks per workgroup in the fused stage
-
-template <int NT, int DIDX>
-__global__ __launch_bounds__(NT) void k_pool_tokens(PoolTokensParams p)
-{
-    constexpr int LPR = DIDX / 16, RPP = NT / LPR, IPT = kLdsKeys / NT;
-    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
-    __shared__ uint32_t s_sm[NT / 64 + 4];
-    __shared__ int32_t s_blk[kMaxChunk];    // pooled blocks of this range ...
-    __shared__ int32_t s_rank[kMaxChunk];   // ... and their ranks in the pool
-    __shared__ uint32_t s_count;
-    const int q = blockIdx.x % p.n_q;
-    const int g = blockIdx.x / p.n_q;
-    const int tid = threadIdx.x, part = tid % LPR;
-
-    // all global loads of the pool selection go out before the first use
-    HistRegs<NT> hr;
-    load_hist<NT>(p.blk_hist + (size_t)q * kRadixBins, hr);
-    uint32_t k[IPT];
-    load_keys_global<IPT>(p.blk_keys + (size_t)q * p.blk_stride, (int)p.blk_stride, k);
-    const int s = p.q_seq[q], t = p.q_pos[q];
-    const int B = p.B;
-    const int n_elig = t / B + 1;
-    const int lo = min(n_elig, g * p.chunk), hi = min(n_elig, lo + p.chunk);
-    if (tid == 0) s_count = 0u;
-
-    if (n_elig <= p.P) {
-        // the pool is every eligible block, rank = id (ids already written)
-        lds_barrier();
-        for (int j = lo + tid; j < hi; j += NT) {
-            s_blk[j - lo] = j;
-            s_rank[j - lo] = j;
-        }
-        if (tid == 0) s_count = (uint32_t)(hi - lo);
-    } else {
-        hist_to_lds<NT>(hr, s_hist);
-        mask_keys<IPT>(n_elig, k);
-        const Threshold th = threshold_regs<NT, IPT>(k, n_elig, (uint32_t)p.P, s_hist, s_sm);
-        int32_t *ids = p.blk_ids + (size_t)q * p.P;
-        auto emit = [&](uint32_t rank, int j) {
-            if (j >= lo && j < hi) {
-                const uint32_t e = atomicAdd(&s_count, 1u);
-                s_blk[e] = j;
-                s_rank[e] = (int)rank;
-                ids[rank] = j;
-            }
-        };
-        compact_regs<NT, IPT>(k, th, emit, s_sm);
-        if (g == 0 && tid == 0) p.blk_cnt[q] = p.P;
-    }
-    for (int b = tid; b < kHistWords; b += NT) s_hist[b] = 0u;
-    lds_barrier();
-
-    // token scores of the pooled blocks in this range; candidate c = rank*B + w
-    const int m = (int)s_count;
-    const int4 qv = *reinterpret_cast<const int4 *>(p.q_idx + (size_t)q * DIDX + part * 16);
-    const int8_t *seq_rows = p.k_idx + (size_t)s * p.T * DIDX + part * 16;
-    uint32_t *tkeys = p.tok_keys + (size_t)q * p.tok_stride;
-    for (int base = 0; base < m * B; base += RPP * kUnroll) {
-        int pos[kUnroll], cidx[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int r = base + u * RPP + tid / LPR;
-            pos[u] = INT32_MAX;
-            cidx[u] = -1;
-            if (r < m * B) {
-                const int e = r / B, w = r - e * B;
-                pos[u] = s_blk[e] * B + w;
-                cidx[u] = s_rank[e] * B + w;
-            }
-        }
-        int4 kv[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            kv[u] = make_int4(0, 0, 0, 0);
-            if (pos[u] <= t) kv[u] = *reinterpret_cast<const int4 *>(seq_rows + (size_t)pos[u] * DIDX);
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            int acc = dot16_i8(kv[u], qv);
-            acc = row_reduce<LPR>(acc);
-            if (cidx[u] >= 0 && part == 0) {
-                const uint32_t key = (pos[u] <= t) ? (uint32_t)(acc + (int)kKeyBias) : 0u;
-                tkeys[cidx[u]] = key;
-                atomicAdd(&s_hist[hist_pad(key >> kRadixBits)], 1u);
-            }
-        }
-    }
-    lds_barrier();
-    flush_hist<NT>(s_hist, p.tok_hist + (size_t)q * kRadixBins);
-}
-
 // Threshold and ordered emit of a query's Top-K from its keys in registers and
 // its pass-1 histogram in LDS; writes topk/topk_cnt.
 template <int NT, int IPT>
@@ -498,37 +409,24 @@ hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &pl, int d
 }
 
 template <int DIDX>
-static void launch_topk_t(const TopkParams &p, const SelectPlan &pl, hipStream_t st)
+static void launch_topk_t(const TopkParams &p, const SelectPlan &pl, hipStream_t st, bool with_select)
 {
     dim3 grid((unsigned)(p.n_q * pl.G));
     if (pl.split) {
         hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
-        hipLaunchKernelGGL((k_topk_select<kSelectThreads>), dim3((unsigned)p.n_q), dim3(kSelectThreads), 0, st, p);
+        if (with_select)
+            hipLaunchKernelGGL((k_topk_select<kSelectThreads>), dim3((unsigned)p.n_q), dim3(kSelectThreads), 0, st, p);
     } else {
         hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
     }
 }
 
-hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &pl, int d_idx, hipStream_t st)
+hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &pl, int d_idx, hipStream_t st,
+                              bool with_select)
 {
     if (p.n_q <= 0) return hipSuccess;
-    if (d_idx == 64) launch_topk_t<64>(p, pl, st);
-    else launch_topk_t<32>(p, pl, st);
-    return hipGetLastError();
-}
-
-template <int DIDX>
-static void launch_pool_tokens_t(const PoolTokensParams &p, hipStream_t st)
-{
-    hipLaunchKernelGGL((k_pool_tokens<kSelectThreads, DIDX>), dim3((unsigned)(p.n_q * p.G)),
-                       dim3(kSelectThreads), 0, st, p);
-}
-
-hipError_t launch_pool_tokens(const PoolTokensParams &p, int d_idx, hipStream_t st)
-{
-    if (p.n_q <= 0) return hipSuccess;
-    if (d_idx == 64) launch_pool_tokens_t<64>(p, st);
-    else launch_pool_tokens_t<32>(p, st);
+    if (d_idx == 64) launch_topk_t<64>(p, pl, st, with_select);
+    else launch_topk_t<32>(p, pl, st, with_select);
     return hipGetLastError();
 }
 
