@@ -112,6 +112,21 @@ def test_prefill_scaled_tie_heavy_d32(lib):
     check(lib, cfg, seed=26, int_range=(-1, 1))
 
 
+def test_prefill_row_kernel_long_lists(lib):
+    """Many queries take the wave-per-item attention kernel: key lists longer
+    than one staged chunk of row codes (K + W up to 1,000), a window-only
+    layer, and an item count that leaves the last workgroups part-filled."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=1501, pool=128, top_k=900, window=100,
+                   layers=("full", "reuse", "swa"))
+    check(lib, cfg, seed=29)
+
+
+def test_prefill_row_kernel_two_head_groups(lib):
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=1100, pool=64, top_k=200, window=128, n_heads=32,
+                   layers=("full", "swa"))
+    check(lib, cfg, seed=30)
+
+
 def test_no_window(lib):
     cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=4096, pool=64, top_k=128, window=0)
     check(lib, cfg, seed=27)

@@ -187,7 +187,7 @@ FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
     f.idx = plan_index(n_q, T, c->block, c->pool, c->d_idx);
     f.tok = plan_topk(n_q, c->block, c->pool, c->top_k, c->d_idx);
     f.att = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
-    f.ok = c->top_k >= 1 && f.idx.split && f.tok.split && n_elig_max <= kMaxCandidates && f.att.mfma &&
+    f.ok = c->top_k >= 1 && f.idx.split && f.tok.split && n_elig_max <= kMaxCandidates && f.att.mfma && !f.att.rows &&
            f.att.keys_per_split <= kAttendRowChunk && c->pool <= kFusedPoolLds;
     f.blk_stride = (n_elig_max + 3) / 4 * 4;
     f.tok_stride = ((long long)c->pool * c->block + 3) / 4 * 4;

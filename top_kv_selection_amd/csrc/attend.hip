@@ -452,12 +452,245 @@ __global__ __launch_bounds__(512) void k_attend_combine(AttendParams p)
     if (p.lse && (threadIdx.x & 31) == 0) p.lse[row_id] = (M + log2f(L)) * kLn2;
 }
 
+// ============================================================ row kernel
+// Many (query, layer, head group) items, as in prefill: one wave owns an item
+// and walks its whole key list, 32 keys per step, so no two waves share a
+// softmax and no workgroup barrier is needed.
+//  * Gather: a step's 32 K rows and 32 V rows go from L2 straight into the
+//    wave's LDS tiles (buffer loads with the LDS destination), 16 lanes per
+//    256-byte row, so every load instruction reads four whole rows.  The
+//    MFMA operands are then read from LDS: K with 16-byte reads in the A
+//    layout (key = lane % 16), V^T with the transposing 8-byte read, which
+//    hands each lane one dim of four keys.  (Loading K rows straight into the
+//    A layout puts 16 different rows on consecutive lanes, which halves the
+//    gather rate.)
+//  * Phases: the key list is walked as the Top-K rows (row ids staged in
+//    LDS) and then the window (contiguous rows), so a step reads one table.
+//  * Lazy running max: m moves only when a score exceeds it by more than
+//    kLazyLog2 (so P <= 2^kLazyLog2 and every term stays finite); the
+//    softmax is invariant to m, so the result is the same function, and a
+//    step whose scores all stay under the bound needs no cross-lane
+//    reduction and no rescale of the accumulators.  The row sum is kept per
+//    lane and reduced across the four lane groups once per item.
+// Tile layout: tile row r (0..31) of a step sits at byte
+// kTileInst * (r % 8) + 256 * (r / 8): load instruction x writes rows
+// x, x+8, x+16, x+24 as one 1 KiB run, and the runs are kTileInst bytes
+// apart so that rows of different instructions start in different banks.
+constexpr int kRowWaves = 4;            // waves (items in flight) per workgroup
+constexpr int kRowCodes = 256;          // Top-K row ids staged per wave at once (8 steps)
+constexpr int kTileInst = 1024 + 16;    // bytes per load instruction in a tile
+constexpr int kTileBytes = 8 * kTileInst;
+constexpr float kLazyLog2 = 8.f;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float max_groups(float x)   // max over lanes l, l^16, l^32, l^48
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_groups(float x)   // sum over lanes l, l^16, l^32, l^48
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Orders this wave's LDS accesses in the compiler; the hardware performs one
+// wave's LDS instructions in issue order.
+__device__ __forceinline__ void wave_lds_order()
+{
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base, long long n_rows)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, (int)(n_rows * 256), kRsrcWord3);
+}
+
+__global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kRowWaves][2][kTileBytes];   // K, V
+    __shared__ __attribute__((aligned(16))) int s_codes[kRowWaves][kRowCodes];
+
+    // the wave index is uniform over the wave: keep it (and the item, its
+    // pointers and buffer descriptors) in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+    // Workgroup b runs on XCD b % 8 (round-robin dispatch); each XCD takes a
+    // contiguous range of items, i.e. of neighbouring queries whose windows
+    // overlap, so window rows are shared inside one L2.
+    const int per_xcd = gridDim.x / 8;
+    const int item = ((blockIdx.x % 8) * per_xcd + blockIdx.x / 8) * kRowWaves + w;
+    const int HG = p.H / 16;
+    if (item >= p.n_q * p.n_layers * HG) return;   // whole wave; no barriers follow
+    const int i = item % p.n_q;
+    const int hg = (item / p.n_q) % HG;
+    const int l = item / (p.n_q * HG);
+
+    const int s = p.q_seq[i], t = p.q_pos[i];
+    const Window win = window_of(t, p.W, p.swa_first, p.swa_len);
+    const int cnt = p.topk ? p.topk_cnt[i] : 0;
+    const int main_steps = (cnt + 31) / 32;
+    const int n_steps = main_steps + (win.nw + 31) / 32;
+
+    const uint16_t *qrow = (const uint16_t *)p.q + (((size_t)l * p.n_q + i) * p.H + hg * 16 + r16) * 128;
+    const size_t main0 = (size_t)s * p.T * 128, swa0 = ((size_t)l * p.n_seq + s) * p.swa_len * 128;
+    const auto rk_main = rows_rsrc((const uint16_t *)p.k_main + main0, p.T);
+    const auto rv_main = rows_rsrc((const uint16_t *)p.v_main + main0, p.T);
+    const auto rk_swa = rows_rsrc((const uint16_t *)p.k_swa + swa0, p.swa_len);
+    const auto rv_swa = rows_rsrc((const uint16_t *)p.v_swa + swa0, p.swa_len);
+    const int32_t *tk = p.topk ? p.topk + (size_t)i * p.K : nullptr;
+    const int wrow0 = win.w0 - p.swa_first;      // window row of the first window key
+    int *codes = s_codes[w];
+    uint8_t *ktile = s_tiles[w][0], *vtile = s_tiles[w][1];
+
+    // Top-K row ids kc .. kc + kRowCodes - 1; slots past cnt repeat the last id
+    int kc = 0;
+    auto stage = [&](int k0) {
+        wave_lds_order();
+        for (int x = lane; x < kRowCodes; x += 64) codes[x] = tk[min(k0 + x, cnt - 1)];
+        wave_lds_order();
+    };
+    // The 16 loads of step st: instruction x brings tile rows x + 8a
+    // (a = lane / 16) of K and of V, lane % 16 taking 16 bytes of the row.
+    auto issue_loads = [&](int st) {
+        int row[8];
+        __amdgpu_buffer_rsrc_t rk, rv;
+        if (st < main_steps) {
+            if (32 * st - kc == kRowCodes) {
+                kc = 32 * st;
+                stage(kc);
+            }
+            const int4 c0 = *reinterpret_cast<const int4 *>(codes + 32 * st - kc + 8 * g);
+            const int4 c1 = *reinterpret_cast<const int4 *>(codes + 32 * st - kc + 8 * g + 4);
+            row[0] = c0.x; row[1] = c0.y; row[2] = c0.z; row[3] = c0.w;
+            row[4] = c1.x; row[5] = c1.y; row[6] = c1.z; row[7] = c1.w;
+            rk = rk_main;
+            rv = rv_main;
+        } else {
+            const int r0 = wrow0 + 32 * (st - main_steps) + 8 * g, r_last = wrow0 + win.nw - 1;
+#pragma unroll
+            for (int x = 0; x < 8; x++) row[x] = min(r0 + x, r_last);
+            rk = rk_swa;
+            rv = rv_swa;
+        }
+#pragma unroll
+        for (int x = 0; x < 8; x++) {
+            const uint32_t off = (uint32_t)row[x] * 256u + (uint32_t)r16 * 16u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(ktile + kTileInst * x), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vtile + kTileInst * x), 16, off, 0, 0, 0);
+        }
+    };
+
+    bf16x8_t qb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) qb[kk] = *reinterpret_cast<const bf16x8_t *>(qrow + kk * 32 + g * 8);
+
+    // operand addresses in the tiles (per lane; tau, kk, m, h are immediates)
+    //   K, A layout: tile row 16 tau + r16, bytes 64 kk + 16 g
+    const uint8_t *ka_base = ktile + kTileInst * (r16 & 7) + 256 * (r16 >> 3) + 16 * g;
+    //   V^T via the transposing read: lane r16 of group g addresses tile row
+    //   16 h + 4 g + r16 / 4, dims 16 m + 4 (r16 % 4) .. +3
+    const int vrow = 4 * g + (r16 >> 2);
+    const uint8_t *va_base = vtile + kTileInst * (vrow & 7) + 256 * (vrow >> 3) + 8 * (r16 & 3);
+
+    float m_run = -INFINITY, l_part = 0.f;
+    f32x4_t acc[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (n_steps > 0) {
+        if (main_steps > 0) stage(0);
+        issue_loads(0);
+    }
+    for (int st = 0; st < n_steps; st++) {
+        const int n_valid = (st < main_steps) ? min(32, cnt - 32 * st) : min(32, win.nw - 32 * (st - main_steps));
+        // this step's rows are in the tiles once the wave's loads are done
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        bf16x8_t ka[2][4], va[8];
+#pragma unroll
+        for (int tau = 0; tau < 2; tau++)
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++)
+                ka[tau][kk] = *reinterpret_cast<const bf16x8_t *>(ka_base + 512 * tau + 64 * kk);
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(va_base + 32 * m));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(va_base + 512 + 32 * m));
+            const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                       __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+            va[m] = __builtin_bit_cast(bf16x8_t, u);
+        }
+        // the tiles are free once these reads have returned: the next step's
+        // rows are fetched during this step's arithmetic
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (st + 1 < n_steps) issue_loads(st + 1);
+
+        // S^T = K Q^T: lane holds keys 4g+ii (tile 0) and 16+4g+ii (tile 1) of head r16
+        f32x4_t sk[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+            for (int tau = 0; tau < 2; tau++)
+                sk[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tau][kk], qb[kk], sk[tau], 0, 0, 0);
+        // softmax terms of this step (log2 domain; the scale is positive, so
+        // the maximum of the raw scores gives the maximum logit)
+        float sc[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) sc[e] = sk[e >> 2][e & 3];
+        if (n_valid < 32) {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                if (slot_key(g, e) >= n_valid) sc[e] = -INFINITY;
+        }
+        const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                               fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))) * p.scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyLog2)) {
+            const float hmax = max_groups(mx);
+            const float m_new = (hmax > m_run + kLazyLog2) ? hmax : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first finite max
+            l_part *= alpha;
+#pragma unroll
+            for (int m = 0; m < 8; m++) acc[m] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        bf16x8_t pb;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(sc[e], p.scale_log2, -m_use));
+            l_part += pr;
+            pb[e] = (__bf16)pr;
+        }
+        // O^T += V^T P^T over the 8 dim tiles
+#pragma unroll
+        for (int m = 0; m < 8; m++) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb, acc[m], 0, 0, 0);
+    }
+    // acc[m][ii] = O[head r16][dim 16m + 4g + ii] (unnormalised)
+    const float L = sum_groups(l_part);
+    const float inv = 1.f / L;
+    const size_t row_id = ((size_t)l * p.n_q + i) * p.H + hg * 16 + r16;
+    uint16_t *orow = (uint16_t *)p.out + row_id * 128;
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(acc[m][0] * inv) | ((uint32_t)f32_to_bf16(acc[m][1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(acc[m][2] * inv) | ((uint32_t)f32_to_bf16(acc[m][3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(orow + 16 * m + 4 * g) = make_uint2(lo, hi);
+    }
+    if (p.lse && g == 0) p.lse[row_id] = (m_run + log2f(L)) * kLn2;
+}
+
 // ============================================================ planning / launch
 static int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dtype)
 {
-    AttendPlan pl{(dtype == 1) && (D == 128) && (H % 16 == 0), 1, 0, 0};
+    AttendPlan pl{(dtype == 1) && (D == 128) && (H % 16 == 0), false, 1, 0, 0};
     if (!pl.mfma) return pl;
     // Split a key list over several workgroups only when there are too few
     // (query, layer, head group) triples to spread the gather over the chip;
@@ -471,6 +704,9 @@ AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dt
     pl.n_splits = n_splits;
     pl.keys_per_split = steps_per_split * kStepKeys;
     pl.part_bytes = n_splits > 1 ? (size_t)base * n_splits * kPartFloats * sizeof(float) : 0;
+    // enough items for one wave each to fill the chip (never split then): the
+    // row kernel, when the row tables fit its 32-bit buffer offsets
+    pl.rows = base >= kRowItemsMin && n_splits == 1;
     return pl;
 }
 
@@ -479,6 +715,13 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
 {
     if (p0.n_q <= 0 || p0.n_layers <= 0) return hipSuccess;
     AttendParams p = p0;
+    const bool rows_fit = (long long)p.T * 256 < INT32_MAX && (long long)p.swa_len * 256 < INT32_MAX;
+    if (pl.rows && !fused_select && rows_fit) {
+        const long long items = (long long)p.n_q * p.n_layers * (p.H / 16);
+        const long long n_wg = (items + kRowWaves - 1) / kRowWaves;
+        hipLaunchKernelGGL(k_attend_rows, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kRowWaves * 64), 0, st, p);
+        return hipGetLastError();
+    }
     if (pl.mfma) {
         p.n_q_pad = (p.n_q + 7) / 8 * 8;
         p.n_splits = pl.n_splits;

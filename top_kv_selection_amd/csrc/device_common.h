@@ -248,7 +248,6 @@ template <int NT, int IPT>
 __device__ Threshold threshold_regs(const uint32_t (&k)[IPT], int count, uint32_t n, uint32_t *hist,
                                     uint32_t *sm)
 {
-    const int tid = threadIdx.x;
     const uint32_t n_valid = (uint32_t)count - hist[0];
     if (n_valid <= n) {
         lds_barrier();

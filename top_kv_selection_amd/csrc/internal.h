@@ -77,7 +77,8 @@ struct SelectPlan {
 };
 
 struct AttendPlan {
-    bool mfma;    // bf16, D = 128, H a multiple of 16: the MFMA kernel; else the generic one
+    bool mfma;    // bf16, D = 128, H a multiple of 16: an MFMA kernel; else the generic one
+    bool rows;    // many items: one wave per (query, layer, head group), no splits
     int n_splits, keys_per_split;
     size_t part_bytes;
 };
@@ -98,6 +99,7 @@ hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &plan, int d
 hipError_t launch_attend(const AttendParams &p, const AttendPlan &plan, int D, int dtype,
                          hipStream_t st, bool fused_select = false);
 
+constexpr int kRowItemsMin = 1024;      // (query, layer, head group) items that take the row kernel
 constexpr int kAttendRowChunk = 2048;   // key-list entries one attention workgroup stages at once
 constexpr int kFusedPoolLds = 2048;     // pooled block ids the fused attention keeps in LDS
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t st);
