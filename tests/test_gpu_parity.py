@@ -127,6 +127,32 @@ def test_prefill_row_kernel_two_head_groups(lib):
     check(lib, cfg, seed=30)
 
 
+def test_prefill_dense_topk_two_sequences(lib):
+    """Pool covering every block: the MFMA tile Top-K, with a workgroup tile
+    that holds queries of both sequences (1,000 is not a multiple of 16)."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], n_seq=2, ctx=1000, pool=256, top_k=200, window=64,
+                   layers=("full", "reuse"))
+    check(lib, cfg, seed=31)
+
+
+def test_prefill_dense_topk_tie_heavy_d32(lib):
+    """Indexer values in {-1, 0, 1} at d_idx 32: thousands of equal scores, so
+    most queries take their last entries from a long run of ties."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=2000, d_idx=32, pool=256, top_k=300, window=32,
+                   layers=("full",))
+    check(lib, cfg, seed=32, int_range=(-1, 1))
+
+
+def test_prefill_dense_topk_longest_context(lib):
+    """16,384 tokens with a pool of 2,048 blocks: the longest context the
+    tile Top-K takes; sampled rows."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=16384, layers=("full",))
+    rng = np.random.default_rng(33)
+    edges = [0, 1, 15, 16, 17, 511, 512, 513, 4095, 8191, 12000, 16367, 16368, 16383]
+    rows = np.unique(np.concatenate([edges, rng.choice(cfg.n_q, 40, replace=False)]))
+    check(lib, cfg, seed=33, rows=rows)
+
+
 def test_no_window(lib):
     cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=4096, pool=64, top_k=128, window=0)
     check(lib, cfg, seed=27)

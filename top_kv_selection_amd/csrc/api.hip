@@ -107,7 +107,7 @@ int32_t do_topk(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32
     if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned4(q_seq) || !aligned4(q_pos) ||
         !aligned4(blk_ids) || !aligned4(blk_cnt) || !aligned4(topk) || !aligned4(topk_cnt))
         return CSA2_E_ALIGN;
-    const SelectPlan pl = plan_topk(n_q, c->block, c->pool, c->top_k, c->d_idx);
+    const SelectPlan pl = plan_topk(n_q, T, c->block, c->pool, c->top_k, c->d_idx);
     Region r;
     if (int32_t e = carve(ws, ws_bytes, select_head_bytes(n_q, pl.split), pl.key_bytes, r)) return e;
     if (!launch) return CSA2_OK;
@@ -185,7 +185,7 @@ FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
     FusedPlan f{};
     const long long n_elig_max = (long long)(T - 1) / c->block + 1;
     f.idx = plan_index(n_q, T, c->block, c->pool, c->d_idx);
-    f.tok = plan_topk(n_q, c->block, c->pool, c->top_k, c->d_idx);
+    f.tok = plan_topk(n_q, T, c->block, c->pool, c->top_k, c->d_idx);
     f.att = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
     f.ok = c->top_k >= 1 && f.idx.split && f.tok.split && n_elig_max <= kMaxCandidates && f.att.mfma && !f.att.rows &&
            f.att.keys_per_split <= kAttendRowChunk && c->pool <= kFusedPoolLds;
@@ -312,7 +312,7 @@ int32_t csa2_workspace_bytes(const csa2_cfg *c, int32_t n_q, int32_t T, int32_t 
     if (int32_t e = check_cfg(c)) return e;
     if (n_q < 0 || T < 1 || T > (1 << 24) || n_layers < 1) return CSA2_E_SHAPE;
     const SelectPlan pi = plan_index(n_q, T, c->block, c->pool, c->d_idx);
-    const SelectPlan pt = plan_topk(n_q, c->block, c->pool, c->top_k, c->d_idx);
+    const SelectPlan pt = plan_topk(n_q, T, c->block, c->pool, c->top_k, c->d_idx);
     const AttendPlan pa = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
     const size_t ctr = std::max(select_head_bytes(n_q, pi.split), select_head_bytes(n_q, pt.split));
     const size_t data = std::max({pi.key_bytes, pt.key_bytes, pa.part_bytes});

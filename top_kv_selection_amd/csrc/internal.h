@@ -74,6 +74,7 @@ struct SelectPlan {
     int G, chunk;
     bool split;       // scores go through the workspace (G > 1 or too many for LDS)
     size_t key_bytes; // workspace bytes for the scores
+    bool dense = false;   // token Top-K: every pool is the whole prefix (MFMA tile kernel)
 };
 
 struct AttendPlan {
@@ -88,7 +89,7 @@ struct AttendPlan {
 size_t select_head_bytes(int n_q, bool split);
 
 SelectPlan plan_index(int n_q, int T, int B, int P, int d_idx);
-SelectPlan plan_topk(int n_q, int B, int P, int K, int d_idx);
+SelectPlan plan_topk(int n_q, int T, int B, int P, int K, int d_idx);
 AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dtype);
 
 hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hipStream_t st);
@@ -100,6 +101,8 @@ hipError_t launch_attend(const AttendParams &p, const AttendPlan &plan, int D, i
                          hipStream_t st, bool fused_select = false);
 
 constexpr int kRowItemsMin = 1024;      // (query, layer, head group) items that take the row kernel
+constexpr int kDenseMaxT = 16384;       // longest context of the dense (MFMA tile) token Top-K
+constexpr int kDenseMinQueries = 256;   // queries per call below which the per-query kernels run
 constexpr int kAttendRowChunk = 2048;   // key-list entries one attention workgroup stages at once
 constexpr int kFusedPoolLds = 2048;     // pooled block ids the fused attention keeps in LDS
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t st);

@@ -329,6 +329,268 @@ __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
     topk_finish<NT, IPT>(p, q, k, n_cand, s_hist, s_pool, s_sm);
 }
 
+// ---------------------------------------------------------------- dense token Top-K
+// Prefill-sized calls where every query's pool is its whole prefix (all its
+// eligible blocks fit the pool) and the context is at most kDenseMaxT tokens:
+// the candidates of a query at position t are then the positions 0..t.  A
+// workgroup takes kDenseQ consecutive queries; for the queries of one
+// sequence, v_mfma_i32_16x16x64_i8 scores 16 positions x 16 queries per
+// instruction (A = k_idx rows, B = q_idx rows; exact int32 sums), and every
+// query's exact Top-K is found by a radix select that rescans the prefix
+// instead of storing its keys:
+//   pass 1: histogram of key >> 11 per query      -> threshold bin b1
+//   pass 2: histogram of key & 2047 within bin b1 -> threshold key tau
+//   pass 3: bitmaps of key > tau and key == tau per query
+// and an ordered emit over the bitmaps takes every key above tau plus the
+// lowest-position ties.  Histogram counts (at most kDenseMaxT) are packed two
+// per 32-bit LDS word; the bitmaps reuse the histogram memory.
+constexpr int kDenseQ = 16;              // queries per workgroup (one MFMA column block)
+constexpr int kDenseWaves = 8;
+constexpr int kDenseUnroll = 4;          // position tiles per wave in flight
+constexpr int kDenseHistWords = kRadixBins / 2;   // packed histogram words per query
+constexpr int kDenseMapWords = kDenseMaxT / 32;   // bitmap words per query
+
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+
+// Threshold search over one query's packed 2048-bin histogram by one wave:
+// the bin b where the count of keys in bins above b is < n <= count in bins
+// >= b; `above` gets the count above b.
+__device__ __forceinline__ void find_bin_packed(const uint32_t *h, uint32_t n, int &bin, uint32_t &above)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t c[16];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(h + 16 * lane + 4 * k);
+        c[4 * k] = v.x; c[4 * k + 1] = v.y; c[4 * k + 2] = v.z; c[4 * k + 3] = v.w;
+    }
+    uint32_t S = 0;
+#pragma unroll
+    for (int k = 0; k < 16; k++) S += (c[k] & 0xffffu) + (c[k] >> 16);
+    const uint32_t incl = wave_incl_scan(S);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t suf = total - incl;   // keys in the bins above this lane's 32
+    const bool here = suf < n && suf + S >= n;
+    int b = 0;
+    uint32_t run = suf;
+    if (here) {
+        for (int k = 15; k >= 0; k--) {
+            const uint32_t hi = c[k] >> 16, lo = c[k] & 0xffffu;
+            if (run + hi >= n) { b = 2 * k + 1; break; }
+            run += hi;
+            if (run + lo >= n) { b = 2 * k; break; }
+            run += lo;
+        }
+    }
+    const uint64_t found = __builtin_amdgcn_ballot_w64(here);   // exactly one lane when n <= total
+    const int src = found ? __builtin_ctzll(found) : 0;
+    bin = __builtin_amdgcn_readlane(32 * lane + b, src);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)run, src);
+}
+
+template <int DIDX>
+__global__ __launch_bounds__(kDenseWaves * 64) void k_topk_dense(TopkParams p)
+{
+    constexpr int NT = kDenseWaves * 64;
+    constexpr int HW = kDenseHistWords, MW = kDenseMapWords;
+    static_assert(2 * kDenseQ * MW <= kDenseQ * HW, "bitmaps reuse the histogram memory");
+    __shared__ __attribute__((aligned(16))) uint32_t s_buf[kDenseQ * HW];
+    __shared__ int s_b1[kDenseQ], s_tau[kDenseQ], s_need[kDenseQ];
+    __shared__ uint32_t s_gt1[kDenseQ];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    const int q0 = blockIdx.x * kDenseQ;
+    const int K = p.K;
+    // this lane's query column: q_idx as the B operand, 16 dims per lane group
+    const int qi = q0 + r16;
+    const bool qvalid = qi < p.n_q;
+    const int tq = qvalid ? p.q_pos[qi] : -1;
+    v4i32 qb = {0, 0, 0, 0};
+    if (qvalid && 16 * g < DIDX) qb = *reinterpret_cast<const v4i32 *>(p.q_idx + (size_t)qi * DIDX + 16 * g);
+
+    auto zero_buf = [&] {
+        for (int x = tid * 4; x < kDenseQ * HW; x += NT * 4) *reinterpret_cast<uint4 *>(s_buf + x) = make_uint4(0, 0, 0, 0);
+    };
+
+    uint32_t remaining = 0;
+    for (int jj = 0; jj < kDenseQ; jj++)
+        if (q0 + jj < p.n_q) remaining |= 1u << jj;
+    // the tile's queries, one sequence at a time (every wave takes the same groups)
+    while (remaining) {
+        const int s = p.q_seq[q0 + __builtin_ctz(remaining)];
+        uint32_t gmask = 0;
+        int tmax = 0;
+        for (int jj = 0; jj < kDenseQ; jj++)
+            if (((remaining >> jj) & 1) && p.q_seq[q0 + jj] == s) {
+                gmask |= 1u << jj;
+                tmax = max(tmax, p.q_pos[q0 + jj]);
+            }
+        remaining &= ~gmask;
+        const bool mine = (gmask >> r16) & 1;
+        const int n_tiles = tmax / 16 + 1;
+        const int8_t *rows = p.k_idx + (size_t)s * p.T * DIDX;
+
+        // Runs fn(pos0, d) for this wave's position tiles: d[ii] is the score
+        // of position pos0 + 4g + ii for query column r16.
+        auto scan = [&](auto &&fn) {
+            for (int tb = w; tb < n_tiles; tb += kDenseWaves * kDenseUnroll) {
+                v4i32 a[kDenseUnroll];
+#pragma unroll
+                for (int u = 0; u < kDenseUnroll; u++) {
+                    const int pos = 16 * (tb + u * kDenseWaves) + r16;
+                    a[u] = v4i32{0, 0, 0, 0};
+                    if (tb + u * kDenseWaves < n_tiles && pos < p.T && 16 * g < DIDX)
+                        a[u] = *reinterpret_cast<const v4i32 *>(rows + (size_t)pos * DIDX + 16 * g);
+                }
+#pragma unroll
+                for (int u = 0; u < kDenseUnroll; u++) {
+                    const int tile = tb + u * kDenseWaves;
+                    if (tile < n_tiles) {
+                        const v4i32 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], qb, v4i32{0, 0, 0, 0}, 0, 0, 0);
+                        fn(16 * tile, d);
+                    }
+                }
+            }
+        };
+
+        // ---- pass 1: top-bit histograms
+        zero_buf();
+        __syncthreads();
+        scan([&](int pos0, v4i32 d) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ii++) {
+                const int pos = pos0 + 4 * g + ii;
+                if (mine && pos <= tq) {
+                    const uint32_t b = ((uint32_t)(d[ii] + (int)kKeyBias)) >> kRadixBits;
+                    atomicAdd(&s_buf[r16 * HW + (b >> 1)], 1u << (16 * (b & 1)));
+                }
+            }
+        });
+        __syncthreads();
+        for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
+            if (!((gmask >> jq) & 1)) continue;
+            const uint32_t n = (uint32_t)p.q_pos[q0 + jq] + 1;
+            int b1 = -1;
+            uint32_t gt1 = 0;
+            if (n > (uint32_t)K) find_bin_packed(s_buf + jq * HW, (uint32_t)K, b1, gt1);
+            if (lane == 0) {
+                s_b1[jq] = b1;
+                s_gt1[jq] = gt1;
+            }
+        }
+        __syncthreads();
+        // ---- pass 2: low-bit histograms inside the threshold bin
+        zero_buf();
+        __syncthreads();
+        const int b1q = mine ? s_b1[r16] : -1;
+        if (__syncthreads_or(b1q >= 0)) {
+            scan([&](int pos0, v4i32 d) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ii++) {
+                    const int pos = pos0 + 4 * g + ii;
+                    const uint32_t key = (uint32_t)(d[ii] + (int)kKeyBias);
+                    if (b1q >= 0 && pos <= tq && (int)(key >> kRadixBits) == b1q) {
+                        const uint32_t b = key & kRadixMask;
+                        atomicAdd(&s_buf[r16 * HW + (b >> 1)], 1u << (16 * (b & 1)));
+                    }
+                }
+            });
+        }
+        __syncthreads();
+        for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
+            if (!((gmask >> jq) & 1)) continue;
+            const int b1 = s_b1[jq];
+            int tau = 0, need = 0;   // fewer candidates than K: every key (> 0) is taken
+            if (b1 >= 0) {
+                const uint32_t need1 = (uint32_t)K - s_gt1[jq];
+                int b2;
+                uint32_t gt2;
+                find_bin_packed(s_buf + jq * HW, need1, b2, gt2);
+                tau = (b1 << kRadixBits) | b2;
+                need = (int)(need1 - gt2);
+            }
+            if (lane == 0) {
+                s_tau[jq] = tau;
+                s_need[jq] = need;
+            }
+        }
+        __syncthreads();
+        // ---- pass 3: bitmaps of keys above tau and equal to tau
+        zero_buf();
+        __syncthreads();
+        const uint32_t tauq = mine ? (uint32_t)s_tau[r16] : 0u;
+        uint32_t *gt_map = s_buf, *eq_map = s_buf + kDenseQ * MW;
+        scan([&](int pos0, v4i32 d) {
+            uint32_t gb = 0, eb = 0;
+#pragma unroll
+            for (int ii = 0; ii < 4; ii++) {
+                const int pos = pos0 + 4 * g + ii;
+                const uint32_t key = (uint32_t)(d[ii] + (int)kKeyBias);
+                if (mine && pos <= tq) {
+                    gb |= (uint32_t)(key > tauq) << (pos & 31);
+                    eb |= (uint32_t)(key == tauq) << (pos & 31);
+                }
+            }
+            const int wd = r16 * MW + ((pos0 + 4 * g) >> 5);
+            if (gb) atomicOr(&gt_map[wd], gb);
+            if (eb) atomicOr(&eq_map[wd], eb);
+        });
+        __syncthreads();
+        // ---- ordered emit: lane l covers positions 256 l .. 256 l + 255
+        for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
+            if (!((gmask >> jq) & 1)) continue;
+            const int i = q0 + jq;
+            const int n = p.q_pos[i] + 1;
+            const int cnt = min(n, K);
+            int need = s_need[jq];
+            uint32_t gt[8], eq[8];
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(gt_map + jq * MW + 8 * lane + 4 * k);
+                const uint4 b = *reinterpret_cast<const uint4 *>(eq_map + jq * MW + 8 * lane + 4 * k);
+                gt[4 * k] = a.x; gt[4 * k + 1] = a.y; gt[4 * k + 2] = a.z; gt[4 * k + 3] = a.w;
+                eq[4 * k] = b.x; eq[4 * k + 1] = b.y; eq[4 * k + 2] = b.z; eq[4 * k + 3] = b.w;
+            }
+            // ties: the first `need` keys equal to tau in position order
+            uint32_t ec = 0;
+#pragma unroll
+            for (int k = 0; k < 8; k++) ec += __builtin_popcount(eq[k]);
+            const int e_before = (int)(wave_incl_scan(ec) - ec);
+            int take = min(max(need - e_before, 0), (int)ec);
+            uint32_t sc = 0;
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                uint32_t x = eq[k], m = 0;
+                while (take > 0 && x) {
+                    const uint32_t lsb = x & (0u - x);
+                    m |= lsb;
+                    x ^= lsb;
+                    take--;
+                }
+                gt[k] |= m;
+                sc += __builtin_popcount(gt[k]);
+            }
+            uint32_t slot = wave_incl_scan(sc) - sc;
+            int32_t *out = p.topk + (size_t)i * K;
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                uint32_t x = gt[k];
+                while (x) {
+                    const int b = __builtin_ctz(x);
+                    x &= x - 1;
+                    if (slot < (uint32_t)K) out[slot] = 256 * lane + 32 * k + b;
+                    slot++;
+                }
+            }
+            for (int o = cnt + lane; o < K; o += 64) out[o] = -1;
+            if (lane == 0) p.topk_cnt[i] = cnt;
+        }
+        __syncthreads();
+    }
+}
+
 __global__ void k_fill_zero(uint32_t *p, size_t n)
 {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -369,9 +631,15 @@ SelectPlan plan_index(int n_q, int T, int B, int P, int d_idx)
     return plan_scan(n_q, n_elig_max, d_idx, n_elig_max > kLdsKeys);
 }
 
-SelectPlan plan_topk(int n_q, int B, int P, int K, int d_idx)
+SelectPlan plan_topk(int n_q, int T, int B, int P, int K, int d_idx)
 {
     (void)K;
+    const long long n_elig_max = (long long)(T - 1) / B + 1;
+    if (n_elig_max <= P && T <= kDenseMaxT && n_q >= kDenseMinQueries) {
+        SelectPlan pl{1, 0, false, 0};
+        pl.dense = true;
+        return pl;
+    }
     return plan_scan(n_q, (long long)P * B, d_idx, false);
 }
 
@@ -411,6 +679,11 @@ hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &pl, int d
 template <int DIDX>
 static void launch_topk_t(const TopkParams &p, const SelectPlan &pl, hipStream_t st, bool with_select)
 {
+    if (pl.dense) {
+        hipLaunchKernelGGL((k_topk_dense<DIDX>), dim3((unsigned)((p.n_q + kDenseQ - 1) / kDenseQ)),
+                           dim3(kDenseWaves * 64), 0, st, p);
+        return;
+    }
     dim3 grid((unsigned)(p.n_q * pl.G));
     if (pl.split) {
         hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
