@@ -338,24 +338,44 @@ __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
 // instruction (A = k_idx rows, B = q_idx rows; exact int32 sums), and every
 // query's exact Top-K is found by a radix select that rescans the prefix
 // instead of storing its keys:
-//   pass 1: histogram of key >> 11 per query      -> threshold bin b1
-//   pass 2: histogram of key & 2047 within bin b1 -> threshold key tau
-//   pass 3: bitmaps of key > tau and key == tau per query
-// and an ordered emit over the bitmaps takes every key above tau plus the
-// lowest-position ties.  Histogram counts (at most kDenseMaxT) are packed two
-// per 32-bit LDS word; the bitmaps reuse the histogram memory.
+//   pass 1: histogram of key >> 11 per query -> threshold bin b1, with gt1
+//           keys above it and eq1 keys in it;
+//   pass 2: bitmaps of the keys above bin b1 and of the keys in bin b1; the
+//           eq1 keys of bin b1 are then scored again one by one and the
+//           K - gt1 best by (key desc, position asc) join the first bitmap.
+// When some query has more than kDenseList keys in its bin b1 (many equal
+// scores), pass 2 instead takes a histogram of the low bits inside bin b1
+// (-> exact threshold key tau and the number of ties to take) and a third
+// pass builds bitmaps of keys above tau and equal to tau.  An ordered emit
+// over the bitmaps writes the positions ascending, ties lowest position
+// first.  Histogram counts (at most kDenseMaxT) are packed two per 32-bit LDS
+// word and the bitmaps reuse the histogram memory; per-query rows are padded
+// so that the 16 queries of a wave instruction fall in different LDS banks,
+// and a wave owns whole bitmap words, which it writes with plain stores.
 constexpr int kDenseQ = 16;              // queries per workgroup (one MFMA column block)
 constexpr int kDenseWaves = 8;
-constexpr int kDenseUnroll = 4;          // position tiles per wave in flight
-constexpr int kDenseHistWords = kRadixBins / 2;   // packed histogram words per query
-constexpr int kDenseMapWords = kDenseMaxT / 32;   // bitmap words per query
+constexpr int kDenseUnroll = 8;          // position tiles per wave per load batch
+constexpr int kDenseBatchPos = 16 * kDenseUnroll;
+constexpr int kDenseBatchWords = kDenseBatchPos / 32;
+constexpr int kDenseHistWords = kRadixBins / 2 + 8;   // packed histogram words per query (+ bank pad)
+constexpr int kDenseMapWords = kDenseMaxT / 32 + 4;   // bitmap words per query (+ bank pad)
+constexpr int kDenseList = 128;          // bin-b1 keys per query the two-pass select resolves
 
 typedef int v4i32 __attribute__((ext_vector_type(4)));
 
+// Orders one wave's LDS accesses in the compiler (the hardware performs a
+// wave's LDS instructions in issue order).
+__device__ __forceinline__ void wave_lds_order_sel()
+{
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Threshold search over one query's packed 2048-bin histogram by one wave:
 // the bin b where the count of keys in bins above b is < n <= count in bins
-// >= b; `above` gets the count above b.
-__device__ __forceinline__ void find_bin_packed(const uint32_t *h, uint32_t n, int &bin, uint32_t &above)
+// >= b; `above` gets the count above b and `in_bin` the count in b.
+__device__ __forceinline__ void find_bin_packed(const uint32_t *h, uint32_t n, int &bin, uint32_t &above,
+                                                uint32_t &in_bin)
 {
     const int lane = threadIdx.x & 63;
     uint32_t c[16];
@@ -372,13 +392,13 @@ __device__ __forceinline__ void find_bin_packed(const uint32_t *h, uint32_t n, i
     const uint32_t suf = total - incl;   // keys in the bins above this lane's 32
     const bool here = suf < n && suf + S >= n;
     int b = 0;
-    uint32_t run = suf;
+    uint32_t run = suf, cb = 0;
     if (here) {
         for (int k = 15; k >= 0; k--) {
             const uint32_t hi = c[k] >> 16, lo = c[k] & 0xffffu;
-            if (run + hi >= n) { b = 2 * k + 1; break; }
+            if (run + hi >= n) { b = 2 * k + 1; cb = hi; break; }
             run += hi;
-            if (run + lo >= n) { b = 2 * k; break; }
+            if (run + lo >= n) { b = 2 * k; cb = lo; break; }
             run += lo;
         }
     }
@@ -386,6 +406,42 @@ __device__ __forceinline__ void find_bin_packed(const uint32_t *h, uint32_t n, i
     const int src = found ? __builtin_ctzll(found) : 0;
     bin = __builtin_amdgcn_readlane(32 * lane + b, src);
     above = (uint32_t)__builtin_amdgcn_readlane((int)run, src);
+    in_bin = (uint32_t)__builtin_amdgcn_readlane((int)cb, src);
+}
+
+__device__ __forceinline__ uint32_t or_groups(uint32_t x)   // OR over lanes l, l^16, l^32, l^48
+{
+    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = r[0] | r[1];
+    r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return r[0] | r[1];
+}
+
+// Positions of the set bits of one query's bitmap row, in order: lane l
+// covers words 8l .. 8l+7; fn(rank, position) for every set bit, rank being
+// its index among all set bits of the row.
+template <class Fn>
+__device__ __forceinline__ void for_set_bits(const uint32_t *row, uint32_t (&m)[8], Fn &&fn)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(row + 8 * lane + 4 * k);
+        m[4 * k] = a.x; m[4 * k + 1] = a.y; m[4 * k + 2] = a.z; m[4 * k + 3] = a.w;
+    }
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) c += __builtin_popcount(m[k]);
+    uint32_t r = wave_incl_scan(c) - c;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        uint32_t x = m[k];
+        while (x) {
+            const int b = __builtin_ctz(x);
+            x &= x - 1;
+            fn(r++, 256 * lane + 32 * k + b);
+        }
+    }
 }
 
 template <int DIDX>
@@ -395,183 +451,286 @@ __global__ __launch_bounds__(kDenseWaves * 64) void k_topk_dense(TopkParams p)
     constexpr int HW = kDenseHistWords, MW = kDenseMapWords;
     static_assert(2 * kDenseQ * MW <= kDenseQ * HW, "bitmaps reuse the histogram memory");
     __shared__ __attribute__((aligned(16))) uint32_t s_buf[kDenseQ * HW];
+    __shared__ uint32_t s_list[kDenseQ][kDenseList];   // bin-b1 positions, then composite keys
     __shared__ int s_b1[kDenseQ], s_tau[kDenseQ], s_need[kDenseQ];
-    __shared__ uint32_t s_gt1[kDenseQ];
+    __shared__ uint32_t s_gt1[kDenseQ], s_eq1[kDenseQ];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, g = lane >> 4, r16 = lane & 15;
-    const int q0 = blockIdx.x * kDenseQ;
+    // Workgroup b takes query tile b in the first half of the grid and the
+    // tiles from the last one down in the second half, so that the two
+    // workgroups a CU holds at once scan prefixes of complementary length.
+    const int n_wg = (int)gridDim.x, half = n_wg / 2;
+    const int tile_q = (int)blockIdx.x < half ? (int)blockIdx.x : n_wg - 1 - ((int)blockIdx.x - half);
+    const int q0 = tile_q * kDenseQ;
     const int K = p.K;
-    // this lane's query column: q_idx as the B operand, 16 dims per lane group
+    // this lane's query column (sequence, position, q_idx as the B operand)
     const int qi = q0 + r16;
     const bool qvalid = qi < p.n_q;
+    const int sq = qvalid ? p.q_seq[qi] : -1;
     const int tq = qvalid ? p.q_pos[qi] : -1;
     v4i32 qb = {0, 0, 0, 0};
     if (qvalid && 16 * g < DIDX) qb = *reinterpret_cast<const v4i32 *>(p.q_idx + (size_t)qi * DIDX + 16 * g);
+    uint32_t *gt_map = s_buf, *eq_map = s_buf + kDenseQ * MW;   // eq_map doubles as the bin-b1 map
 
     auto zero_buf = [&] {
         for (int x = tid * 4; x < kDenseQ * HW; x += NT * 4) *reinterpret_cast<uint4 *>(s_buf + x) = make_uint4(0, 0, 0, 0);
     };
 
-    uint32_t remaining = 0;
-    for (int jj = 0; jj < kDenseQ; jj++)
-        if (q0 + jj < p.n_q) remaining |= 1u << jj;
+    uint32_t remaining = (uint32_t)__builtin_amdgcn_ballot_w64(qvalid && g == 0) & 0xffffu;
     // the tile's queries, one sequence at a time (every wave takes the same groups)
     while (remaining) {
-        const int s = p.q_seq[q0 + __builtin_ctz(remaining)];
-        uint32_t gmask = 0;
-        int tmax = 0;
-        for (int jj = 0; jj < kDenseQ; jj++)
-            if (((remaining >> jj) & 1) && p.q_seq[q0 + jj] == s) {
-                gmask |= 1u << jj;
-                tmax = max(tmax, p.q_pos[q0 + jj]);
-            }
+        const int s = __builtin_amdgcn_readlane(sq, __builtin_ctz(remaining));
+        const bool in_group = qvalid && sq == s && ((remaining >> r16) & 1);
+        const uint32_t gmask = (uint32_t)__builtin_amdgcn_ballot_w64(in_group && g == 0) & 0xffffu;
         remaining &= ~gmask;
-        const bool mine = (gmask >> r16) & 1;
-        const int n_tiles = tmax / 16 + 1;
+        int tmax = 0, tmin = INT32_MAX;
+        for (uint32_t m = gmask; m; m &= m - 1) {
+            const int t = __builtin_amdgcn_readlane(tq, __builtin_ctz(m));
+            tmax = max(tmax, t);
+            tmin = min(tmin, t);
+        }
+        const bool mine = in_group;
         const int8_t *rows = p.k_idx + (size_t)s * p.T * DIDX;
 
-        // Runs fn(pos0, d) for this wave's position tiles: d[ii] is the score
-        // of position pos0 + 4g + ii for query column r16.
-        auto scan = [&](auto &&fn) {
-            for (int tb = w; tb < n_tiles; tb += kDenseWaves * kDenseUnroll) {
+        // Runs fn(u, pos0, d, check) for every position tile of this wave and
+        // done(word0) after each batch: batch gi covers positions
+        // kDenseBatchPos * gi .. + kDenseBatchPos - 1 (bitmap words
+        // kDenseBatchWords * gi ..), tile u of it positions pos0 =
+        // kDenseBatchPos * gi + 16 u ..; d[ii] is the score of position
+        // pos0 + 4g + ii for query column r16, and `check` is false when every
+        // position of the tile precedes every query.  A batch's loads are
+        // issued together and unconditionally (rows clamped into the
+        // sequence; the dims a d_idx of 32 lacks meet zeros in q_idx).
+        const int n_batches = tmax / kDenseBatchPos + 1;
+        auto scan = [&](auto &&fn, auto &&done) {
+            const int part = (16 * g < DIDX) ? 16 * g : 16 * (g & 1);
+            for (int gi = w; gi < n_batches; gi += kDenseWaves) {
                 v4i32 a[kDenseUnroll];
 #pragma unroll
                 for (int u = 0; u < kDenseUnroll; u++) {
-                    const int pos = 16 * (tb + u * kDenseWaves) + r16;
-                    a[u] = v4i32{0, 0, 0, 0};
-                    if (tb + u * kDenseWaves < n_tiles && pos < p.T && 16 * g < DIDX)
-                        a[u] = *reinterpret_cast<const v4i32 *>(rows + (size_t)pos * DIDX + 16 * g);
+                    const int pos = min(kDenseBatchPos * gi + 16 * u + r16, p.T - 1);
+                    a[u] = *reinterpret_cast<const v4i32 *>(rows + (size_t)pos * DIDX + part);
                 }
 #pragma unroll
                 for (int u = 0; u < kDenseUnroll; u++) {
-                    const int tile = tb + u * kDenseWaves;
-                    if (tile < n_tiles) {
+                    const int pos0 = kDenseBatchPos * gi + 16 * u;
+                    if (pos0 <= tmax) {
                         const v4i32 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], qb, v4i32{0, 0, 0, 0}, 0, 0, 0);
-                        fn(16 * tile, d);
+                        if (pos0 + 15 > tmin) fn(u, pos0, d, true);
+                        else fn(u, pos0, d, false);
                     }
                 }
+                done(kDenseBatchWords * gi);
+            }
+        };
+        auto nothing = [](int) {};
+        // bits of this batch for query column r16 (OR over the lane groups),
+        // stored by lane group 0 as the batch's bitmap words
+        auto store_bits = [&](uint32_t *map, int word0, uint32_t (&bits)[kDenseBatchWords]) {
+#pragma unroll
+            for (int k = 0; k < kDenseBatchWords; k++) {
+                const uint32_t b = or_groups(bits[k]);
+                if (g == 0 && mine && word0 + k < MW) map[r16 * MW + word0 + k] = b;
+                bits[k] = 0u;
             }
         };
 
         // ---- pass 1: top-bit histograms
         zero_buf();
         __syncthreads();
-        scan([&](int pos0, v4i32 d) {
+        scan([&](int, int pos0, v4i32 d, bool check) {
+            if (!mine) return;
 #pragma unroll
             for (int ii = 0; ii < 4; ii++) {
-                const int pos = pos0 + 4 * g + ii;
-                if (mine && pos <= tq) {
+                if (!check || pos0 + 4 * g + ii <= tq) {
                     const uint32_t b = ((uint32_t)(d[ii] + (int)kKeyBias)) >> kRadixBits;
                     atomicAdd(&s_buf[r16 * HW + (b >> 1)], 1u << (16 * (b & 1)));
                 }
             }
-        });
+        }, nothing);
         __syncthreads();
         for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
             if (!((gmask >> jq) & 1)) continue;
-            const uint32_t n = (uint32_t)p.q_pos[q0 + jq] + 1;
-            int b1 = -1;
-            uint32_t gt1 = 0;
-            if (n > (uint32_t)K) find_bin_packed(s_buf + jq * HW, (uint32_t)K, b1, gt1);
+            const uint32_t n = (uint32_t)__builtin_amdgcn_readlane(tq, jq) + 1;
+            int b1 = -1;                 // fewer candidates than K: every key is taken
+            uint32_t gt1 = 0, eq1 = 0;
+            if (n > (uint32_t)K) find_bin_packed(s_buf + jq * HW, (uint32_t)K, b1, gt1, eq1);
             if (lane == 0) {
                 s_b1[jq] = b1;
                 s_gt1[jq] = gt1;
+                s_eq1[jq] = eq1;
+                s_need[jq] = 0;
             }
         }
         __syncthreads();
-        // ---- pass 2: low-bit histograms inside the threshold bin
+        const int b1q = mine ? s_b1[r16] : -1;
+        const bool listed = __syncthreads_and(!mine || s_eq1[r16] <= (uint32_t)kDenseList);
         zero_buf();
         __syncthreads();
-        const int b1q = mine ? s_b1[r16] : -1;
-        if (__syncthreads_or(b1q >= 0)) {
-            scan([&](int pos0, v4i32 d) {
+        if (listed) {
+            // ---- pass 2: bitmaps of keys above bin b1 and of keys in bin b1
+            uint32_t gw[kDenseBatchWords] = {}, bw[kDenseBatchWords] = {};
+            scan([&](int u, int pos0, v4i32 d, bool check) {
+                if (!mine) return;
 #pragma unroll
                 for (int ii = 0; ii < 4; ii++) {
                     const int pos = pos0 + 4 * g + ii;
+                    const bool ok = !check || pos <= tq;
+                    const int b = (int)(((uint32_t)(d[ii] + (int)kKeyBias)) >> kRadixBits);
+                    gw[u >> 1] |= (uint32_t)(ok && b > b1q) << (pos & 31);
+                    bw[u >> 1] |= (uint32_t)(ok && b == b1q) << (pos & 31);
+                }
+            }, [&](int word0) {
+                store_bits(gt_map, word0, gw);
+                store_bits(eq_map, word0, bw);
+            });
+            __syncthreads();
+            // bin b1: score its (at most kDenseList) keys again and add the
+            // K - gt1 best by (key desc, position asc) to the first bitmap
+            for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
+                if (!((gmask >> jq) & 1) || s_b1[jq] < 0) continue;
+                const int n_list = (int)s_eq1[jq];
+                const int need1 = K - (int)s_gt1[jq];
+                uint32_t m[8];
+                for_set_bits(eq_map + jq * MW, m, [&](uint32_t r, int pos) {
+                    if (r < (uint32_t)kDenseList) s_list[jq][r] = (uint32_t)pos;
+                });
+                wave_lds_order_sel();
+                // composite key: low 11 key bits above (kDenseMaxT - 1 - position)
+                const int8_t *qrow = p.q_idx + (size_t)(q0 + jq) * DIDX;
+                uint32_t c[2] = {0u, 0u};
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int x = lane + 64 * h;
+                    if (x < n_list) {
+                        const int pos = (int)s_list[jq][x];
+                        const int8_t *krow = rows + (size_t)pos * DIDX;
+                        int acc = 0;
+#pragma unroll
+                        for (int k = 0; k < DIDX / 16; k++) {
+                            const int4 a = *reinterpret_cast<const int4 *>(krow + 16 * k);
+                            const int4 b = *reinterpret_cast<const int4 *>(qrow + 16 * k);
+                            acc = dot4_i8(a.x, b.x, acc);
+                            acc = dot4_i8(a.y, b.y, acc);
+                            acc = dot4_i8(a.z, b.z, acc);
+                            acc = dot4_i8(a.w, b.w, acc);
+                        }
+                        const uint32_t low = ((uint32_t)(acc + (int)kKeyBias)) & kRadixMask;
+                        c[h] = (low << 14) | (uint32_t)(kDenseMaxT - 1 - pos);
+                    }
+                }
+                // rank of each entry = entries with a larger composite key
+                int rank[2] = {0, 0};
+                for (int y = 0; y < n_list; y++) {
+                    const uint32_t cy = (uint32_t)__builtin_amdgcn_readlane((int)c[y >> 6], y & 63);
+                    rank[0] += cy > c[0];
+                    rank[1] += cy > c[1];
+                }
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int x = lane + 64 * h;
+                    if (x < n_list && rank[h] < need1) {
+                        const int pos = kDenseMaxT - 1 - (int)(c[h] & 0x3fffu);
+                        atomicOr(&gt_map[jq * MW + (pos >> 5)], 1u << (pos & 31));
+                    }
+                }
+            }
+        } else {
+            // ---- pass 2': low-bit histograms inside the threshold bin
+            scan([&](int, int pos0, v4i32 d, bool check) {
+                if (b1q < 0) return;
+#pragma unroll
+                for (int ii = 0; ii < 4; ii++) {
                     const uint32_t key = (uint32_t)(d[ii] + (int)kKeyBias);
-                    if (b1q >= 0 && pos <= tq && (int)(key >> kRadixBits) == b1q) {
+                    if ((!check || pos0 + 4 * g + ii <= tq) && (int)(key >> kRadixBits) == b1q) {
                         const uint32_t b = key & kRadixMask;
                         atomicAdd(&s_buf[r16 * HW + (b >> 1)], 1u << (16 * (b & 1)));
                     }
                 }
-            });
-        }
-        __syncthreads();
-        for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
-            if (!((gmask >> jq) & 1)) continue;
-            const int b1 = s_b1[jq];
-            int tau = 0, need = 0;   // fewer candidates than K: every key (> 0) is taken
-            if (b1 >= 0) {
-                const uint32_t need1 = (uint32_t)K - s_gt1[jq];
-                int b2;
-                uint32_t gt2;
-                find_bin_packed(s_buf + jq * HW, need1, b2, gt2);
-                tau = (b1 << kRadixBits) | b2;
-                need = (int)(need1 - gt2);
-            }
-            if (lane == 0) {
-                s_tau[jq] = tau;
-                s_need[jq] = need;
-            }
-        }
-        __syncthreads();
-        // ---- pass 3: bitmaps of keys above tau and equal to tau
-        zero_buf();
-        __syncthreads();
-        const uint32_t tauq = mine ? (uint32_t)s_tau[r16] : 0u;
-        uint32_t *gt_map = s_buf, *eq_map = s_buf + kDenseQ * MW;
-        scan([&](int pos0, v4i32 d) {
-            uint32_t gb = 0, eb = 0;
-#pragma unroll
-            for (int ii = 0; ii < 4; ii++) {
-                const int pos = pos0 + 4 * g + ii;
-                const uint32_t key = (uint32_t)(d[ii] + (int)kKeyBias);
-                if (mine && pos <= tq) {
-                    gb |= (uint32_t)(key > tauq) << (pos & 31);
-                    eb |= (uint32_t)(key == tauq) << (pos & 31);
+            }, nothing);
+            __syncthreads();
+            for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
+                if (!((gmask >> jq) & 1)) continue;
+                const int b1 = s_b1[jq];
+                int tau = 0, need = 0;   // fewer candidates than K: every key (> 0) is taken
+                if (b1 >= 0) {
+                    const uint32_t need1 = (uint32_t)K - s_gt1[jq];
+                    int b2;
+                    uint32_t gt2, eq2;
+                    find_bin_packed(s_buf + jq * HW, need1, b2, gt2, eq2);
+                    tau = (b1 << kRadixBits) | b2;
+                    need = (int)(need1 - gt2);
+                }
+                if (lane == 0) {
+                    s_tau[jq] = tau;
+                    s_need[jq] = need;
                 }
             }
-            const int wd = r16 * MW + ((pos0 + 4 * g) >> 5);
-            if (gb) atomicOr(&gt_map[wd], gb);
-            if (eb) atomicOr(&eq_map[wd], eb);
-        });
+            __syncthreads();
+            // ---- pass 3: bitmaps of keys above tau and equal to tau
+            zero_buf();
+            __syncthreads();
+            const uint32_t tauq = mine ? (uint32_t)s_tau[r16] : 0u;
+            uint32_t gw[kDenseBatchWords] = {}, ew[kDenseBatchWords] = {};
+            scan([&](int u, int pos0, v4i32 d, bool check) {
+                if (!mine) return;
+#pragma unroll
+                for (int ii = 0; ii < 4; ii++) {
+                    const int pos = pos0 + 4 * g + ii;
+                    const bool ok = !check || pos <= tq;
+                    const uint32_t key = (uint32_t)(d[ii] + (int)kKeyBias);
+                    gw[u >> 1] |= (uint32_t)(ok && key > tauq) << (pos & 31);
+                    ew[u >> 1] |= (uint32_t)(ok && key == tauq) << (pos & 31);
+                }
+            }, [&](int word0) {
+                store_bits(gt_map, word0, gw);
+                store_bits(eq_map, word0, ew);
+            });
+        }
         __syncthreads();
         // ---- ordered emit: lane l covers positions 256 l .. 256 l + 255
         for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
             if (!((gmask >> jq) & 1)) continue;
             const int i = q0 + jq;
-            const int n = p.q_pos[i] + 1;
+            const int n = __builtin_amdgcn_readlane(tq, jq) + 1;
             const int cnt = min(n, K);
-            int need = s_need[jq];
-            uint32_t gt[8], eq[8];
+            const int need = s_need[jq];   // ties to take (the third pass only)
+            uint32_t gt[8];
 #pragma unroll
             for (int k = 0; k < 2; k++) {
                 const uint4 a = *reinterpret_cast<const uint4 *>(gt_map + jq * MW + 8 * lane + 4 * k);
-                const uint4 b = *reinterpret_cast<const uint4 *>(eq_map + jq * MW + 8 * lane + 4 * k);
                 gt[4 * k] = a.x; gt[4 * k + 1] = a.y; gt[4 * k + 2] = a.z; gt[4 * k + 3] = a.w;
-                eq[4 * k] = b.x; eq[4 * k + 1] = b.y; eq[4 * k + 2] = b.z; eq[4 * k + 3] = b.w;
             }
-            // ties: the first `need` keys equal to tau in position order
-            uint32_t ec = 0;
+            if (need > 0) {
+                // the first `need` keys equal to tau in position order
+                uint32_t eq[8];
 #pragma unroll
-            for (int k = 0; k < 8; k++) ec += __builtin_popcount(eq[k]);
-            const int e_before = (int)(wave_incl_scan(ec) - ec);
-            int take = min(max(need - e_before, 0), (int)ec);
+                for (int k = 0; k < 2; k++) {
+                    const uint4 b = *reinterpret_cast<const uint4 *>(eq_map + jq * MW + 8 * lane + 4 * k);
+                    eq[4 * k] = b.x; eq[4 * k + 1] = b.y; eq[4 * k + 2] = b.z; eq[4 * k + 3] = b.w;
+                }
+                uint32_t ec = 0;
+#pragma unroll
+                for (int k = 0; k < 8; k++) ec += __builtin_popcount(eq[k]);
+                const int e_before = (int)(wave_incl_scan(ec) - ec);
+                int take = min(max(need - e_before, 0), (int)ec);
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    uint32_t x = eq[k], m = 0;
+                    while (take > 0 && x) {
+                        const uint32_t lsb = x & (0u - x);
+                        m |= lsb;
+                        x ^= lsb;
+                        take--;
+                    }
+                    gt[k] |= m;
+                }
+            }
             uint32_t sc = 0;
 #pragma unroll
-            for (int k = 0; k < 8; k++) {
-                uint32_t x = eq[k], m = 0;
-                while (take > 0 && x) {
-                    const uint32_t lsb = x & (0u - x);
-                    m |= lsb;
-                    x ^= lsb;
-                    take--;
-                }
-                gt[k] |= m;
-                sc += __builtin_popcount(gt[k]);
-            }
+            for (int k = 0; k < 8; k++) sc += __builtin_popcount(gt[k]);
             uint32_t slot = wave_incl_scan(sc) - sc;
             int32_t *out = p.topk + (size_t)i * K;
 #pragma unroll
