@@ -75,6 +75,7 @@ struct SelectPlan {
     bool split;       // scores go through the workspace (G > 1 or too many for LDS)
     size_t key_bytes; // workspace bytes for the scores
     bool dense = false;   // token Top-K: every pool is the whole prefix (MFMA tile kernel)
+    bool all = false;     // block pass: every pool is the whole prefix (no scoring)
 };
 
 struct AttendPlan {

@@ -179,6 +179,51 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     if (tid == 0) p.blk_cnt[q] = (int32_t)min(chosen, cap);
 }
 
+// Pools when every eligible block of every query fits (n_elig <= P for the
+// longest context): the pool of a query is its blocks 0 .. t/B, so no score
+// is needed.  A grid-stride kernel writes the ids (then -1 padding), 16 bytes
+// per store when the rows allow it, and the counts; a Full layer also stores
+// the key of the block its query completes.
+constexpr int kPoolAllThreads = 256;
+constexpr int kPoolAllBlocks = 2048;
+
+template <int DIDX>
+__global__ __launch_bounds__(kPoolAllThreads) void k_pool_all(IndexParams p)
+{
+    constexpr int LPR = DIDX / 16;
+    const size_t stride = (size_t)gridDim.x * kPoolAllThreads;
+    const size_t id = (size_t)blockIdx.x * kPoolAllThreads + threadIdx.x;
+    const bool vec = (p.P % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.blk_ids) & 15) == 0);
+    if (vec) {
+        const int P4 = p.P / 4;
+        const size_t total = (size_t)p.n_q * P4;
+        for (size_t k = id; k < total; k += stride) {
+            const int q = (int)(k / P4), j = 4 * (int)(k % P4);
+            const int n = p.q_pos[q] / p.B + 1;
+            const int4 v = make_int4(j < n ? j : -1, j + 1 < n ? j + 1 : -1, j + 2 < n ? j + 2 : -1,
+                                     j + 3 < n ? j + 3 : -1);
+            *reinterpret_cast<int4 *>(p.blk_ids + (size_t)q * p.P + j) = v;
+        }
+    } else {
+        const size_t total = (size_t)p.n_q * p.P;
+        for (size_t k = id; k < total; k += stride) {
+            const int q = (int)(k / p.P), j = (int)(k % p.P);
+            p.blk_ids[k] = (j < p.q_pos[q] / p.B + 1) ? j : -1;
+        }
+    }
+    for (size_t k = id; k < (size_t)p.n_q * LPR; k += stride) {
+        const int q = (int)(k / LPR), part = (int)(k % LPR);
+        const int s = p.q_seq[q], t = p.q_pos[q];
+        const int jt = t / p.B;
+        if (part == 0) p.blk_cnt[q] = jt + 1;
+        if (p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk) {
+            const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX + part * 16;
+            *reinterpret_cast<int4 *>(p.k_blk_store + ((size_t)s * p.nblk + jt) * DIDX + part * 16) =
+                block_key_part<DIDX>(own_rows, p.B);
+        }
+    }
+}
+
 // Pool selection of a split launch: one workgroup per query, after every
 // scoring workgroup of k_index_blocks<.., true> has finished (kernel order).
 // The histogram (pass 1) and the keys are loaded together.
@@ -445,7 +490,7 @@ __device__ __forceinline__ void for_set_bits(const uint32_t *row, uint32_t (&m)[
 }
 
 template <int DIDX>
-__global__ __launch_bounds__(kDenseWaves * 64) void k_topk_dense(TopkParams p)
+__global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_topk_dense(TopkParams p)
 {
     constexpr int NT = kDenseWaves * 64;
     constexpr int HW = kDenseHistWords, MW = kDenseMapWords;
@@ -598,28 +643,33 @@ __global__ __launch_bounds__(kDenseWaves * 64) void k_topk_dense(TopkParams p)
                     if (r < (uint32_t)kDenseList) s_list[jq][r] = (uint32_t)pos;
                 });
                 wave_lds_order_sel();
-                // composite key: low 11 key bits above (kDenseMaxT - 1 - position)
                 const int8_t *qrow = p.q_idx + (size_t)(q0 + jq) * DIDX;
-                uint32_t c[2] = {0u, 0u};
+                int4 qv[DIDX / 16], kv[2][DIDX / 16];
+                int pos_e[2];
+#pragma unroll
+                for (int k = 0; k < DIDX / 16; k++) qv[k] = *reinterpret_cast<const int4 *>(qrow + 16 * k);
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const int x = lane + 64 * h;
-                    if (x < n_list) {
-                        const int pos = (int)s_list[jq][x];
-                        const int8_t *krow = rows + (size_t)pos * DIDX;
-                        int acc = 0;
+                    pos_e[h] = (x < n_list) ? (int)s_list[jq][x] : 0;
 #pragma unroll
-                        for (int k = 0; k < DIDX / 16; k++) {
-                            const int4 a = *reinterpret_cast<const int4 *>(krow + 16 * k);
-                            const int4 b = *reinterpret_cast<const int4 *>(qrow + 16 * k);
-                            acc = dot4_i8(a.x, b.x, acc);
-                            acc = dot4_i8(a.y, b.y, acc);
-                            acc = dot4_i8(a.z, b.z, acc);
-                            acc = dot4_i8(a.w, b.w, acc);
-                        }
-                        const uint32_t low = ((uint32_t)(acc + (int)kKeyBias)) & kRadixMask;
-                        c[h] = (low << 14) | (uint32_t)(kDenseMaxT - 1 - pos);
+                    for (int k = 0; k < DIDX / 16; k++)
+                        kv[h][k] = *reinterpret_cast<const int4 *>(rows + (size_t)pos_e[h] * DIDX + 16 * k);
+                }
+                // composite key: low 11 key bits above (kDenseMaxT - 1 - position)
+                uint32_t c[2];
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    int acc = 0;
+#pragma unroll
+                    for (int k = 0; k < DIDX / 16; k++) {
+                        acc = dot4_i8(kv[h][k].x, qv[k].x, acc);
+                        acc = dot4_i8(kv[h][k].y, qv[k].y, acc);
+                        acc = dot4_i8(kv[h][k].z, qv[k].z, acc);
+                        acc = dot4_i8(kv[h][k].w, qv[k].w, acc);
                     }
+                    const uint32_t low = ((uint32_t)(acc + (int)kKeyBias)) & kRadixMask;
+                    c[h] = (lane + 64 * h < n_list) ? (low << 14) | (uint32_t)(kDenseMaxT - 1 - pos_e[h]) : 0u;
                 }
                 // rank of each entry = entries with a larger composite key
                 int rank[2] = {0, 0};
@@ -629,13 +679,9 @@ __global__ __launch_bounds__(kDenseWaves * 64) void k_topk_dense(TopkParams p)
                     rank[1] += cy > c[1];
                 }
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const int x = lane + 64 * h;
-                    if (x < n_list && rank[h] < need1) {
-                        const int pos = kDenseMaxT - 1 - (int)(c[h] & 0x3fffu);
-                        atomicOr(&gt_map[jq * MW + (pos >> 5)], 1u << (pos & 31));
-                    }
-                }
+                for (int h = 0; h < 2; h++)
+                    if (lane + 64 * h < n_list && rank[h] < need1)
+                        atomicOr(&gt_map[jq * MW + (pos_e[h] >> 5)], 1u << (pos_e[h] & 31));
             }
         } else {
             // ---- pass 2': low-bit histograms inside the threshold bin
@@ -690,58 +736,44 @@ __global__ __launch_bounds__(kDenseWaves * 64) void k_topk_dense(TopkParams p)
             });
         }
         __syncthreads();
-        // ---- ordered emit: lane l covers positions 256 l .. 256 l + 255
+        // ---- ordered emit, 64 bitmap words (2048 positions) per round: lane l
+        // takes word 64 r + l, so a round costs at most 32 bit steps
         for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
             if (!((gmask >> jq) & 1)) continue;
             const int i = q0 + jq;
             const int n = __builtin_amdgcn_readlane(tq, jq) + 1;
             const int cnt = min(n, K);
             const int need = s_need[jq];   // ties to take (the third pass only)
-            uint32_t gt[8];
-#pragma unroll
-            for (int k = 0; k < 2; k++) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(gt_map + jq * MW + 8 * lane + 4 * k);
-                gt[4 * k] = a.x; gt[4 * k + 1] = a.y; gt[4 * k + 2] = a.z; gt[4 * k + 3] = a.w;
-            }
-            if (need > 0) {
-                // the first `need` keys equal to tau in position order
-                uint32_t eq[8];
-#pragma unroll
-                for (int k = 0; k < 2; k++) {
-                    const uint4 b = *reinterpret_cast<const uint4 *>(eq_map + jq * MW + 8 * lane + 4 * k);
-                    eq[4 * k] = b.x; eq[4 * k + 1] = b.y; eq[4 * k + 2] = b.z; eq[4 * k + 3] = b.w;
-                }
-                uint32_t ec = 0;
-#pragma unroll
-                for (int k = 0; k < 8; k++) ec += __builtin_popcount(eq[k]);
-                const int e_before = (int)(wave_incl_scan(ec) - ec);
-                int take = min(max(need - e_before, 0), (int)ec);
-#pragma unroll
-                for (int k = 0; k < 8; k++) {
-                    uint32_t x = eq[k], m = 0;
-                    while (take > 0 && x) {
-                        const uint32_t lsb = x & (0u - x);
-                        m |= lsb;
-                        x ^= lsb;
+            int32_t *out = p.topk + (size_t)i * K;
+            const int n_words = (n + 31) / 32;
+            uint32_t base = 0, ties = 0;
+            for (int r0 = 0; r0 < n_words; r0 += 64) {
+                const int wd = r0 + lane;
+                uint32_t x = (wd < n_words) ? gt_map[jq * MW + wd] : 0u;
+                if (need > 0) {
+                    // the first `need` keys equal to tau in position order
+                    uint32_t e = (wd < n_words) ? eq_map[jq * MW + wd] : 0u;
+                    const uint32_t ec = __builtin_popcount(e);
+                    const uint32_t e_incl = wave_incl_scan(ec);
+                    int take = min(max(need - (int)(ties + e_incl - ec), 0), (int)ec);
+                    while (take > 0) {
+                        const uint32_t lsb = e & (0u - e);
+                        x |= lsb;
+                        e ^= lsb;
                         take--;
                     }
-                    gt[k] |= m;
+                    ties += (uint32_t)__builtin_amdgcn_readlane((int)e_incl, 63);
                 }
-            }
-            uint32_t sc = 0;
-#pragma unroll
-            for (int k = 0; k < 8; k++) sc += __builtin_popcount(gt[k]);
-            uint32_t slot = wave_incl_scan(sc) - sc;
-            int32_t *out = p.topk + (size_t)i * K;
-#pragma unroll
-            for (int k = 0; k < 8; k++) {
-                uint32_t x = gt[k];
+                const uint32_t sc = __builtin_popcount(x);
+                const uint32_t s_incl = wave_incl_scan(sc);
+                uint32_t slot = base + s_incl - sc;
                 while (x) {
                     const int b = __builtin_ctz(x);
                     x &= x - 1;
-                    if (slot < (uint32_t)K) out[slot] = 256 * lane + 32 * k + b;
+                    if (slot < (uint32_t)K) out[slot] = 32 * wd + b;
                     slot++;
                 }
+                base += (uint32_t)__builtin_amdgcn_readlane((int)s_incl, 63);
             }
             for (int o = cnt + lane; o < K; o += 64) out[o] = -1;
             if (lane == 0) p.topk_cnt[i] = cnt;
@@ -786,7 +818,11 @@ size_t select_head_bytes(int n_q, bool split)
 SelectPlan plan_index(int n_q, int T, int B, int P, int d_idx)
 {
     const long long n_elig_max = (long long)(T - 1) / B + 1;
-    if (n_elig_max <= P) return SelectPlan{1, (int)n_elig_max, false, 0};
+    if (n_elig_max <= P) {
+        SelectPlan pl{1, (int)n_elig_max, false, 0};
+        pl.all = true;
+        return pl;
+    }
     return plan_scan(n_q, n_elig_max, d_idx, n_elig_max > kLdsKeys);
 }
 
@@ -816,6 +852,12 @@ hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hip
 template <int DIDX>
 static void launch_index_t(const IndexParams &p, const SelectPlan &pl, hipStream_t st, bool with_select)
 {
+    if (pl.all) {
+        const long long work = (long long)p.n_q * std::max(p.P / 4, 1);
+        const unsigned blocks = (unsigned)std::min<long long>((work + kPoolAllThreads - 1) / kPoolAllThreads, kPoolAllBlocks);
+        hipLaunchKernelGGL((k_pool_all<DIDX>), dim3(std::max(blocks, 1u)), dim3(kPoolAllThreads), 0, st, p);
+        return;
+    }
     dim3 grid((unsigned)(p.n_q * pl.G));
     if (pl.split) {
         hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
