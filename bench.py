@@ -1,12 +1,16 @@
 #!/usr/bin/env python3
-"""Benchmark of the CSA2 sparse-attention decode step on one MI355X.
+"""Benchmark of the CSA2 sparse-attention step on one MI355X.
 
-Workload (default ``decode_group_128k``): batch 8, 128K context, one layer
-group of a Full layer plus 5 Reuse layers sharing one index set and one main
-K/V cache; 16 heads x 128, int8 indexer of dim 64, blocks of 8, pool 2,048,
-Top-512 plus a 128-token window.  A step is one pass of the whole path:
-block-key update of the newest block, hierarchical block pass, token Top-K and
-the attention of all 6 layers (48 queries).
+Default workload ``decode_group_128k``: batch 8, 128K context, one layer group
+of a Full layer plus 5 Reuse layers sharing one index set and one main K/V
+cache; 16 heads x 128, int8 indexer of dim 64, blocks of 8, pool 2,048,
+Top-512 plus a 128-token window.  A step is one pass of the whole path: block
+pass (storing the key of the block the newest token completes), token Top-K
+and the attention of all 6 layers (48 queries).  Its roofline is HBM bandwidth.
+
+``--workload prefill_8k``: one 8,192-token prompt, a Full layer and two
+window-only layers (24,576 queries per step); its roofline is the MFMA peak
+(int8 indexer, bf16 attention).
 
 Inputs are resident in HBM before timing starts.  Steps rotate over R device
 replicas of the caches (each with fresh queries) so that the working set of
@@ -28,7 +32,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse-attn queries/sec + achieved HBM GB/s, decode at 128K ctx (1 GPU)"
+METRIC_PREFILL = "sparse-attn queries/sec + MFMA utilisation, prefill of 8K tokens (1 GPU)"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, MI355X
+INT8_PEAK_TOPS = 5000.0
 KERNEL_SOURCES = {
     "index_blocks": ["select.hip", "device_common.h"],
     "topk_tokens": ["select.hip", "device_common.h"],
@@ -64,9 +71,10 @@ def measured_traffic(kernel, workload):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3200)
-    ap.add_argument("--warmup", type=int, default=320)
-    ap.add_argument("--replicas", type=int, default=32)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (decode 3200, prefill 200)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 320, prefill 20)")
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="device replicas rotated over (decode 32, prefill 2: about 450 MB)")
     ap.add_argument("--streams", type=int, default=1,
                     help="independent steps in flight on separate streams (micro-batch overlap); "
                          "each stream owns replicas/streams replicas")
@@ -106,8 +114,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = W.CONFIGS[args.workload]
-    if not cfg.decode:
-        raise SystemExit("bench.py times decode workloads")
+    if args.steps is None:
+        args.steps = 3200 if cfg.decode else 200
+    if args.warmup is None:
+        args.warmup = 320 if cfg.decode else 20
+    if args.replicas is None:
+        args.replicas = 32 if cfg.decode else 2
     R = max(1, args.replicas)
     NS = max(1, args.streams)
     if R % NS:
@@ -205,10 +217,13 @@ def main():
             B.csa2_attend_group(lc, grp.q, dw.q_seq, dw.q_pos, dw.k_main, dw.v_main, grp.k_swa, grp.v_swa,
                                 cfg.swa_first, dw.topk.get(src), dw.topk_cnt.get(src), grp.out, grp.lse, dw.ws)
 
-    algo = pipeline.algorithmic_bytes(cfg)
+    if cfg.decode:
+        work = pipeline.algorithmic_bytes(cfg)            # bytes per launch
+    else:
+        work = pipeline.algorithmic_ops(cfg)              # int8 ops / bf16 flops per launch
     kernels = {}
     for name, fn in (("index_blocks", k_index), ("topk_tokens", k_topk), ("attend", k_attend)):
-        launches = len(algo[name])
+        launches = len(work[name])
         if launches == 0:
             continue
         g = capture(fn, dws)
@@ -221,18 +236,39 @@ def main():
         e.record()
         torch.cuda.synchronize()
         us = s.elapsed_time(e) * 1e3 / (args.kernel_reps * R * launches)
-        per_launch = sum(algo[name]) / launches
-        kernels[name] = {"us_per_launch": round(us, 3), "launches_per_step": launches,
-                         "algorithmic_bytes_per_launch": int(per_launch),
-                         "achieved_gbs": round(per_launch / (us * 1e-6) / 1e9, 1)}
-        log(f"kernel {name}: {us:.2f} us/launch, {kernels[name]['achieved_gbs']} GB/s algorithmic")
+        per_launch = sum(work[name]) / launches
+        rec = {"us_per_launch": round(us, 3), "launches_per_step": launches}
+        if cfg.decode:
+            rec["algorithmic_bytes_per_launch"] = int(per_launch)
+            rec["achieved_gbs"] = round(per_launch / (us * 1e-6) / 1e9, 1)
+            log(f"kernel {name}: {us:.2f} us/launch, {rec['achieved_gbs']} GB/s algorithmic")
+        else:
+            unit = "int8_ops" if name != "attend" else "bf16_flops"
+            rec[f"algorithmic_{unit}_per_launch"] = int(per_launch)
+            rec["achieved_tops"] = round(per_launch / (us * 1e-6) / 1e12, 1)
+            log(f"kernel {name}: {us:.2f} us/launch, {rec['achieved_tops']} T{unit.split('_')[0]}/s")
+        kernels[name] = rec
 
     dom = max(kernels, key=lambda k: kernels[k]["us_per_launch"] * kernels[k]["launches_per_step"])
-    ach = kernels[dom]["achieved_gbs"]
-    traffic = measured_traffic(dom, cfg.name)
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
-    step_bytes = sum(sum(v) for v in algo.values())
+    extra = {}
+    if cfg.decode:
+        ach = kernels[dom]["achieved_gbs"]
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, cfg.name)}
+        step_bytes = sum(sum(v) for v in work.values())
+        extra = {"hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                 "step_algorithmic_bytes": step_bytes}
+    else:
+        peak = BF16_PEAK_TFLOPS if dom == "attend" else INT8_PEAK_TOPS
+        ach = kernels[dom]["achieved_tops"]
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": peak,
+                    "unit": "TFLOP/s" if dom == "attend" else "TOP/s", "frac": round(ach / peak, 4),
+                    "traffic": measured_traffic(dom, cfg.name)}
+        int8_ops = sum(work["index_blocks"]) + sum(work["topk_tokens"])
+        bf16_flops = sum(work["attend"])
+        ideal_us = int8_ops / (INT8_PEAK_TOPS * 1e6) + bf16_flops / (BF16_PEAK_TFLOPS * 1e6)
+        extra = {"step_int8_ops": int8_ops, "step_bf16_flops": bf16_flops,
+                 "mfma_fraction_step": round(ideal_us / (ms_per_step * 1e3), 4)}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same step
     cpu = None
@@ -243,18 +279,33 @@ def main():
         log(f"cpu baseline: oracle steps on {threads} threads for ~{args.cpu_seconds:.0f}s")
         n = 0
         t0 = time.time()
-        while True:
-            oracle.run_layers(wl, threads=threads)
-            n += 1
-            if time.time() - t0 >= args.cpu_seconds:
-                break
-        dt = time.time() - t0
-        cpu = {"value": round(n * n_queries / dt, 2), "unit": "queries/s", "cores": threads, "kind": "oracle",
-               "sample": f"{n} full steps of {cfg.name} ({n_queries} queries each) on replica 0, {dt:.1f}s"}
+        if cfg.decode:
+            while True:
+                oracle.run_layers(wl, threads=threads)
+                n += 1
+                if time.time() - t0 >= args.cpu_seconds:
+                    break
+            dt = time.time() - t0
+            cpu = {"value": round(n * n_queries / dt, 2), "unit": "queries/s", "cores": threads, "kind": "oracle",
+                   "sample": f"{n} full steps of {cfg.name} ({n_queries} queries each) on replica 0, {dt:.1f}s"}
+        else:
+            # prefill: every layer of an evenly spaced sample of query rows
+            rng = np.random.default_rng(0)
+            rows_done = 0
+            while True:
+                rows = np.sort(rng.choice(cfg.n_q, 256, replace=False))
+                oracle.run_layers(wl, rows=rows, threads=threads)
+                rows_done += len(rows)
+                if time.time() - t0 >= args.cpu_seconds:
+                    break
+            dt = time.time() - t0
+            cpu = {"value": round(rows_done * cfg.n_layers / dt, 2), "unit": "queries/s", "cores": threads,
+                   "kind": "oracle",
+                   "sample": f"{rows_done} random query rows of {cfg.name}, all {cfg.n_layers} layers, {dt:.1f}s"}
         log(f"cpu baseline {cpu['value']} queries/s")
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if cfg.decode else METRIC_PREFILL,
         "value": round(value, 1),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -271,8 +322,7 @@ def main():
                    "head_dim": cfg.head_dim, "d_idx": cfg.d_idx, "block": cfg.block, "pool": cfg.pool,
                    "top_k": cfg.top_k, "window": cfg.window, "replicas": R, "streams": NS,
                    "parallelism": "none (1 GPU)"},
-        "hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "step_algorithmic_bytes": step_bytes,
+        **extra,
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from . import binding as B
-from .workloads import Config, Workload
+from .workloads import Config, Workload, query_rows
 
 
 def _dev(a: np.ndarray, device, dtype=None):
@@ -191,4 +191,30 @@ def algorithmic_bytes(cfg: Config) -> dict:
             out["topk_tokens"].append(n_q * (d + pool * 4 + 4 + n_cand * d + K * 4 + 4))
         main = 0 if mode == "swa" else K * 4 + 4 + sel * 2 * D * esz
         out["attend"].append(n_q * (main + len(layers) * per_layer))
+    return out
+
+
+def algorithmic_ops(cfg: Config) -> dict:
+    """Arithmetic each call of one step must do at minimum, for the MFMA
+    roofline of prefill: int8 multiply-adds of the block and token scoring
+    (2 ops each) and the bf16 flops of attention (QK and PV, 2 each), every
+    query at its own position t.  Returns call -> list per launch."""
+    S, T, d, B, P, K, W_, H, D = (cfg.n_seq, cfg.ctx, cfg.d_idx, cfg.block, cfg.pool, cfg.top_k,
+                                  cfg.window, cfg.n_heads, cfg.head_dim)
+    _, q_pos = query_rows(cfg)
+    t = q_pos.astype(np.int64)
+    n_elig = t // B + 1
+    pool = np.minimum(P, n_elig)
+    block_ops = np.where(n_elig > P, n_elig * d * 2, 0)      # no scoring when the pool is the prefix
+    own = t - (n_elig - 1) * B + 1
+    n_cand = pool * B - (B - own)
+    sel = np.minimum(K, n_cand)
+    win = np.minimum(W_, t + 1)
+    out = {"index_blocks": [], "topk_tokens": [], "attend": []}
+    for mode, layers in cfg.groups():
+        if mode in ("full", "reindex"):
+            out["index_blocks"].append(int(block_ops.sum()))
+            out["topk_tokens"].append(int((n_cand * d * 2).sum()))
+        keys = win + (0 if mode == "swa" else sel)
+        out["attend"].append(int(len(layers) * (keys * H * D * 4).sum()))
     return out
