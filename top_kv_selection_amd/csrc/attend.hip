@@ -176,6 +176,20 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         for (int r = threadIdx.x; r < n_pool; r += NT) s_pool[r] = p.sel_pool[(size_t)i * p.sel_P + r];
         hist_to_lds<NT>(hr, s_hist);
         const int n_cand = n_pool * B;
+        // The selection's size is known from the histogram (bin 0 holds the
+        // positions past t), so the window codes of this workgroup's slots,
+        // and the padding past the list when it ends with a window key, are
+        // written now, off the selection's critical path.
+        {
+            const int cnt_pre = min(p.K, n_cand - (int)s_hist[0]);
+            const int nk = cnt_pre + win.nw;
+            const int kb = min(nk, split * p.keys_per_split), ke = min(nk, kb + p.keys_per_split);
+            for (int x = threadIdx.x; x < p.keys_per_split; x += NT) {
+                const int kk = kb + x;
+                if (kk >= cnt_pre && kk < ke) s_rows[x] = -(win.w0 + (kk - cnt_pre) - p.swa_first) - 1;
+                else if (kk >= ke && ke > kb && win.nw > 0) s_rows[x] = -(win.w0 + (ke - 1 - cnt_pre) - p.swa_first) - 1;
+            }
+        }
         mask_keys<IPT>(n_cand, k);
         const Threshold th = threshold_regs<NT, IPT>(k, n_cand, (uint32_t)p.K, s_hist, s_sm);
         const bool writer = (l == 0 && hg == 0 && split == 0);
@@ -328,18 +342,15 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
     uint4 vv[8];
     if (k_begin < k_end) {
         if constexpr (FUSED) {
-            // main slots were written by the selection; add the window and
-            // repeat the last key in the slots past the end
+            // main slots were written by the selection, window slots and (if
+            // the list ends with a window key) the padding before it; without
+            // a window, repeat the last selected key in the slots past the end
             lds_barrier();
-            const int kps = p.keys_per_split;
-            for (int x = threadIdx.x; x < kps; x += NT) {
-                const int kk = k_begin + x;
-                if (kk >= cnt && kk < k_end) s_rows[x] = -(win.w0 + (kk - cnt) - p.swa_first) - 1;
+            if (win.nw == 0) {
+                const int last = s_rows[k_end - 1 - k_begin];
+                for (int x = k_end - k_begin + (int)threadIdx.x; x < p.keys_per_split; x += NT) s_rows[x] = last;
+                lds_barrier();
             }
-            lds_barrier();
-            const int last = s_rows[k_end - 1 - k_begin];
-            for (int x = k_end - k_begin + (int)threadIdx.x; x < kps; x += NT) s_rows[x] = last;
-            lds_barrier();
         } else {
             stage_rows(k_begin);
         }

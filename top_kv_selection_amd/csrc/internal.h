@@ -7,7 +7,8 @@
 
 namespace csa2 {
 
-constexpr int kSelectThreads = 512;     // threads of a selection workgroup
+constexpr int kSelectThreads = 512;     // threads of a scoring or many-query selection workgroup
+constexpr int kSelectWideThreads = 1024; // threads of a one-query-per-workgroup select launch (16 keys each)
 constexpr int kTargetWorkgroups = 512;  // ~2 per CU on a 256-CU MI355X
 constexpr int kMaxCandidates = 16384;   // P*B cap: candidates one query may score
 

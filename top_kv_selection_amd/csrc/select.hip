@@ -862,7 +862,7 @@ static void launch_index_t(const IndexParams &p, const SelectPlan &pl, hipStream
     if (pl.split) {
         hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
         if (with_select)
-            hipLaunchKernelGGL((k_index_select<kSelectThreads>), dim3((unsigned)p.n_q), dim3(kSelectThreads), 0, st, p);
+            hipLaunchKernelGGL((k_index_select<kSelectWideThreads>), dim3((unsigned)p.n_q), dim3(kSelectWideThreads), 0, st, p);
     } else {
         hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
     }
@@ -889,7 +889,7 @@ static void launch_topk_t(const TopkParams &p, const SelectPlan &pl, hipStream_t
     if (pl.split) {
         hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
         if (with_select)
-            hipLaunchKernelGGL((k_topk_select<kSelectThreads>), dim3((unsigned)p.n_q), dim3(kSelectThreads), 0, st, p);
+            hipLaunchKernelGGL((k_topk_select<kSelectWideThreads>), dim3((unsigned)p.n_q), dim3(kSelectWideThreads), 0, st, p);
     } else {
         hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
     }
