@@ -65,11 +65,14 @@ __device__ __forceinline__ int dot16_i8(int4 a, int4 b)
     return dot4_i8(a.w, b.w, acc);
 }
 
+// Sum over the LPR (2 or 4) consecutive lanes of a row with DPP quad
+// permutes (lane ^ 1, then lane ^ 2), which stay in the vector ALU.
 template <int LPR>
 __device__ __forceinline__ int row_reduce(int v)
 {
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) v += __shfl_xor(v, o, 64);
+    static_assert(LPR == 2 || LPR == 4, "rows of 32 or 64 bytes");
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, true);        // quad_perm [1,0,3,2]
+    if (LPR == 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, true);   // quad_perm [2,3,0,1]
     return v;
 }
 
@@ -136,12 +139,10 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     const int8_t *blk_rows = p.k_blk + (size_t)s * p.nblk * DIDX + part * 16;
 
     // the query's own block (computed from its visible rows) belongs to the
-    // workgroup whose range holds it; computed once, outside the unrolled loop
+    // workgroup whose range holds it; its rows are read in the first batch,
+    // after that batch's block-key loads have been issued
     int4 own_key = make_int4(0, 0, 0, 0);
-    if (jt >= lo && jt < hi) {
-        own_key = block_key_part<DIDX>(own_rows, t - jt * p.B + 1);
-        if (store_own && (tid / LPR) == 0) *reinterpret_cast<int4 *>(own_store) = own_key;
-    }
+    bool own_pending = jt >= lo && jt < hi;
     for (int base = lo; base < hi; base += RPP * kUnroll) {
         int4 kv[kUnroll];
 #pragma unroll
@@ -149,6 +150,11 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
             const int j = base + u * RPP + tid / LPR;
             kv[u] = make_int4(0, 0, 0, 0);
             if (j < hi && j < jt) kv[u] = *reinterpret_cast<const int4 *>(blk_rows + (size_t)j * DIDX);
+        }
+        if (own_pending) {
+            own_pending = false;
+            own_key = block_key_part<DIDX>(own_rows, t - jt * p.B + 1);
+            if (store_own && (tid / LPR) == 0) *reinterpret_cast<int4 *>(own_store) = own_key;
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
