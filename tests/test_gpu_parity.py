@@ -153,6 +153,23 @@ def test_prefill_dense_topk_longest_context(lib):
     check(lib, cfg, seed=33, rows=rows)
 
 
+def test_decode_more_blocks_than_one_workgroup_holds(lib):
+    """Blocks of 2 at a 40,000-token context: 20,000 eligible blocks, more than
+    the 16,384 keys one selection workgroup keeps in registers, so the pool is
+    chosen by the streaming two-pass path over the workspace keys."""
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=2, ctx=40000, block=2, pool=4096, top_k=512)
+    check(lib, cfg, seed=34)
+
+
+def test_prefill_window_layer_chunks_and_mixed_tiles(lib):
+    """Window-only layers take the shared-window kernel: a 300-token window is
+    wider than one staged chunk of rows, and with two prompts of 1,003 tokens
+    some 8-query tiles hold queries of both sequences."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], n_seq=2, ctx=1003, pool=128, top_k=200, window=300,
+                   layers=("full", "swa"))
+    check(lib, cfg, seed=35)
+
+
 def test_no_window(lib):
     cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=4096, pool=64, top_k=128, window=0)
     check(lib, cfg, seed=27)

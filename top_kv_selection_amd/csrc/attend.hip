@@ -696,6 +696,277 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
     if (p.lse && g == 0) p.lse[row_id] = (m_run + log2f(L)) * kLn2;
 }
 
+// ============================================================ window kernel
+// Window-only layers with many queries (prefill): neighbouring queries share
+// most of their windows, so a workgroup takes kWinQ consecutive queries and
+// brings the union of their windows into LDS once; its waves then run the row
+// kernel's step on one query at a time with both operands read from LDS (K in
+// the A layout, V^T by the transposing read).  K rows are padded to 272 bytes
+// (the 16 rows of an A-operand read start in different banks) and V rows to
+// 288 bytes (the 8 rows of a transposing read pass do).
+//  * Fast path: the tile's queries share a sequence and the union of their
+//    windows fits kWinRows rows: one staging, each wave takes kWinQPW queries.
+//  * Otherwise the tile is done as kWinQPW parts of kWinWaves queries (one per
+//    wave), each walking the union of its windows in chunks of kWinRows rows,
+//    one sequence at a time; a query's softmax state stays in its wave's
+//    registers across chunks.
+constexpr int kWinWaves = 8;
+constexpr int kWinQPW = 1;               // queries per wave
+constexpr int kWinQ = kWinQPW * kWinWaves;   // queries per workgroup
+constexpr int kWinRows = 136;            // window rows staged at once (8 queries of a 128 window: 135)
+constexpr int kWinKStride = 272;         // bytes per staged K row
+constexpr int kWinVStride = 288;         // bytes per staged V row
+
+// Copies window rows [c0, c0 + n_rows) of K and V (256 bytes each) into the
+// padded LDS rows of the window kernel; every load is issued before the
+// first store, and the stores wait for the workgroup to be done with the
+// previous rows.
+__device__ __forceinline__ void win_stage(const uint8_t *ksrc, const uint8_t *vsrc, int c0, int n_rows,
+                                          uint8_t *s_k, uint8_t *s_v)
+{
+    constexpr int NT = kWinWaves * 64;
+    constexpr int PER = (kWinRows * 16 + NT - 1) / NT;
+    const int tid = threadIdx.x;
+    uint4 k0, k1, k2, k3, k4, v0, v1, v2, v3, v4;
+    static_assert(PER == 5, "staging is written out for five 16-byte pieces per thread");
+    auto src = [&](int u) {
+        const int x = tid + u * NT;
+        return (size_t)(c0 + min(x >> 4, n_rows - 1)) * 256 + 16 * (x & 15);
+    };
+    k0 = *reinterpret_cast<const uint4 *>(ksrc + src(0)); v0 = *reinterpret_cast<const uint4 *>(vsrc + src(0));
+    k1 = *reinterpret_cast<const uint4 *>(ksrc + src(1)); v1 = *reinterpret_cast<const uint4 *>(vsrc + src(1));
+    k2 = *reinterpret_cast<const uint4 *>(ksrc + src(2)); v2 = *reinterpret_cast<const uint4 *>(vsrc + src(2));
+    k3 = *reinterpret_cast<const uint4 *>(ksrc + src(3)); v3 = *reinterpret_cast<const uint4 *>(vsrc + src(3));
+    k4 = *reinterpret_cast<const uint4 *>(ksrc + src(4)); v4 = *reinterpret_cast<const uint4 *>(vsrc + src(4));
+    __syncthreads();
+    auto put = [&](int u, uint4 kv, uint4 vv) {
+        const int x = tid + u * NT;
+        const int r = x >> 4, c = x & 15;
+        if (r < n_rows) {
+            *reinterpret_cast<uint4 *>(s_k + r * kWinKStride + 16 * c) = kv;
+            *reinterpret_cast<uint4 *>(s_v + r * kWinVStride + 16 * c) = vv;
+        }
+    };
+    put(0, k0, v0);
+    put(1, k1, v1);
+    put(2, k2, v2);
+    put(3, k3, v3);
+    put(4, k4, v4);
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kWinWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void k_attend_window(AttendParams p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t s_k[kWinRows * kWinKStride];
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[kWinRows * kWinVStride];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    const int HG = p.H / 16;
+    const int tiles_q = (p.n_q + kWinQ - 1) / kWinQ;
+    // Workgroup b runs on XCD b % 8 (round-robin dispatch); each XCD takes a
+    // contiguous range of tiles, so the window rows it stages stay in its L2.
+    const int per_xcd = (int)gridDim.x / 8;
+    const int tile = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+    if (tile >= tiles_q * HG * p.n_layers) return;   // whole workgroup
+    const int q0 = (tile % tiles_q) * kWinQ;
+    const int hg = (tile / tiles_q) % HG;
+    const int l = tile / (tiles_q * HG);
+
+    // the tile's sequences and window rows (uniform loads)
+    int qs[kWinQ], r0[kWinQ], nw[kWinQ];
+#pragma unroll
+    for (int j = 0; j < kWinQ; j++) {
+        qs[j] = -1;
+        r0[j] = nw[j] = 0;
+        if (q0 + j < p.n_q) {
+            const Window win = window_of(p.q_pos[q0 + j], p.W, p.swa_first, p.swa_len);
+            qs[j] = p.q_seq[q0 + j];
+            r0[j] = win.w0 - p.swa_first;
+            nw[j] = win.nw;
+        }
+    }
+    // Stages window rows [c0, c0 + n_rows) of sequence s (all loads first).
+    auto stage = [&](int s, int c0, int n_rows) {
+        const size_t row0 = ((size_t)l * p.n_seq + s) * p.swa_len;
+        win_stage((const uint8_t *)p.k_swa + row0 * 256, (const uint8_t *)p.v_swa + row0 * 256, c0, n_rows, s_k, s_v);
+    };
+    struct State {
+        bf16x8_t qb[4];
+        f32x4_t acc[8];
+        float m_run, l_part;
+    };
+    auto begin = [&](State &st, int i) {
+        const uint16_t *qrow = (const uint16_t *)p.q + (((size_t)l * p.n_q + i) * p.H + hg * 16 + r16) * 128;
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) st.qb[kk] = *reinterpret_cast<const bf16x8_t *>(qrow + kk * 32 + g * 8);
+#pragma unroll
+        for (int m = 0; m < 8; m++) st.acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        st.m_run = -INFINITY;
+        st.l_part = 0.f;
+    };
+    // The keys of window rows [a, b), staged from row c0, 32 per step.
+    auto attend_rows = [&](State &st, int a, int b, int c0) {
+        for (int k0 = a; k0 < b; k0 += 32) {
+            const int n_valid = min(32, b - k0);
+            bf16x8_t ka[2][4], va[8];
+#pragma unroll
+            for (int tau = 0; tau < 2; tau++) {
+                const int r = min(k0 + 16 * tau + r16, b - 1) - c0;
+#pragma unroll
+                for (int kk = 0; kk < 4; kk++)
+                    ka[tau][kk] = *reinterpret_cast<const bf16x8_t *>(s_k + r * kWinKStride + 64 * kk + 16 * g);
+            }
+            f32x4_t sk[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+                for (int tau = 0; tau < 2; tau++)
+                    sk[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tau][kk], st.qb[kk], sk[tau], 0, 0, 0);
+            // V^T operands after QK, in the registers K has left
+            const int rv0 = min(k0 + 4 * g + (r16 >> 2), b - 1) - c0;
+            const int rv1 = min(k0 + 16 + 4 * g + (r16 >> 2), b - 1) - c0;
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(s_v + rv0 * kWinVStride + 32 * m + 8 * (r16 & 3)));
+                const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(s_v + rv1 * kWinVStride + 32 * m + 8 * (r16 & 3)));
+                const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo4).x, __builtin_bit_cast(uint2, lo4).y,
+                                           __builtin_bit_cast(uint2, hi4).x, __builtin_bit_cast(uint2, hi4).y);
+                va[m] = __builtin_bit_cast(bf16x8_t, u);
+            }
+            float sc[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) sc[e] = sk[e >> 2][e & 3];
+            if (n_valid < 32) {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    if (slot_key(g, e) >= n_valid) sc[e] = -INFINITY;
+            }
+            const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                                   fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))) * p.scale_log2;
+            if (__builtin_amdgcn_ballot_w64(mx > st.m_run + kLazyLog2)) {
+                const float hmax = max_groups(mx);
+                const float m_new = (hmax > st.m_run + kLazyLog2) ? hmax : st.m_run;
+                const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+                st.l_part *= alpha;
+#pragma unroll
+                for (int m = 0; m < 8; m++) st.acc[m] *= alpha;
+                st.m_run = m_new;
+            }
+            const float m_use = (st.m_run == -INFINITY) ? 0.f : st.m_run;
+            bf16x8_t pb;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float pr = __builtin_amdgcn_exp2f(fmaf(sc[e], p.scale_log2, -m_use));
+                st.l_part += pr;
+                pb[e] = (__bf16)pr;
+            }
+#pragma unroll
+            for (int m = 0; m < 8; m++) st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb, st.acc[m], 0, 0, 0);
+        }
+    };
+    // st.acc[m][ii] = O[head r16][dim 16m + 4g + ii] (unnormalised)
+    auto finish = [&](State &st, int i) {
+        const float L = sum_groups(st.l_part);
+        const float inv = 1.f / L;
+        const size_t row_id = ((size_t)l * p.n_q + i) * p.H + hg * 16 + r16;
+        uint16_t *orow = (uint16_t *)p.out + row_id * 128;
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const uint32_t lo2 = (uint32_t)f32_to_bf16(st.acc[m][0] * inv) | ((uint32_t)f32_to_bf16(st.acc[m][1] * inv) << 16);
+            const uint32_t hi2 = (uint32_t)f32_to_bf16(st.acc[m][2] * inv) | ((uint32_t)f32_to_bf16(st.acc[m][3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(orow + 16 * m + 4 * g) = make_uint2(lo2, hi2);
+        }
+        if (p.lse && g == 0) p.lse[row_id] = (st.m_run + log2f(L)) * kLn2;
+    };
+
+    // the fast path's condition: one sequence, and the union fits one staging
+    int s0 = -1, lo = INT32_MAX, hi = 0;
+    bool one_seq = true;
+#pragma unroll
+    for (int j = 0; j < kWinQ; j++) {
+        if (qs[j] < 0 || nw[j] == 0) continue;
+        if (s0 < 0) s0 = qs[j];
+        one_seq = one_seq && qs[j] == s0;
+        lo = min(lo, r0[j]);
+        hi = max(hi, r0[j] + nw[j]);
+    }
+    if (one_seq && (s0 < 0 || hi - lo <= kWinRows)) {
+        if (s0 >= 0) stage(s0, lo, hi - lo);
+#pragma unroll
+        for (int half = 0; half < kWinQPW; half++) {
+            const int j = w + kWinWaves * half, i = q0 + j;
+            if (i >= p.n_q) continue;
+            int my_r0 = 0, my_nw = 0;
+#pragma unroll
+            for (int jj = 0; jj < kWinQ; jj++)
+                if (jj == j) {
+                    my_r0 = r0[jj];
+                    my_nw = nw[jj];
+                }
+            State st;
+            begin(st, i);
+            if (my_nw > 0) attend_rows(st, my_r0, my_r0 + my_nw, lo);
+            finish(st, i);
+        }
+        return;
+    }
+    // general path: parts of kWinWaves queries, chunks of kWinRows rows
+    // (unrolled, so that the tile arrays are indexed by constants)
+#pragma unroll
+    for (int half = 0; half < kWinQPW; half++) {
+        const int j = w + kWinWaves * half, i = q0 + j;
+        const bool valid = i < p.n_q;
+        int my_r0 = 0, my_nw = 0;
+#pragma unroll
+        for (int jj = 0; jj < kWinQ; jj++)
+            if (jj == j) {
+                my_r0 = r0[jj];
+                my_nw = nw[jj];
+            }
+        State st;
+        if (valid) begin(st, i);
+        uint32_t remaining = 0;
+#pragma unroll
+        for (int jj = 0; jj < kWinWaves; jj++) {
+            const int k = jj + kWinWaves * half;
+            if (qs[k] >= 0 && nw[k] > 0) remaining |= 1u << jj;
+        }
+        // one sequence at a time; every wave takes the same groups and chunks
+        while (remaining) {
+            int s = -1;
+#pragma unroll
+            for (int jj = kWinWaves - 1; jj >= 0; jj--)
+                if ((remaining >> jj) & 1) s = qs[jj + kWinWaves * half];
+            uint32_t gmask = 0;
+            int glo = INT32_MAX, ghi = 0;
+#pragma unroll
+            for (int jj = 0; jj < kWinWaves; jj++) {
+                const int k = jj + kWinWaves * half;
+                if (((remaining >> jj) & 1) && qs[k] == s) {
+                    gmask |= 1u << jj;
+                    glo = min(glo, r0[k]);
+                    ghi = max(ghi, r0[k] + nw[k]);
+                }
+            }
+            remaining &= ~gmask;
+            const bool mine = valid && ((gmask >> w) & 1);
+            for (int c0 = glo; c0 < ghi; c0 += kWinRows) {
+                const int n_rows = min(kWinRows, ghi - c0);
+                stage(s, c0, n_rows);
+                if (!mine) continue;
+                const int a = max(my_r0, c0), b = min(my_r0 + my_nw, c0 + n_rows);
+                if (a < b) attend_rows(st, a, b, c0);
+            }
+        }
+        if (valid) finish(st, i);
+    }
+}
+
 // ============================================================ planning / launch
 static int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b); }
 
@@ -727,6 +998,12 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
     if (p0.n_q <= 0 || p0.n_layers <= 0) return hipSuccess;
     AttendParams p = p0;
     const bool rows_fit = (long long)p.T * 256 < INT32_MAX && (long long)p.swa_len * 256 < INT32_MAX;
+    if (pl.rows && !fused_select && p0.topk == nullptr) {
+        // window-only layer with many queries: shared windows in LDS
+        const long long n_wg = (long long)((p.n_q + kWinQ - 1) / kWinQ) * (p.H / 16) * p.n_layers;
+        hipLaunchKernelGGL(k_attend_window, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kWinWaves * 64), 0, st, p);
+        return hipGetLastError();
+    }
     if (pl.rows && !fused_select && rows_fit) {
         const long long items = (long long)p.n_q * p.n_layers * (p.H / 16);
         const long long n_wg = (items + kRowWaves - 1) / kRowWaves;
