@@ -408,6 +408,7 @@ constexpr int kDenseWaves = 8;
 constexpr int kDenseUnroll = 8;          // position tiles per wave per load batch
 constexpr int kDenseBatchPos = 16 * kDenseUnroll;
 constexpr int kDenseBatchWords = kDenseBatchPos / 32;
+static_assert(kDenseBatchPos % 32 == 0, "a batch covers whole bitmap words");
 constexpr int kDenseHistWords = kRadixBins / 2 + 8;   // packed histogram words per query (+ bank pad)
 constexpr int kDenseMapWords = kDenseMaxT / 32 + 4;   // bitmap words per query (+ bank pad)
 constexpr int kDenseList = 128;          // bin-b1 keys per query the two-pass select resolves
@@ -588,18 +589,27 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
             }
         };
 
-        // ---- pass 1: top-bit histograms
+        // every column of the wave is in the group: tiles before every query
+        // need no per-lane test at all
+        const bool all_mine = __builtin_amdgcn_ballot_w64(mine) == ~0ull;
+
+        // ---- pass 1: top-bit histograms.  With key = score + 2^21, the word
+        // of bin key >> 11 is (score >> 12) + 512 and its half is bit 11 of
+        // the score (the bias does not reach bits below 21).
         zero_buf();
         __syncthreads();
+        uint32_t *hrow = s_buf + r16 * HW + (kKeyBias >> (kRadixBits + 1));
+        auto hist_add = [&](int sc) { atomicAdd(&hrow[sc >> (kRadixBits + 1)], ((sc >> kRadixBits) & 1) ? 0x10000u : 1u); };
         scan([&](int, int pos0, v4i32 d, bool check) {
+            if (!check && all_mine) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ii++) hist_add(d[ii]);
+                return;
+            }
             if (!mine) return;
 #pragma unroll
-            for (int ii = 0; ii < 4; ii++) {
-                if (!check || pos0 + 4 * g + ii <= tq) {
-                    const uint32_t b = ((uint32_t)(d[ii] + (int)kKeyBias)) >> kRadixBits;
-                    atomicAdd(&s_buf[r16 * HW + (b >> 1)], 1u << (16 * (b & 1)));
-                }
-            }
+            for (int ii = 0; ii < 4; ii++)
+                if (!check || pos0 + 4 * g + ii <= tq) hist_add(d[ii]);
         }, nothing);
         __syncthreads();
         for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
@@ -623,15 +633,20 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
         if (listed) {
             // ---- pass 2: bitmaps of keys above bin b1 and of keys in bin b1
             uint32_t gw[kDenseBatchWords] = {}, bw[kDenseBatchWords] = {};
+            // bins as score >> 11 (the bias moves every bin by 1024)
+            const int b1s = b1q - (int)(kKeyBias >> kRadixBits);
+            const uint32_t lane_bit = 1u << (4 * g);    // position 4g of a 16-position tile
             scan([&](int u, int pos0, v4i32 d, bool check) {
                 if (!mine) return;
 #pragma unroll
                 for (int ii = 0; ii < 4; ii++) {
-                    const int pos = pos0 + 4 * g + ii;
-                    const bool ok = !check || pos <= tq;
-                    const int b = (int)(((uint32_t)(d[ii] + (int)kKeyBias)) >> kRadixBits);
-                    gw[u >> 1] |= (uint32_t)(ok && b > b1q) << (pos & 31);
-                    bw[u >> 1] |= (uint32_t)(ok && b == b1q) << (pos & 31);
+                    // pos0 is a multiple of 16, so the bit of position
+                    // pos0 + 4g + ii in its word is 16 (u & 1) + 4g + ii
+                    const uint32_t bit = lane_bit << (16 * (u & 1) + ii);
+                    const bool ok = !check || pos0 + 4 * g + ii <= tq;
+                    const int b = d[ii] >> kRadixBits;
+                    gw[u >> 1] |= (ok && b > b1s) ? bit : 0u;
+                    bw[u >> 1] |= (ok && b == b1s) ? bit : 0u;
                 }
             }, [&](int word0) {
                 store_bits(gt_map, word0, gw);
