@@ -75,7 +75,8 @@ typedef enum {
     CSA2_FULL = 0,      /* own keys: update block keys, fresh pool + Top-K, attend */
     CSA2_REINDEX = 1,   /* shared keys, own q_idx: fresh pool + Top-K, attend      */
     CSA2_REUSE = 2,     /* shared keys and indices: attend only                    */
-    CSA2_SWA = 3        /* sliding-window-only layer: attend to the window alone   */
+    CSA2_SWA = 3,       /* sliding-window-only layer: attend to the window alone   */
+    CSA2_REINDEX_TOKENS = 4 /* shared keys and pool, own q_idx: fresh token Top-K  */
 } csa2_mode;
 
 typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
@@ -139,7 +140,9 @@ int32_t csa2_index_blocks(const csa2_cfg *cfg, int32_t n_q, const int8_t *q_idx,
 /* Token Top-K.  The candidates of query row i are the visible positions
  * (p <= t) of its pooled blocks.  If there are at most K, all are selected;
  * otherwise the K with the highest token score, ties to the lower position.
- *   blk_ids, blk_cnt : as written by csa2_index_blocks
+ *   blk_ids, blk_cnt : as written by csa2_index_blocks for the same cfg, T and
+ *                      queries (when every pool is the whole prefix, i.e.
+ *                      (T-1)/B + 1 <= P, they are not read)
  *   topk     : device int32 [n_q][K] out: selected positions ascending, then -1
  *   topk_cnt : device int32 [n_q]    out: number selected                   */
 int32_t csa2_topk_tokens(const csa2_cfg *cfg, int32_t n_q, const int8_t *q_idx,
@@ -191,8 +194,13 @@ int32_t csa2_attend(const csa2_cfg *cfg, int32_t n_q, const void *q, const int32
  *                  over the shared k_idx/k_blk (read only), csa2_attend_group
  *   CSA2_REUSE   : csa2_attend_group with the given topk/topk_cnt (read only)
  *   CSA2_SWA     : csa2_attend_group with no main entries (topk ignored)
+ *   CSA2_REINDEX_TOKENS : csa2_topk_tokens with this layer's q_idx over the
+ *                  given pool (blk_ids/blk_cnt of the group whose index set it
+ *                  shares, read only), csa2_attend_group: the reading of the
+ *                  Reindex layer that recomputes only the token Top-K
  * blk_ids/blk_cnt/topk/topk_cnt are outputs for FULL/REINDEX, inputs for
- * REUSE.  Shapes as in the calls above. */
+ * REUSE; for REINDEX_TOKENS blk_ids/blk_cnt are inputs and topk/topk_cnt
+ * outputs.  Shapes as in the calls above. */
 int32_t csa2_layer_group(const csa2_cfg *cfg, int32_t mode, int32_t n_layers, int32_t n_q,
                          const int8_t *q_idx, const int32_t *q_seq, const int32_t *q_pos,
                          const int8_t *k_idx, int8_t *k_blk, int32_t blk_update_begin,

@@ -11,7 +11,10 @@ the C loops over independent query ranges (ctypes releases the GIL), and applies
 the layer-mode rules of the "CSA2 with cross-layer reuse" mode table on the
 DeepSeek V4.1 Flash page (k-a.in): Full and Reindex layers compute fresh
 indices with their own indexer query, Reuse layers take the indices of the most
-recent Full/Reindex layer, and every layer has its own Q and window K/V.
+recent Full/Reindex layer, and every layer has its own Q and window K/V.  A
+token-only Reindex layer (the page's Reindex "recomputes only the Top-K"
+reading) keeps the pool of the most recent index set and reselects the tokens
+with its own indexer query.
 Sliding-window-only layers (the page's first two encoder layers) attend to the
 window alone.
 """
@@ -61,6 +64,8 @@ def lib():
         L.orc_select_batch.restype = i32
         L.orc_select_batch.argtypes = [i32, i32, P, P, P, P, i32, i32, i32, i32, i32, i32,
                                        P, P, P, P]
+        L.orc_topk_batch.restype = i32
+        L.orc_topk_batch.argtypes = [i32, i32, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]
         L.orc_attend_batch.restype = i32
         L.orc_attend_batch.argtypes = [i32, i32, P, P, P, P, P, i32, i32, P, P, i32, i32,
                                        P, P, i32, i32, i32, i32, i32, ctypes.c_double, P, P]
@@ -157,6 +162,35 @@ def select(q_idx, q_seq, q_pos, k_idx, B, P, K, threads=None):
     return blk_ids, blk_cnt, topk, topk_cnt
 
 
+def topk_given_pool(q_idx, q_seq, q_pos, k_idx, B, K, blk_ids, blk_cnt, threads=None):
+    """Step 5 alone over given pools: the Reindex variant that keeps the pool
+    of the shared index set and reselects only the tokens with its own
+    q_idx.  blk_ids [n_q][P] ascending, -1 padded; blk_cnt [n_q].
+    Returns (topk [n_q][K], topk_cnt [n_q])."""
+    q_idx = np.ascontiguousarray(q_idx, dtype=np.int8)
+    k_idx = np.ascontiguousarray(k_idx, dtype=np.int8)
+    q_seq = np.ascontiguousarray(q_seq, dtype=np.int32)
+    q_pos = np.ascontiguousarray(q_pos, dtype=np.int32)
+    blk_ids = np.ascontiguousarray(blk_ids, dtype=np.int32)
+    blk_cnt = np.ascontiguousarray(blk_cnt, dtype=np.int32)
+    n_q, d = q_idx.shape
+    S, T, d2 = k_idx.shape
+    assert d == d2 and blk_ids.shape[0] == n_q
+    P = blk_ids.shape[1]
+    topk = np.empty((n_q, max(K, 1)), np.int32)[:, :K].copy()
+    topk_cnt = np.empty(n_q, np.int32)
+    L = lib()
+
+    def run(a, b):
+        return L.orc_topk_batch(int(a), int(b), _ptr(q_idx), _ptr(q_seq), _ptr(q_pos), _ptr(k_idx),
+                                T, d, B, P, K, _ptr(blk_ids), _ptr(blk_cnt), _ptr(topk), _ptr(topk_cnt))
+
+    bad = _parallel(n_q, threads or default_threads(), run)
+    if bad:
+        raise ValueError(f"oracle token Top-K rejected {bad} queries")
+    return topk, topk_cnt
+
+
 # --------------------------------------------------------------------------
 # Steps 6-7: window + attention
 # --------------------------------------------------------------------------
@@ -217,6 +251,14 @@ def run_layers(wl, rows=None, threads=None):
         if mode in ("full", "reindex"):
             sel = select(wl.q_idx[layer][idx], q_seq, q_pos, wl.k_idx, cfg.block, cfg.pool,
                          cfg.top_k, threads)
+            res["index"][layer] = dict(zip(("blk_ids", "blk_cnt", "topk", "topk_cnt"), sel))
+            current = sel
+        elif mode == "reindex_tokens":
+            if current is None:
+                raise ValueError("a token-only Reindex layer needs an earlier Full/Reindex layer")
+            topk, cnt = topk_given_pool(wl.q_idx[layer][idx], q_seq, q_pos, wl.k_idx, cfg.block,
+                                        cfg.top_k, current[0], current[1], threads)
+            sel = (current[0], current[1], topk, cnt)
             res["index"][layer] = dict(zip(("blk_ids", "blk_cnt", "topk", "topk_cnt"), sel))
             current = sel
         if mode == "swa":

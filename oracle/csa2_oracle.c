@@ -121,6 +121,59 @@ static int by_id(const void *pa, const void *pb)
  * Top-K: if there are at most K candidates all are kept, otherwise the K best
  * by (token score desc, position asc).
  * Returns 0, or -1 on bad arguments. */
+/* Token Top-K of one query over a given pool (ascending block ids, n_pool
+ * of them): the candidates are the positions p <= t of the pooled blocks,
+ * scored <q_idx, k_idx[p]>; if there are more than K, the K best by (score
+ * desc, position asc) are kept ("Sparse attention": Top-512 main-KV entries;
+ * ties go to the lower position).  Output ascending, padded with -1. */
+int orc_topk_one(const int8_t *q_idx, const int8_t *k_seq, int T, int t, int d, int B,
+                 const int32_t *pool, int n_pool, int K, int32_t *topk, int32_t *topk_cnt)
+{
+    if (t < 0 || t >= T || d <= 0 || B <= 0 || K < 0 || n_pool < 0) return -1;
+    scored *cand = malloc(sizeof(scored) * (size_t)(n_pool > 0 ? n_pool : 1) * (size_t)B);
+    if (!cand) return -1;
+    int n_cand = 0;
+    for (int i = 0; i < n_pool; i++) {
+        if (pool[i] < 0 || pool[i] > t / B) { free(cand); return -1; }
+        for (int w = 0; w < B; w++) {
+            int p = pool[i] * B + w;
+            if (p > t) break;
+            cand[n_cand].score = dot_i8(q_idx, k_seq + (size_t)p * d, d);
+            cand[n_cand].id = p;
+            n_cand++;
+        }
+    }
+    int n_keep = n_cand;
+    if (n_cand > K) {
+        qsort(cand, (size_t)n_cand, sizeof(scored), by_score_then_id);
+        n_keep = K;
+    }
+    int32_t *sel = malloc(sizeof(int32_t) * (size_t)(n_keep > 0 ? n_keep : 1));
+    if (!sel) { free(cand); return -1; }
+    for (int i = 0; i < n_keep; i++) sel[i] = cand[i].id;
+    qsort(sel, (size_t)n_keep, sizeof(int32_t), by_id);
+    for (int i = 0; i < K; i++) topk[i] = (i < n_keep) ? sel[i] : -1;
+    *topk_cnt = n_keep;
+    free(sel); free(cand);
+    return 0;
+}
+
+/* Token Top-K over given pools (blk_ids rows of P entries, blk_cnt counts)
+ * for queries [q_begin, q_end): the Reindex variant that keeps the pool of
+ * the shared index set and reruns only the token selection. */
+int orc_topk_batch(int q_begin, int q_end, const int8_t *q_idx, const int32_t *q_seq,
+                   const int32_t *q_pos, const int8_t *k_idx, int T, int d, int B, int P, int K,
+                   const int32_t *blk_ids, const int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt)
+{
+    int bad = 0;
+    for (int i = q_begin; i < q_end; i++) {
+        const int s = q_seq[i];
+        bad += orc_topk_one(q_idx + (size_t)i * d, k_idx + (size_t)s * T * d, T, q_pos[i], d, B,
+                            blk_ids + (size_t)i * P, blk_cnt[i], K, topk + (size_t)i * K, topk_cnt + i) != 0;
+    }
+    return bad;
+}
+
 int orc_select_one(const int8_t *q_idx, const int8_t *k_seq, int T, int t,
                    int d, int B, int P, int K,
                    int32_t *blk_ids, int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt)
@@ -148,31 +201,9 @@ int orc_select_one(const int8_t *q_idx, const int8_t *k_seq, int T, int t,
     for (int i = 0; i < P; i++) blk_ids[i] = (i < n_pool) ? pool[i] : -1;
     *blk_cnt = n_pool;
 
-    /* candidate scores */
-    scored *cand = malloc(sizeof(scored) * (size_t)n_pool * (size_t)B);
-    int n_cand = 0;
-    for (int i = 0; i < n_pool; i++) {
-        for (int w = 0; w < B; w++) {
-            int p = pool[i] * B + w;
-            if (p > t) break;
-            cand[n_cand].score = dot_i8(q_idx, k_seq + (size_t)p * d, d);
-            cand[n_cand].id = p;
-            n_cand++;
-        }
-    }
-    int n_keep = n_cand;
-    if (n_cand > K) {
-        qsort(cand, (size_t)n_cand, sizeof(scored), by_score_then_id);
-        n_keep = K;
-    }
-    int32_t *sel = malloc(sizeof(int32_t) * (size_t)(n_keep > 0 ? n_keep : 1));
-    for (int i = 0; i < n_keep; i++) sel[i] = cand[i].id;
-    qsort(sel, (size_t)n_keep, sizeof(int32_t), by_id);
-    for (int i = 0; i < K; i++) topk[i] = (i < n_keep) ? sel[i] : -1;
-    *topk_cnt = n_keep;
-
-    free(sel); free(cand); free(pool); free(key); free(blocks);
-    return 0;
+    int bad = orc_topk_one(q_idx, k_seq, T, t, d, B, pool, n_pool, K, topk, topk_cnt);
+    free(pool); free(key); free(blocks);
+    return bad;
 }
 
 /* Queries [q_begin, q_end) of a batch.  q_idx [n_q][d]; k_idx [S][T][d];

@@ -127,6 +127,21 @@ def test_layer_group_checks_every_stage_before_launching(B):
     assert args(0, FAKE, 16) == 6            # workspace too small for the block pass
     assert args(9, FAKE, need) == 8          # unknown mode
     assert args(2, None, need) == 1          # reuse with no output
+    assert args(4, None, need) == 1          # token-only reindex with no output
+
+
+def test_token_only_reindex_needs_the_shared_pool(B):
+    """CSA2_REINDEX_TOKENS reads blk_ids/blk_cnt: without them it fails before
+    any launch."""
+    cfg = B.Cfg(pool=64)
+    P = ctypes.c_void_p
+    need = B.csa2_workspace_bytes(cfg, 4, 4096, 1)
+    call = lambda blk: B._lib.csa2_layer_group(
+        ctypes.byref(cfg.c()), 4, 1, 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 0, 1, 4096,
+        P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 4096 - 128, 128, P(blk), P(blk), P(FAKE), P(FAKE),
+        P(FAKE), None, P(FAKE), need, None)
+    assert call(None) == 1
+    assert B.MODES["reindex_tokens"] == 4
 
 
 def test_reuse_and_attend_argument_errors(B):

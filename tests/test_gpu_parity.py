@@ -170,6 +170,22 @@ def test_prefill_window_layer_chunks_and_mixed_tiles(lib):
     check(lib, cfg, seed=35)
 
 
+def test_token_only_reindex_decode(lib):
+    """A token-only Reindex group reads the Full group's pool and writes its
+    own Top-K; the Reuse layer after it takes those indices."""
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=3, ctx=9000, pool=256,
+                   layers=("full", "reuse", "reindex_tokens", "reuse"))
+    check(lib, cfg, seed=36)
+
+
+def test_token_only_reindex_prefill_whole_prefix_pools(lib):
+    """In prefill with every pool the whole prefix, the token-only Reindex runs
+    the MFMA tile Top-K with its own indexer query."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=1200, pool=256, top_k=128, window=64,
+                   layers=("full", "reindex_tokens", "swa"))
+    check(lib, cfg, seed=37)
+
+
 def test_no_window(lib):
     cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=4096, pool=64, top_k=128, window=0)
     check(lib, cfg, seed=27)

@@ -24,7 +24,7 @@ import pytest
 import torch
 
 import oracle
-from brute import block_key_exact, dot, select_brute
+from brute import block_key_exact, dot, select_brute, top_n_by_enumeration
 from top_kv_selection_amd import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "toy16.json")
@@ -120,6 +120,47 @@ def test_select_matches_enumeration_wide_value_range():
         pool, top = select_brute(q, k, t, B, P, K)
         assert list(blk[0, :bc[0]]) == pool
         assert list(tk[0, :tc[0]]) == top
+
+
+def test_token_topk_over_a_given_pool_matches_enumeration():
+    """The token step alone, over arbitrary pools (any ascending subset of the
+    eligible blocks, not only the hierarchical one)."""
+    rng = np.random.default_rng(14)
+    for B, T, d, P, K, k, q, t in _tiny_cases(5, 200):
+        n_elig = t // B + 1
+        n_pool = int(rng.integers(0, min(n_elig, P) + 1))
+        pool = np.sort(rng.choice(n_elig, n_pool, replace=False)).astype(np.int32)
+        blk = np.full((1, P), -1, np.int32)
+        blk[0, :n_pool] = pool
+        tk, tc = oracle.topk_given_pool(q[None], [0], [t], k[None], B, K, blk, [n_pool])
+        cands = [(dot(q, k[p]), p) for j in pool for p in range(j * B, j * B + B) if p <= t]
+        want = top_n_by_enumeration(cands, K) if cands else []
+        assert list(tk[0, :tc[0]]) == want
+        assert (tk[0, tc[0]:] == -1).all()
+
+
+def test_token_only_reindex_keeps_the_pool_and_reselects_tokens():
+    """A token-only Reindex layer shares the pool of the index set before it;
+    with the Full layer's own query it reproduces the Full indices, and with
+    its own query it takes the flat Top-K of the pool's candidates."""
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=3, ctx=2048, pool=32, top_k=40, window=16,
+                   layers=("full", "reuse", "reindex_tokens", "reuse"))
+    wl = W.generate(cfg, seed=15)
+    res = oracle.run_layers(wl)
+    full, tok = res["index"][0], res["index"][2]
+    assert (tok["blk_ids"] == full["blk_ids"]).all() and (tok["blk_cnt"] == full["blk_cnt"]).all()
+    for i in range(cfg.n_q):
+        t = wl.q_pos[i]
+        pool = full["blk_ids"][i, :full["blk_cnt"][i]]
+        pos = np.array([p for j in pool for p in range(j * 8, j * 8 + 8) if p <= t])
+        s = wl.k_idx[wl.q_seq[i], pos].astype(np.int64) @ wl.q_idx[2][i].astype(np.int64)
+        want = np.sort(pos[np.lexsort((pos, -s))[:cfg.top_k]])
+        assert (tok["topk"][i, :tok["topk_cnt"][i]] == want).all()
+    same = W.generate(cfg, seed=15)
+    same.q_idx[2] = same.q_idx[0].copy()
+    res2 = oracle.run_layers(same)
+    for key in ("topk", "topk_cnt"):
+        assert (res2["index"][2][key] == res2["index"][0][key]).all()
 
 
 def test_flat_case_is_lexsort_topk():

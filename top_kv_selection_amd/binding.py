@@ -18,8 +18,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
-FULL, REINDEX, REUSE, SWA = 0, 1, 2, 3
-MODES = {"full": FULL, "reindex": REINDEX, "reuse": REUSE, "swa": SWA}
+FULL, REINDEX, REUSE, SWA, REINDEX_TOKENS = 0, 1, 2, 3, 4
+MODES = {"full": FULL, "reindex": REINDEX, "reuse": REUSE, "swa": SWA, "reindex_tokens": REINDEX_TOKENS}
 F32, BF16 = 0, 1
 
 STATUS = {0: "CSA2_OK", 1: "CSA2_E_NULL", 2: "CSA2_E_SHAPE", 3: "CSA2_E_DTYPE",
@@ -217,9 +217,9 @@ def csa2_attend(cfg: Cfg, q, q_seq, q_pos, k_main, v_main, k_swa, v_swa, swa_fir
 def csa2_layer_group(cfg: Cfg, mode, q_idx, q_seq, q_pos, k_idx, k_blk, blk_update_begin, q, k_main,
                      v_main, k_swa, v_swa, swa_first, blk_ids, blk_cnt, topk, topk_cnt, out, lse=None,
                      ws=None):
-    """One CSA2 layer group: the first layer's mode (full/reindex/reuse/swa)
-    picks the selection work; all layers of q [L][n_q][H][D] attend with the
-    shared indices."""
+    """One CSA2 layer group: the first layer's mode (full/reindex/reuse/swa/
+    reindex_tokens) picks the selection work; all layers of q [L][n_q][H][D]
+    attend with the shared indices."""
     mode = MODES[mode] if isinstance(mode, str) else int(mode)
     _attend_checks(cfg, q, k_main, v_main, k_swa, v_swa, out, lse, q_seq, q_pos, topk, topk_cnt, ws)
     for t, n, d in ((q_idx, "q_idx", torch.int8), (k_idx, "k_idx", torch.int8), (k_blk, "k_blk", torch.int8),

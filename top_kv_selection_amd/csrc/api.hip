@@ -400,12 +400,13 @@ int32_t csa2_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int3
 {
     if (int32_t e = check_cfg(c)) return e;
     if (int32_t e = check_sizes(n_q, n_seq, T)) return e;
-    if (mode < CSA2_FULL || mode > CSA2_SWA) return CSA2_E_MODE;
+    if (mode < CSA2_FULL || mode > CSA2_REINDEX_TOKENS) return CSA2_E_MODE;
     if (n_layers < 1) return CSA2_E_SHAPE;
     if (mode != CSA2_SWA && c->top_k < 1) return CSA2_E_MODE;
     if (n_q == 0) return CSA2_OK;
     hipStream_t st = (hipStream_t)stream;
     const bool selects = mode == CSA2_FULL || mode == CSA2_REINDEX;
+    const bool tokens_only = mode == CSA2_REINDEX_TOKENS;
     const bool window_only = mode == CSA2_SWA;
     if (mode == CSA2_REUSE && (!topk || !topk_cnt)) return CSA2_E_NULL;
     if (selects) {
@@ -429,6 +430,11 @@ int32_t csa2_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int3
                                      blk_cnt, ws, ws_bytes, st, launch,
                                      mode == CSA2_FULL ? k_blk : nullptr))
                 return e;
+            if (int32_t e = do_topk(c, n_q, q_idx, q_seq, q_pos, k_idx, T, blk_ids, blk_cnt, topk,
+                                    topk_cnt, ws, ws_bytes, st, launch))
+                return e;
+        }
+        if (tokens_only) {   // the shared pool is read, only the token Top-K is fresh
             if (int32_t e = do_topk(c, n_q, q_idx, q_seq, q_pos, k_idx, T, blk_ids, blk_cnt, topk,
                                     topk_cnt, ws, ws_bytes, st, launch))
                 return e;

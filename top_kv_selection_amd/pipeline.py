@@ -35,8 +35,9 @@ class Group:
     v_swa: torch.Tensor
     out: torch.Tensor               # [L][n_q][H][D]
     lse: torch.Tensor               # [L][n_q][H]
-    q_idx: torch.Tensor = None      # [n_q][d] for full/reindex
+    q_idx: torch.Tensor = None      # [n_q][d] for full/reindex/reindex_tokens
     index_of: int = -1              # group whose indices a reuse group takes
+    pool_of: int = -1               # group whose pool a token-only Reindex group reads
 
 
 @dataclass
@@ -78,17 +79,23 @@ def upload(wl: Workload, device="cuda", q_idx=None, q=None) -> DeviceWorkload:
                     _real(np.stack([wl.v_swa[l] for l in layers]), cfg, device),
                     torch.empty((len(layers), cfg.n_q, cfg.n_heads, cfg.head_dim), dtype=tdt, device=device),
                     torch.empty((len(layers), cfg.n_q, cfg.n_heads), dtype=torch.float32, device=device))
-        if mode in ("full", "reindex"):
+        if mode in ("full", "reindex", "reindex_tokens"):
             grp.q_idx = _dev(q_idx[layers[0]], device)
             g = len(dw.groups)
-            dw.blk_ids[g] = torch.empty((cfg.n_q, cfg.pool), dtype=torch.int32, device=device)
-            dw.blk_cnt[g] = torch.empty(cfg.n_q, dtype=torch.int32, device=device)
+            if mode != "reindex_tokens":   # a token-only Reindex group reads the shared pool
+                dw.blk_ids[g] = torch.empty((cfg.n_q, cfg.pool), dtype=torch.int32, device=device)
+                dw.blk_cnt[g] = torch.empty(cfg.n_q, dtype=torch.int32, device=device)
             dw.topk[g] = torch.empty((cfg.n_q, cfg.top_k), dtype=torch.int32, device=device)
             dw.topk_cnt[g] = torch.empty(cfg.n_q, dtype=torch.int32, device=device)
         dw.groups.append(grp)
     last = -1
     for g, grp in enumerate(dw.groups):
-        if grp.mode in ("full", "reindex"):
+        if grp.mode == "reindex_tokens":
+            if last < 0:
+                raise ValueError("a token-only Reindex layer needs an earlier Full/Reindex layer")
+            # the pool of the most recent index set (a token-only group passes its own on)
+            grp.pool_of = last if dw.groups[last].mode != "reindex_tokens" else dw.groups[last].pool_of
+        if grp.mode in ("full", "reindex", "reindex_tokens"):
             last = g
         grp.index_of = last if grp.mode != "swa" else -1
     max_layers = max(len(g.layers) for g in dw.groups)
@@ -117,10 +124,11 @@ def run(dw: DeviceWorkload):
     for g, grp in enumerate(dw.groups):
         src = grp.index_of
         idx = src if src >= 0 else None
+        pool = grp.pool_of if grp.mode == "reindex_tokens" else idx
         B.csa2_layer_group(
             dw.lcfg, grp.mode, grp.q_idx, dw.q_seq, dw.q_pos, dw.k_idx, dw.k_blk, begin, grp.q,
             dw.k_main, dw.v_main, grp.k_swa, grp.v_swa, dw.cfg.swa_first,
-            dw.blk_ids.get(idx), dw.blk_cnt.get(idx), dw.topk.get(idx), dw.topk_cnt.get(idx),
+            dw.blk_ids.get(pool), dw.blk_cnt.get(pool), dw.topk.get(idx), dw.topk_cnt.get(idx),
             grp.out, grp.lse, dw.ws)
 
 
@@ -135,8 +143,9 @@ def outputs(dw: DeviceWorkload):
         for j, layer in enumerate(grp.layers):
             out[layer], lse[layer] = o[j], l[j]
         if g in dw.topk:
+            pg = grp.pool_of if grp.mode == "reindex_tokens" else g
             index[grp.layers[0]] = {
-                "blk_ids": dw.blk_ids[g].cpu().numpy(), "blk_cnt": dw.blk_cnt[g].cpu().numpy(),
+                "blk_ids": dw.blk_ids[pg].cpu().numpy(), "blk_cnt": dw.blk_cnt[pg].cpu().numpy(),
                 "topk": dw.topk[g].cpu().numpy(), "topk_cnt": dw.topk_cnt[g].cpu().numpy()}
     return {"out": out, "lse": lse, "index": index}
 
@@ -153,11 +162,12 @@ def replicate(dw: DeviceWorkload, q_idx=None, q=None) -> DeviceWorkload:
         ng = Group(grp.mode, list(grp.layers),
                    grp.q.clone() if q is None else _real(np.stack([q[l] for l in grp.layers]), cfg, dev),
                    grp.k_swa.clone(), grp.v_swa.clone(), torch.empty_like(grp.out), torch.empty_like(grp.lse),
-                   None, grp.index_of)
+                   None, grp.index_of, grp.pool_of)
         if grp.q_idx is not None:
             ng.q_idx = grp.q_idx.clone() if q_idx is None else _dev(q_idx[grp.layers[0]], dev)
-            new.blk_ids[g] = torch.empty_like(dw.blk_ids[g])
-            new.blk_cnt[g] = torch.empty_like(dw.blk_cnt[g])
+            if g in dw.blk_ids:
+                new.blk_ids[g] = torch.empty_like(dw.blk_ids[g])
+                new.blk_cnt[g] = torch.empty_like(dw.blk_cnt[g])
             new.topk[g] = torch.empty_like(dw.topk[g])
             new.topk_cnt[g] = torch.empty_like(dw.topk_cnt[g])
         new.groups.append(ng)
@@ -189,6 +199,8 @@ def algorithmic_bytes(cfg: Config) -> dict:
             else:
                 out["index_blocks"].append(n_q * (own * d + P * 4 + 4) + store)
             out["topk_tokens"].append(n_q * (d + pool * 4 + 4 + n_cand * d + K * 4 + 4))
+        elif mode == "reindex_tokens":
+            out["topk_tokens"].append(n_q * (d + pool * 4 + 4 + n_cand * d + K * 4 + 4))
         main = 0 if mode == "swa" else K * 4 + 4 + sel * 2 * D * esz
         out["attend"].append(n_q * (main + len(layers) * per_layer))
     return out
@@ -214,6 +226,7 @@ def algorithmic_ops(cfg: Config) -> dict:
     for mode, layers in cfg.groups():
         if mode in ("full", "reindex"):
             out["index_blocks"].append(int(block_ops.sum()))
+        if mode in ("full", "reindex", "reindex_tokens"):
             out["topk_tokens"].append(int((n_cand * d * 2).sum()))
         keys = win + (0 if mode == "swa" else sel)
         out["attend"].append(int(len(layers) * (keys * H * D * 4).sum()))

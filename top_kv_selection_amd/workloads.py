@@ -31,6 +31,7 @@ from typing import List, Optional
 import numpy as np
 
 FULL, REINDEX, REUSE, SWA_ONLY = "full", "reindex", "reuse", "swa"
+REINDEX_TOKENS = "reindex_tokens"   # own q_idx over the shared pool: token Top-K only
 
 
 @dataclasses.dataclass(frozen=True)
@@ -64,7 +65,7 @@ class Config:
 
     @property
     def index_layers(self) -> List[int]:
-        return [i for i, m in enumerate(self.layers) if m in (FULL, REINDEX)]
+        return [i for i, m in enumerate(self.layers) if m in (FULL, REINDEX, REINDEX_TOKENS)]
 
     @property
     def swa_first(self) -> int:
