@@ -57,6 +57,32 @@ __device__ __forceinline__ int4 block_key_part(const int8_t *rows, int n)
     return make_int4(out[0], out[1], out[2], out[3]);
 }
 
+// Dimension `lane` (one lane per dimension, lanes >= DIDX give 0) of the key
+// of a block whose first row is `rows`: the rounded mean of its n visible
+// rows.  One byte load per row and one division per lane, so a single wave
+// computes a whole key with little work (the per-thread block_key_part spends
+// 16 divisions per lane).
+template <int DIDX>
+__device__ __forceinline__ int block_key_dim(const int8_t *rows, int n, int lane)
+{
+    if (lane >= DIDX) return 0;
+    int v[kMaxBlock];
+#pragma unroll
+    for (int r = 0; r < kMaxBlock; r++) v[r] = (r < n) ? (int)rows[(size_t)r * DIDX + lane] : 0;
+    int sum = 0;
+#pragma unroll
+    for (int r = 0; r < kMaxBlock; r++) sum += v[r];
+    return round_mean_half_even(sum, n);
+}
+
+// Sum over the 64 lanes of a wave (every lane gets the total).
+__device__ __forceinline__ int wave_sum_i32(int v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
 __device__ __forceinline__ int dot16_i8(int4 a, int4 b)
 {
     int acc = dot4_i8(a.x, b.x, 0);
@@ -112,11 +138,13 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     const int jt = t / p.B, n_elig = jt + 1;
     int32_t *ids = p.blk_ids + (size_t)q * p.P;
 
-    // A Full layer stores the key of a block its query has just completed
-    // (the query's own block, when t is the block's last position).
+    // The query's own block (its last eligible one, jt) is scored from the
+    // rows visible to the query, by wave 0 of the workgroup whose range holds
+    // it, one lane per dimension.  A Full layer also stores the key of a block
+    // its query has just completed (t is the block's last position).
     const bool store_own = p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk;
-    int8_t *own_store = store_own ? p.k_blk_store + ((size_t)s * p.nblk + jt) * DIDX + part * 16 : nullptr;
-    const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX + part * 16;
+    int8_t *own_store = store_own ? p.k_blk_store + ((size_t)s * p.nblk + jt) * DIDX : nullptr;
+    const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX;
 
     if (p.tok_hist_clear != nullptr && g == 0)
         for (int b = tid; b < kRadixBins; b += NT) p.tok_hist_clear[(size_t)q * kRadixBins + b] = 0u;
@@ -124,8 +152,7 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     if (n_elig <= p.P) {   // the pool is every eligible block
         for (int j = g * NT + tid; j < p.P; j += p.G * NT) ids[j] = (j < n_elig) ? j : -1;
         if (g == 0 && tid == 0) p.blk_cnt[q] = n_elig;
-        if (store_own && g == 0 && tid < LPR)
-            *reinterpret_cast<int4 *>(own_store) = block_key_part<DIDX>(own_rows, p.B);
+        if (store_own && g == 0 && tid < DIDX) own_store[tid] = (int8_t)block_key_dim<DIDX>(own_rows, p.B, tid);
         return;
     }
     for (int b = tid; b < kHist2Words; b += NT) s_hist[b] = 0;
@@ -138,11 +165,9 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     uint32_t *ghist = p.ws_hist + (size_t)q * kRadixBins;
     const int8_t *blk_rows = p.k_blk + (size_t)s * p.nblk * DIDX + part * 16;
 
-    // the query's own block (computed from its visible rows) belongs to the
-    // workgroup whose range holds it; its rows are read in the first batch,
-    // after that batch's block-key loads have been issued
-    int4 own_key = make_int4(0, 0, 0, 0);
-    bool own_pending = jt >= lo && jt < hi;
+    // the own block's rows are read after the first batch's block-key loads
+    // have been issued
+    bool own_pending = jt >= lo && jt < hi && tid < 64;
     for (int base = lo; base < hi; base += RPP * kUnroll) {
         int4 kv[kUnroll];
 #pragma unroll
@@ -153,16 +178,22 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
         }
         if (own_pending) {
             own_pending = false;
-            own_key = block_key_part<DIDX>(own_rows, t - jt * p.B + 1);
-            if (store_own && (tid / LPR) == 0) *reinterpret_cast<int4 *>(own_store) = own_key;
+            const int kd = block_key_dim<DIDX>(own_rows, t - jt * p.B + 1, tid);
+            if (store_own && tid < DIDX) own_store[tid] = (int8_t)kd;
+            const int qd = (tid < DIDX) ? (int)p.q_idx[(size_t)q * DIDX + tid] : 0;
+            const uint32_t key = (uint32_t)(wave_sum_i32(kd * qd) + (int)kKeyBias);
+            if (tid == 0) {
+                if (SPLIT) gkeys[jt] = key;
+                else s_keys[lds_pad(jt)] = key;
+                atomicAdd(&s_hist[hist_pad(key >> kRadixBits)], 1u);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             const int j = base + u * RPP + tid / LPR;
-            if (j == jt) kv[u] = own_key;
             int acc = (j < hi) ? dot16_i8(kv[u], qv) : 0;
             acc = row_reduce<LPR>(acc);
-            if (j < hi && part == 0) {
+            if (j < hi && j < jt && part == 0) {
                 const uint32_t key = (uint32_t)(acc + (int)kKeyBias);
                 if (SPLIT) gkeys[j] = key;
                 else s_keys[lds_pad(j)] = key;
@@ -196,7 +227,6 @@ constexpr int kPoolAllBlocks = 2048;
 template <int DIDX>
 __global__ __launch_bounds__(kPoolAllThreads) void k_pool_all(IndexParams p)
 {
-    constexpr int LPR = DIDX / 16;
     const size_t stride = (size_t)gridDim.x * kPoolAllThreads;
     const size_t id = (size_t)blockIdx.x * kPoolAllThreads + threadIdx.x;
     const bool vec = (p.P % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.blk_ids) & 15) == 0);
@@ -217,15 +247,14 @@ __global__ __launch_bounds__(kPoolAllThreads) void k_pool_all(IndexParams p)
             p.blk_ids[k] = (j < p.q_pos[q] / p.B + 1) ? j : -1;
         }
     }
-    for (size_t k = id; k < (size_t)p.n_q * LPR; k += stride) {
-        const int q = (int)(k / LPR), part = (int)(k % LPR);
+    for (size_t k = id; k < (size_t)p.n_q * DIDX; k += stride) {
+        const int q = (int)(k / DIDX), d = (int)(k % DIDX);
         const int s = p.q_seq[q], t = p.q_pos[q];
         const int jt = t / p.B;
-        if (part == 0) p.blk_cnt[q] = jt + 1;
+        if (d == 0) p.blk_cnt[q] = jt + 1;
         if (p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk) {
-            const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX + part * 16;
-            *reinterpret_cast<int4 *>(p.k_blk_store + ((size_t)s * p.nblk + jt) * DIDX + part * 16) =
-                block_key_part<DIDX>(own_rows, p.B);
+            const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX;
+            p.k_blk_store[((size_t)s * p.nblk + jt) * DIDX + d] = (int8_t)block_key_dim<DIDX>(own_rows, p.B, d);
         }
     }
 }
