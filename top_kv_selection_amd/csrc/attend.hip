@@ -147,6 +147,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
     __shared__ int s_rows[kRowChunk];
     __shared__ __attribute__((aligned(16))) uint32_t s_hist[FUSED ? kHist2Words : 4];
     __shared__ int32_t s_pool[FUSED ? kFusedPoolLds : 4];
+    static_assert(!FUSED || kFusedPoolLds % (kWaves * 64) == 0, "whole pool loads per thread");
     __shared__ uint32_t s_sm[NT / 64 + 4];
 
     const int HG = p.H / 16;
@@ -171,9 +172,19 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         load_hist<NT>(p.sel_hist + (size_t)i * kRadixBins, hr);
         uint32_t k[IPT];
         load_keys_global<IPT>(p.sel_keys + (size_t)i * p.sel_stride, (int)p.sel_stride, k);
+        // every pool slot is read (slots past the count are never used), so
+        // these loads go out with the others instead of waiting for the count
+        constexpr int PPT = kFusedPoolLds / NT;
+        int32_t pv[PPT];
+#pragma unroll
+        for (int u = 0; u < PPT; u++) {
+            const int r = u * NT + (int)threadIdx.x;
+            pv[u] = (r < p.sel_P) ? p.sel_pool[(size_t)i * p.sel_P + r] : -1;
+        }
         const int n_pool = p.sel_pool_cnt[i];
         const int B = p.sel_B;
-        for (int r = threadIdx.x; r < n_pool; r += NT) s_pool[r] = p.sel_pool[(size_t)i * p.sel_P + r];
+#pragma unroll
+        for (int u = 0; u < PPT; u++) s_pool[u * NT + threadIdx.x] = pv[u];
         hist_to_lds<NT>(hr, s_hist);
         const int n_cand = n_pool * B;
         // The selection's size is known from the histogram (bin 0 holds the

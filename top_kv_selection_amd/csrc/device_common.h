@@ -365,22 +365,25 @@ __device__ __forceinline__ void store_hist(const HistRegs<NT> &h, uint32_t *ghis
     lds_barrier();
 }
 
-// Loads this thread's IPT keys of a global key row (16-byte aligned, `count`
-// valid entries) into registers, 0 past the end.
 // Issues the loads of this thread's IPT keys of a global key row that holds
-// `row_len` words (a multiple of 4, 16-byte aligned); entries past the row are
-// 0.  The count of valid keys is applied later by mask_keys, so the loads do
-// not wait for it.
+// `row_len` words (a multiple of 4, at least 4, 16-byte aligned); entries past
+// the row are 0.  The count of valid keys is applied later by mask_keys, so
+// the loads do not wait for it.  Every load is issued (from a slot clamped
+// into the row) and its value masked afterwards: a load under a divergent
+// branch can make the compiler wait for it before issuing the next.
 template <int IPT>
 __device__ __forceinline__ void load_keys_global(const uint32_t *g, int row_len, uint32_t (&k)[IPT])
 {
     const int lo = (int)threadIdx.x * IPT;
-    const uint4 *g4 = reinterpret_cast<const uint4 *>(g + lo);
 #pragma unroll
     for (int u = 0; u < IPT / 4; u++) {
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (lo + 4 * u < row_len) v = g4[u];
-        k[4 * u] = v.x; k[4 * u + 1] = v.y; k[4 * u + 2] = v.z; k[4 * u + 3] = v.w;
+        const int i = lo + 4 * u;
+        const uint4 v = *reinterpret_cast<const uint4 *>(g + min(i, row_len - 4));
+        const bool in = i < row_len;
+        k[4 * u] = in ? v.x : 0u;
+        k[4 * u + 1] = in ? v.y : 0u;
+        k[4 * u + 2] = in ? v.z : 0u;
+        k[4 * u + 3] = in ? v.w : 0u;
     }
 }
 template <int IPT>

@@ -340,40 +340,56 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
     const int n_pool = p.blk_cnt[q];
     const int n_cand = n_pool * B;                    // <= P*B <= kLdsKeys
     const int32_t *pool = p.blk_ids + (size_t)q * p.P;
+    // the histogram is cleared now; the barrier that orders the clearing
+    // before the first count comes after the first batch's loads are issued
     for (int b = tid; b < kHist2Words; b += NT) s_hist[b] = 0;
-    lds_barrier();
 
     const int4 qv = *reinterpret_cast<const int4 *>(p.q_idx + (size_t)q * DIDX + part * 16);
-    const int lo = SPLIT ? min(n_cand, g * p.chunk) : 0;
-    const int hi = SPLIT ? min(n_cand, lo + p.chunk) : n_cand;
     uint32_t *gkeys = p.ws_keys + (size_t)q * p.ws_stride;
     uint32_t *ghist = p.ws_hist + (size_t)q * kRadixBins;
-    const int8_t *seq_rows = p.k_idx + (size_t)s * p.T * DIDX + part * 16;
 
-    for (int base = lo; base < hi; base += RPP * kUnroll) {
-        int pos[kUnroll];
+    // A split launch walks its whole chunk of pool slots (every slot below P
+    // exists, slots past the count are ignored), so the pool entries are
+    // loaded together with the count instead of after it.  Loads are
+    // unconditional, from clamped slots and rows (row 0 of the sequence for
+    // a slot that is not a visible candidate), and masked afterwards: a load
+    // under a divergent branch would be waited for before the next is issued.
+    const int lo_w = SPLIT ? g * p.chunk : 0;
+    const int hi_w = SPLIT ? min(p.P * B, lo_w + p.chunk) : n_cand;
+    for (int base = lo_w; base < hi_w; base += RPP * kUnroll) {
+        int cl[kUnroll], blk[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            const int c = base + u * RPP + tid / LPR;
-            pos[u] = INT32_MAX;
-            if (c < hi) {
-                const int r = c / B;
-                pos[u] = pool[r] * B + (c - r * B);
-            }
+            cl[u] = min(base + u * RPP + tid / LPR, hi_w - 1);
+            blk[u] = pool[cl[u] / B];
         }
+        // the query's sequence and count are first used here, so the wait for
+        // them stays behind the pool loads (the empty asm keeps the compiler
+        // from hoisting their uses out of the loop)
+        __builtin_amdgcn_sched_barrier(0);
+        int np = n_pool, sq = s;
+        asm volatile("" : "+s"(np), "+s"(sq));
+        const int hi = SPLIT ? min(np * B, lo_w + p.chunk) : n_cand;
+        const int8_t *seq_rows = p.k_idx + (size_t)sq * p.T * DIDX + part * 16;
+        int pos[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) pos[u] = blk[u] * B + (cl[u] % B);
+        bool vis[kUnroll];
         int4 kv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            kv[u] = make_int4(0, 0, 0, 0);
-            if (pos[u] <= t) kv[u] = *reinterpret_cast<const int4 *>(seq_rows + (size_t)pos[u] * DIDX);
+            const int c = base + u * RPP + tid / LPR;
+            vis[u] = c < hi && pos[u] <= t;
+            kv[u] = *reinterpret_cast<const int4 *>(seq_rows + (size_t)(vis[u] ? pos[u] : 0) * DIDX);
         }
+        if (base == lo_w) lds_barrier();
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             const int c = base + u * RPP + tid / LPR;
             int acc = dot16_i8(kv[u], qv);
             acc = row_reduce<LPR>(acc);
             if (c < hi && part == 0) {
-                const uint32_t key = (pos[u] <= t) ? (uint32_t)(acc + (int)kKeyBias) : 0u;
+                const uint32_t key = vis[u] ? (uint32_t)(acc + (int)kKeyBias) : 0u;
                 if (SPLIT) gkeys[c] = key;
                 else s_keys[lds_pad(c)] = key;
                 atomicAdd(&s_hist[hist_pad(key >> kRadixBits)], 1u);
