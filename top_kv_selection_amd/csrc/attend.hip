@@ -124,6 +124,11 @@ constexpr int kWaves = 8;                      // waves per workgroup, 32 keys e
 constexpr int kStepKeys = kWaves * 32;         // keys per workgroup step
 constexpr int kRowChunk = kAttendRowChunk;     // row codes staged in LDS at once
 constexpr int kVtStride = 40;                  // bf16 per V^T row in LDS (32 keys + pad)
+// After the key loop a wave's V^T buffer holds its partial output, 16 heads x
+// kObStride floats: with 144 floats per head, the 16-byte writes of a wave
+// (lane -> head r16, dims 16m + 4g) cover every bank equally.
+constexpr int kObStride = 144;
+static_assert(16 * kObStride * 4 <= 128 * kVtStride * 2, "a wave's partial output fits its V^T buffer");
 constexpr int kHeadRec = 4 + 128;              // split record per head: max, sum, 2 pad, acc[128]
 constexpr int kPartFloats = 16 * kHeadRec;     // one split record (16 heads), 16-byte aligned
 constexpr int kMergeBatch = 8;                 // split records loaded at once by the merge
@@ -380,12 +385,13 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         }
     }
 
-    // ---- merge the waves (the V^T buffer is free now)
-    float *ob = reinterpret_cast<float *>(&s_vt[0][0]);   // [kWaves][16][128]
+    // ---- merge the waves (every wave has finished with its V^T buffer: the
+    // key loop ends with a workgroup barrier)
+    float *ob = reinterpret_cast<float *>(&s_vt[w][0]);   // this wave's [16][kObStride]
 #pragma unroll
     for (int m = 0; m < 8; m++)
-#pragma unroll
-        for (int ii = 0; ii < 4; ii++) ob[(w * 16 + r16) * 128 + 16 * m + 4 * g + ii] = acc[m][ii];
+        *reinterpret_cast<float4 *>(ob + r16 * kObStride + 16 * m + 4 * g) =
+            make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
     if (g == 0) {
         s_ml[w][r16][0] = m_run;
         s_ml[w][r16][1] = l_run;
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
     for (int ww = 0; ww < kWaves; ww++) {
         const float f = exp2f(s_ml[ww][hh][0] - Mu);
         L += f * s_ml[ww][hh][1];
-        const float4 v = *reinterpret_cast<const float4 *>(ob + (ww * 16 + hh) * 128 + d0);
+        const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(&s_vt[ww][0]) + hh * kObStride + d0);
         o[0] += f * v.x; o[1] += f * v.y; o[2] += f * v.z; o[3] += f * v.w;
     }
     const size_t row_id = ((size_t)l * p.n_q + i) * p.H + hg * 16 + hh;
