@@ -123,6 +123,7 @@ __global__ __launch_bounds__(256) void k_attend_generic(AttendParams p)
 constexpr int kWaves = 8;                      // waves per workgroup, 32 keys each per step
 constexpr int kStepKeys = kWaves * 32;         // keys per workgroup step
 constexpr int kRowChunk = kAttendRowChunk;     // row codes staged in LDS at once
+static_assert(kRowChunk % (kWaves * 64) == 0 && kRowChunk % kStepKeys == 0, "whole staging rounds and steps");
 constexpr int kVtStride = 40;                  // bf16 per V^T row in LDS (32 keys + pad)
 // After the key loop a wave's V^T buffer holds its partial output, 16 heads x
 // kObStride floats: with 144 floats per head, the 16-byte writes of a wave
@@ -241,11 +242,24 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
     const int32_t *tk = p.topk ? p.topk + (size_t)i * p.K : nullptr;
 
     // Row code of key kk: main row r -> r, window row r -> -(r + 1).  Slots
-    // past the last key repeat the last key (read, then masked).
+    // past the last key repeat the last key (read, then masked).  Only the
+    // slots the chunk's steps read are staged, and every Top-K id load is
+    // issued (from a clamped entry) before any is used, so the loads overlap
+    // instead of each waiting under its own branch.
     auto stage_rows = [&](int kc) {
-        for (int x = threadIdx.x; x < kRowChunk; x += kWaves * 64) {
+        constexpr int SPT = kRowChunk / (kWaves * 64);
+        const int n_stage = min(kRowChunk, (k_end - kc + kStepKeys - 1) / kStepKeys * kStepKeys);
+        int id[SPT];
+#pragma unroll
+        for (int u = 0; u < SPT; u++) {
+            const int kk = min(kc + u * kWaves * 64 + (int)threadIdx.x, k_end - 1);
+            id[u] = (tk && p.K > 0) ? tk[min(kk, p.K - 1)] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < SPT; u++) {
+            const int x = u * kWaves * 64 + (int)threadIdx.x;
             const int kk = min(kc + x, k_end - 1);
-            s_rows[x] = (kk < cnt) ? tk[kk] : -(win.w0 + (kk - cnt) - p.swa_first) - 1;
+            if (x < n_stage) s_rows[x] = (kk < cnt) ? id[u] : -(win.w0 + (kk - cnt) - p.swa_first) - 1;
         }
         lds_barrier();
     };
