@@ -60,9 +60,9 @@ def lib():
         L.orc_block_key.restype = None
         L.orc_block_key.argtypes = [P, i32, i32, i32, i32, P]
         L.orc_select_one.restype = i32
-        L.orc_select_one.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, P, P]
+        L.orc_select_one.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P]
         L.orc_select_batch.restype = i32
-        L.orc_select_batch.argtypes = [i32, i32, P, P, P, P, i32, i32, i32, i32, i32, i32,
+        L.orc_select_batch.argtypes = [i32, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
                                        P, P, P, P]
         L.orc_topk_batch.restype = i32
         L.orc_topk_batch.argtypes = [i32, i32, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]
@@ -134,9 +134,13 @@ def block_key(k_seq: np.ndarray, B: int, j: int, t: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Steps 2-5: block pool and token Top-K
 # --------------------------------------------------------------------------
-def select(q_idx, q_seq, q_pos, k_idx, B, P, K, threads=None):
+TAIL_VISIBLE, TAIL_EXCLUDE, TAIL_WHOLE = 0, 1, 2
+
+
+def select(q_idx, q_seq, q_pos, k_idx, B, P, K, threads=None, tail=TAIL_VISIBLE):
     """Per query: pooled blocks and Top-K positions (ascending, -1 padded).
-    q_idx int8 [n_q][d]; k_idx int8 [S][T][d].
+    q_idx int8 [n_q][d]; k_idx int8 [S][T][d].  ``tail`` picks the reading of
+    the query's partial own block (visible rows / excluded / whole block).
     Returns (blk_ids [n_q][P], blk_cnt [n_q], topk [n_q][K], topk_cnt [n_q])."""
     q_idx = np.ascontiguousarray(q_idx, dtype=np.int8)
     k_idx = np.ascontiguousarray(k_idx, dtype=np.int8)
@@ -153,7 +157,7 @@ def select(q_idx, q_seq, q_pos, k_idx, B, P, K, threads=None):
 
     def run(a, b):
         return L.orc_select_batch(int(a), int(b), _ptr(q_idx), _ptr(q_seq), _ptr(q_pos),
-                                  _ptr(k_idx), S, T, d, B, P, K, _ptr(blk_ids), _ptr(blk_cnt),
+                                  _ptr(k_idx), S, T, d, B, P, K, int(tail), _ptr(blk_ids), _ptr(blk_cnt),
                                   _ptr(topk), _ptr(topk_cnt))
 
     bad = _parallel(n_q, threads or default_threads(), run)
@@ -250,7 +254,7 @@ def run_layers(wl, rows=None, threads=None):
     for layer, mode in enumerate(cfg.layers):
         if mode in ("full", "reindex"):
             sel = select(wl.q_idx[layer][idx], q_seq, q_pos, wl.k_idx, cfg.block, cfg.pool,
-                         cfg.top_k, threads)
+                         cfg.top_k, threads, cfg.tail)
             res["index"][layer] = dict(zip(("blk_ids", "blk_cnt", "topk", "topk_cnt"), sel))
             current = sel
         elif mode == "reindex_tokens":

@@ -67,6 +67,7 @@ int64_t orc_round_half_even_div(int64_t sum, int64_t n)
  * mean of the block's rows that are visible to the query (positions
  * j*B .. min(j*B+B-1, t)).  A block that is not yet full (only the query's own
  * block can be) therefore averages only the tokens that exist at time t.
+ * (The whole-block tail reading passes t = T-1 here.)
  * k_seq is one sequence's indexer keys, row-major [T][d]. */
 void orc_block_key(const int8_t *k_seq, int d, int B, int j, int t, int8_t *key)
 {
@@ -174,19 +175,36 @@ int orc_topk_batch(int q_begin, int q_end, const int8_t *q_idx, const int32_t *q
     return bad;
 }
 
+/* The query's own block is partial when t is not its last position.  The
+ * pages do not say how such a block enters the block pass; three readings:
+ *   ORC_TAIL_VISIBLE (the library's default): it is eligible and its key is
+ *       the rounded mean of its rows at positions <= t;
+ *   ORC_TAIL_EXCLUDE: it is not eligible (its tokens are still in the sliding
+ *       window, whose length is at least B);
+ *   ORC_TAIL_WHOLE: it is eligible and its key averages all of its rows that
+ *       exist in k_seq (positions < T), including positions after t.
+ * Complete blocks are the same under every reading, and in every reading a
+ * candidate token is a position <= t. */
+enum { ORC_TAIL_VISIBLE = 0, ORC_TAIL_EXCLUDE = 1, ORC_TAIL_WHOLE = 2 };
+
 int orc_select_one(const int8_t *q_idx, const int8_t *k_seq, int T, int t,
-                   int d, int B, int P, int K,
+                   int d, int B, int P, int K, int tail,
                    int32_t *blk_ids, int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt)
 {
     if (t < 0 || t >= T || d <= 0 || B <= 0 || P <= 0 || K < 0) return -1;
-    int n_elig = t / B + 1;                  /* blocks j with j*B <= t */
+    if (tail < ORC_TAIL_VISIBLE || tail > ORC_TAIL_WHOLE) return -1;
+    /* eligible blocks: those with a visible token (j*B <= t), or only the
+     * complete ones ((j+1)*B <= t+1) when the partial block is excluded */
+    int n_elig = (tail == ORC_TAIL_EXCLUDE) ? (t + 1) / B : t / B + 1;
+    /* last row a block key may average: t, or the last row of the cache */
+    int key_limit = (tail == ORC_TAIL_WHOLE) ? T - 1 : t;
 
     /* block scores */
-    scored *blocks = malloc(sizeof(scored) * (size_t)n_elig);
+    scored *blocks = malloc(sizeof(scored) * (size_t)(n_elig > 0 ? n_elig : 1));
     int8_t *key = malloc((size_t)d);
     if (!blocks || !key) { free(blocks); free(key); return -1; }
     for (int j = 0; j < n_elig; j++) {
-        orc_block_key(k_seq, d, B, j, t, key);
+        orc_block_key(k_seq, d, B, j, key_limit, key);
         blocks[j].score = dot_i8(q_idx, key, d);
         blocks[j].id = j;
     }
@@ -195,7 +213,8 @@ int orc_select_one(const int8_t *q_idx, const int8_t *k_seq, int T, int t,
         qsort(blocks, (size_t)n_elig, sizeof(scored), by_score_then_id);
         n_pool = P;
     }
-    int32_t *pool = malloc(sizeof(int32_t) * (size_t)n_pool);
+    int32_t *pool = malloc(sizeof(int32_t) * (size_t)(n_pool > 0 ? n_pool : 1));
+    if (!pool) { free(key); free(blocks); return -1; }
     for (int i = 0; i < n_pool; i++) pool[i] = blocks[i].id;
     qsort(pool, (size_t)n_pool, sizeof(int32_t), by_id);
     for (int i = 0; i < P; i++) blk_ids[i] = (i < n_pool) ? pool[i] : -1;
@@ -210,7 +229,7 @@ int orc_select_one(const int8_t *q_idx, const int8_t *k_seq, int T, int t,
  * blk_ids [n_q][P]; topk [n_q][K].  Returns the number of failed queries. */
 int orc_select_batch(int q_begin, int q_end, const int8_t *q_idx,
                      const int32_t *q_seq, const int32_t *q_pos,
-                     const int8_t *k_idx, int S, int T, int d, int B, int P, int K,
+                     const int8_t *k_idx, int S, int T, int d, int B, int P, int K, int tail,
                      int32_t *blk_ids, int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt)
 {
     int bad = 0;
@@ -218,7 +237,7 @@ int orc_select_batch(int q_begin, int q_end, const int8_t *q_idx,
         int s = q_seq[i];
         if (s < 0 || s >= S) { bad++; continue; }
         bad += orc_select_one(q_idx + (size_t)i * d, k_idx + (size_t)s * T * d, T, q_pos[i],
-                              d, B, P, K, blk_ids + (size_t)i * P, blk_cnt + i,
+                              d, B, P, K, tail, blk_ids + (size_t)i * P, blk_cnt + i,
                               topk + (size_t)i * K, topk_cnt + i) != 0;
     }
     return bad;

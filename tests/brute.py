@@ -42,10 +42,14 @@ def top_n_by_enumeration(items, n):
     return found[0]
 
 
-def select_brute(q_idx, k_seq, t, B, P, K):
-    """Pool and Top-K for one query by enumeration (tiny inputs only)."""
-    n_elig = t // B + 1
-    blocks = [(dot(q_idx, block_key_exact(k_seq, B, j, t)), j) for j in range(n_elig)]
+def select_brute(q_idx, k_seq, t, B, P, K, tail=0):
+    """Pool and Top-K for one query by enumeration (tiny inputs only).
+    ``tail`` is the reading of a partial own block: 0 keyed by its visible
+    rows, 1 not eligible, 2 keyed by all of its rows in k_seq (future ones
+    too).  Candidates are always positions <= t."""
+    n_elig = (t + 1) // B if tail == 1 else t // B + 1
+    last_row = len(k_seq) - 1 if tail == 2 else t
+    blocks = [(dot(q_idx, block_key_exact(k_seq, B, j, last_row)), j) for j in range(n_elig)]
     pool = top_n_by_enumeration(blocks, P)
     cands = [(dot(q_idx, k_seq[p]), p) for j in pool for p in range(j * B, j * B + B) if p <= t]
     return pool, top_n_by_enumeration(cands, K)

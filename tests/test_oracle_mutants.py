@@ -23,7 +23,10 @@ MUTANTS = {
     "partial block reads future rows": ("if (last > t) last = t;", ""),
     "tie goes to the higher id": ("return (a->id < b->id) ? -1 : (a->id > b->id);",
                                   "return (a->id > b->id) ? -1 : (a->id < b->id);"),
-    "own block not eligible": ("int n_elig = t / B + 1;", "int n_elig = (t + 1) / B;"),
+    "own block not eligible": ("? (t + 1) / B : t / B + 1;", "? (t + 1) / B : (t + 1) / B;"),
+    "excluded tail block kept": ("? (t + 1) / B : t / B + 1;", "? t / B + 1 : t / B + 1;"),
+    "whole-block tail reads visible rows only": ("int key_limit = (tail == ORC_TAIL_WHOLE) ? T - 1 : t;",
+                                                 "int key_limit = t;"),
     "query's own position excluded": ("if (p > t) break;", "if (p >= t) break;"),
     "score sign flipped": ("s += (int64_t)a[c] * (int64_t)b[c];", "s -= (int64_t)a[c] * (int64_t)b[c];"),
     "pool one short": ("n_pool = P;", "n_pool = P - 1;"),

@@ -122,6 +122,76 @@ def test_select_matches_enumeration_wide_value_range():
         assert list(tk[0, :tc[0]]) == top
 
 
+@pytest.mark.parametrize("tail", [oracle.TAIL_EXCLUDE, oracle.TAIL_WHOLE])
+def test_tail_block_readings_match_enumeration(tail):
+    """The two other readings of a partial own block (not eligible; keyed by
+    the whole block including rows after t) against enumeration."""
+    for B, T, d, P, K, k, q, t in _tiny_cases(11 + tail, 250):
+        blk, bc, tk, tc = oracle.select(q[None], [0], [t], k[None], B, P, K, tail=tail)
+        pool, top = select_brute(q, k, t, B, P, K, tail)
+        assert list(blk[0, :bc[0]]) == pool, (B, T, t)
+        assert (blk[0, bc[0]:] == -1).all()
+        assert list(tk[0, :tc[0]]) == top, (B, T, t)
+        assert (tk[0, tc[0]:] == -1).all()
+
+
+def test_tail_readings_agree_when_the_own_block_is_complete():
+    rng = np.random.default_rng(17)
+    for _ in range(200):
+        B = int(rng.choice([2, 4, 8]))
+        T = B * int(rng.integers(1, 6))
+        k = rng.integers(-4, 5, size=(T, 3), dtype=np.int8)
+        q = rng.integers(-4, 5, size=3, dtype=np.int8)
+        t = B * int(rng.integers(1, T // B + 1)) - 1          # last position of a block
+        P, K = int(rng.integers(1, 4)), int(rng.integers(1, 6))
+        base = oracle.select(q[None], [0], [t], k[None], B, P, K)
+        for tail in (oracle.TAIL_EXCLUDE, oracle.TAIL_WHOLE):
+            got = oracle.select(q[None], [0], [t], k[None], B, P, K, tail=tail)
+            for a, b in zip(base, got):
+                assert (a == b).all(), (B, T, t, tail)
+
+
+def test_excluding_the_partial_block_is_selecting_at_its_last_complete_position():
+    """Without the partial own block the eligible blocks, their keys and the
+    candidates are those of a query at the last position of the previous
+    block (same indexer query)."""
+    rng = np.random.default_rng(18)
+    for _ in range(300):
+        B = int(rng.choice([2, 4, 8]))
+        T = int(rng.integers(B + 1, 6 * B))
+        k = rng.integers(-3, 4, size=(T, 2), dtype=np.int8)
+        q = rng.integers(-3, 4, size=2, dtype=np.int8)
+        t = int(rng.integers(B, T))
+        if (t + 1) % B == 0:
+            continue
+        t_prev = (t + 1) // B * B - 1
+        P, K = int(rng.integers(1, 4)), int(rng.integers(1, 6))
+        got = oracle.select(q[None], [0], [t], k[None], B, P, K, tail=oracle.TAIL_EXCLUDE)
+        want = oracle.select(q[None], [0], [t_prev], k[None], B, P, K)
+        for a, b in zip(got, want):
+            assert (a == b).all(), (B, T, t)
+
+
+def test_block_size_one_with_pool_k_is_the_flat_topk():
+    """Blocks of one token with a pool of K blocks select the K best tokens
+    of the whole prefix directly (the flat Top-K variant): numpy.lexsort on
+    (position, -score) over every visible token."""
+    rng = np.random.default_rng(19)
+    for _ in range(30):
+        T = int(rng.integers(40, 3000))
+        d = int(rng.choice([8, 32]))
+        K = int(rng.integers(1, 64))
+        k = rng.integers(-4, 5, size=(T, d), dtype=np.int8)   # narrow range: many ties
+        q = rng.integers(-4, 5, size=d, dtype=np.int8)
+        t = int(rng.integers(0, T))
+        blk, bc, tk, tc = oracle.select(q[None], [0], [t], k[None], 1, K, K)
+        scores = k[: t + 1].astype(np.int64) @ q.astype(np.int64)
+        order = np.lexsort((np.arange(t + 1), -scores))
+        want = np.sort(order[:K])
+        assert list(tk[0, :tc[0]]) == list(want)
+        assert list(blk[0, :bc[0]]) == list(want)
+
+
 def test_token_topk_over_a_given_pool_matches_enumeration():
     """The token step alone, over arbitrary pools (any ascending subset of the
     eligible blocks, not only the hierarchical one)."""

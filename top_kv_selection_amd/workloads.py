@@ -32,6 +32,9 @@ import numpy as np
 
 FULL, REINDEX, REUSE, SWA_ONLY = "full", "reindex", "reuse", "swa"
 REINDEX_TOKENS = "reindex_tokens"   # own q_idx over the shared pool: token Top-K only
+# Readings of a query's partial own block in the block pass: keyed by its
+# visible rows (default), not eligible, or keyed by all of its rows.
+TAIL_VISIBLE, TAIL_EXCLUDE, TAIL_WHOLE = 0, 1, 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -50,6 +53,7 @@ class Config:
     top_k: int               # K
     window: int              # W
     layers: tuple            # per-layer mode, model order
+    tail: int = TAIL_VISIBLE  # reading of a partial own block (see TAIL_*)
 
     @property
     def seed(self) -> int:
