@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 typedef enum {
     CSA2_OK = 0,
@@ -81,6 +81,20 @@ typedef enum {
 
 typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
 
+/* How the block pass treats a query's own block when it is partial (t is not
+ * its last position).  The pages say nothing about it; three readings:
+ *   CSA2_TAIL_VISIBLE: eligible, keyed by the rounded mean of its rows at
+ *                      positions <= t (the default);
+ *   CSA2_TAIL_EXCLUDE: not eligible (its tokens are in the sliding window
+ *                      whenever W >= B); a query at t < B-1 then has no
+ *                      eligible block and selects nothing;
+ *   CSA2_TAIL_WHOLE:   eligible, keyed by the rounded mean of all of its rows
+ *                      that exist in k_idx (positions < T), i.e. including
+ *                      positions after t (only prefill has any).
+ * Complete blocks are the same under every reading, and the token Top-K
+ * takes positions <= t only. */
+typedef enum { CSA2_TAIL_VISIBLE = 0, CSA2_TAIL_EXCLUDE = 1, CSA2_TAIL_WHOLE = 2 } csa2_tail;
+
 /* Selection and attention sizes (one struct shared by every call). */
 typedef struct {
     int32_t block;     /* B: tokens per block; 1..16                              */
@@ -92,9 +106,13 @@ typedef struct {
     int32_t head_dim;  /* D: 64 or 128                                            */
     int32_t dtype;     /* csa2_dtype of Q, K, V and the output                    */
     float scale;       /* logit scale; 0 means 1/sqrt(head_dim)                  */
+    int32_t tail;      /* csa2_tail reading of a partial own block                */
 } csa2_cfg;
 /* Limits: P*B <= 16384 candidates per query (the pages' cap on candidates
- * scored by an indexer); T <= 2^24 positions. */
+ * scored by an indexer); T <= 2^24 positions.
+ * Flat Top-K (no block hierarchy): block = 1 and pool = top_k select the K
+ * best tokens of the whole prefix directly; the block keys of blocks of one
+ * token are the k_idx rows themselves (csa2_build_block_keys copies them). */
 
 int32_t csa2_abi_version(void);
 const char *csa2_status_str(int32_t status);

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(B):
 
 
 def test_abi_version_and_status_strings(B):
-    assert B.csa2_abi_version() == 1
+    assert B.csa2_abi_version() == B.ABI_VERSION == 2
     for s in range(9):
         assert B._lib.csa2_status_str(s).decode()
     assert B._lib.csa2_status_str(99).decode() == "unknown status"
@@ -67,7 +67,7 @@ def test_workspace_bytes_follow_the_work_split(B):
 @pytest.mark.parametrize("field,value,status", [
     ("d_idx", 48, 4), ("head_dim", 96, 4), ("block", 0, 2), ("block", 17, 2), ("pool", 0, 2),
     ("top_k", -1, 2), ("window", 2000, 2), ("dtype", 7, 3), ("n_heads", 0, 2),
-    ("scale", float("nan"), 2), ("scale", -1.0, 2),
+    ("scale", float("nan"), 2), ("scale", -1.0, 2), ("tail", 3, 2), ("tail", -1, 2),
 ])
 def test_bad_config_is_rejected(B, field, value, status):
     c = dataclasses.asdict(B.Cfg())

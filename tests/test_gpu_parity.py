@@ -127,6 +127,49 @@ def test_prefill_row_kernel_two_head_groups(lib):
     check(lib, cfg, seed=30)
 
 
+# ------------------------------------------------------------------ selection variants
+@pytest.mark.parametrize("tail", [W.TAIL_EXCLUDE, W.TAIL_WHOLE])
+def test_tail_reading_prefill_block_pass(lib, tail):
+    """Every position of a prompt under the other two readings of a partial
+    own block: block pass with one workgroup per query (pool smaller than the
+    eligible blocks), per-query token Top-K; with the tail excluded the first
+    B-1 queries select nothing and attend to their window alone."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=700, pool=64, top_k=96, window=40,
+                   layers=("full", "reuse"), tail=tail)
+    check(lib, cfg, seed=40 + tail)
+
+
+@pytest.mark.parametrize("tail", [W.TAIL_EXCLUDE, W.TAIL_WHOLE])
+def test_tail_reading_prefill_whole_prefix_pools(lib, tail):
+    """Pools that hold every eligible block: the pool-all kernel and the dense
+    (MFMA tile) token Top-K under the other two tail readings."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=1200, pool=2048, top_k=96, window=16, layers=("full",),
+                   tail=tail)
+    check(lib, cfg, seed=42 + tail)
+
+
+def test_tail_excluded_decode_split_pass_and_layer_group(lib):
+    """Decode with a partial own block excluded: block pass split over many
+    workgroups per query, fused layer group with two Reuse layers."""
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=4, ctx=20003, pool=256, top_k=300, window=64,
+                   layers=("full", "reuse", "reuse"), tail=W.TAIL_EXCLUDE)
+    check(lib, cfg, seed=44)
+
+
+def test_flat_topk_blocks_of_one_token_decode(lib):
+    """Flat Top-K: blocks of one token and a pool of K blocks select the K
+    best tokens of a 40,000-token prefix (more blocks than one workgroup holds
+    in registers)."""
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=40000, block=1, pool=512, top_k=512)
+    check(lib, cfg, seed=45)
+
+
+def test_flat_topk_blocks_of_one_token_prefill(lib):
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=600, block=1, pool=64, top_k=64, window=32,
+                   layers=("full", "reuse"))
+    check(lib, cfg, seed=46)
+
+
 def test_prefill_dense_topk_two_sequences(lib):
     """Pool covering every block: the MFMA tile Top-K, with a workgroup tile
     that holds queries of both sequences (1,000 is not a multiple of 16)."""

@@ -33,6 +33,8 @@ int32_t check_cfg(const csa2_cfg *c)
     if (c->d_idx != 32 && c->d_idx != 64) return CSA2_E_UNSUPPORTED;
     if (c->head_dim != 64 && c->head_dim != 128) return CSA2_E_UNSUPPORTED;
     if (!(c->scale >= 0.f) || !isfinite(c->scale)) return CSA2_E_SHAPE;
+    if (c->tail != CSA2_TAIL_VISIBLE && c->tail != CSA2_TAIL_EXCLUDE && c->tail != CSA2_TAIL_WHOLE)
+        return CSA2_E_SHAPE;
     return CSA2_OK;
 }
 
@@ -87,7 +89,7 @@ int32_t do_index(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int3
     IndexParams p{};
     p.q_idx = q_idx; p.q_seq = q_seq; p.q_pos = q_pos; p.k_idx = k_idx; p.k_blk = k_blk;
     p.k_blk_store = k_blk_store;
-    p.T = T; p.B = c->block; p.P = c->pool; p.n_q = n_q; p.G = pl.G; p.chunk = pl.chunk;
+    p.T = T; p.B = c->block; p.P = c->pool; p.n_q = n_q; p.G = pl.G; p.chunk = pl.chunk; p.tail = c->tail;
     p.nblk = T / c->block;
     p.ws_keys = (uint32_t *)r.data;
     p.ws_stride = ((long long)(T - 1) / c->block + 1 + 3) / 4 * 4;   // rows 16-byte aligned
@@ -114,7 +116,7 @@ int32_t do_topk(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32
     TopkParams p{};
     p.q_idx = q_idx; p.q_seq = q_seq; p.q_pos = q_pos; p.k_idx = k_idx;
     p.blk_ids = blk_ids; p.blk_cnt = blk_cnt;
-    p.T = T; p.B = c->block; p.P = c->pool; p.K = c->top_k; p.n_q = n_q; p.G = pl.G;
+    p.T = T; p.B = c->block; p.P = c->pool; p.K = c->top_k; p.n_q = n_q; p.G = pl.G; p.tail = c->tail;
     p.chunk = pl.chunk;
     p.ws_keys = (uint32_t *)r.data;
     p.ws_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
@@ -252,6 +254,7 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     ip.k_blk_store = mode == CSA2_FULL ? k_blk : nullptr;
     ip.tok_hist_clear = tok_hist;
     ip.T = T; ip.B = c->block; ip.P = c->pool; ip.n_q = n_q; ip.G = f.idx.G; ip.chunk = f.idx.chunk;
+    ip.tail = c->tail;
     ip.nblk = T / c->block;
     ip.ws_keys = blk_keys; ip.ws_stride = f.blk_stride; ip.ws_hist = head;
     ip.blk_ids = blk_ids; ip.blk_cnt = blk_cnt;
@@ -263,7 +266,7 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     TopkParams tp{};
     tp.q_idx = q_idx; tp.q_seq = q_seq; tp.q_pos = q_pos; tp.k_idx = k_idx;
     tp.blk_ids = blk_ids; tp.blk_cnt = blk_cnt;
-    tp.T = T; tp.B = c->block; tp.P = c->pool; tp.K = c->top_k; tp.n_q = n_q;
+    tp.T = T; tp.B = c->block; tp.P = c->pool; tp.K = c->top_k; tp.n_q = n_q; tp.tail = c->tail;
     tp.G = f.tok.G; tp.chunk = f.tok.chunk;
     tp.ws_keys = tok_keys; tp.ws_stride = f.tok_stride; tp.ws_hist = tok_hist;
     tp.topk = topk; tp.topk_cnt = topk_cnt;

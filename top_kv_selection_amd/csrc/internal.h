@@ -11,6 +11,15 @@ constexpr int kSelectThreads = 512;     // threads of a scoring or many-query se
 constexpr int kSelectWideThreads = 1024; // threads of a one-query-per-workgroup select launch (16 keys each)
 constexpr int kTargetWorkgroups = 512;  // ~2 per CU on a 256-CU MI355X
 constexpr int kMaxCandidates = 16384;   // P*B cap: candidates one query may score
+constexpr int kTailExclude = 1;         // csa2_tail values the kernels test
+constexpr int kTailWhole = 2;
+
+// Blocks eligible for a query at position t: every block holding a visible
+// token, or only the complete ones when a partial own block is excluded.
+__host__ __device__ inline int eligible_blocks(int t, int B, int tail)
+{
+    return tail == kTailExclude ? (t + 1) / B : t / B + 1;
+}
 
 struct BlockKeysParams {
     const int8_t *k_idx;
@@ -25,6 +34,7 @@ struct IndexParams {
     int8_t *k_blk_store;    // non-null: store each query's own block key when the query completes it
     uint32_t *tok_hist_clear;   // non-null (fused layer group): zero [n_q][2048] token histograms
     int T, B, P, n_q, G, chunk, nblk;
+    int tail;               // csa2_tail reading of a partial own block
     uint32_t *ws_keys;
     int64_t ws_stride;
     uint32_t *ws_hist;      // [n_q][2048] top-11-bit histograms (split launches)
@@ -37,6 +47,7 @@ struct TopkParams {
     const int8_t *k_idx;
     const int32_t *blk_ids, *blk_cnt;
     int T, B, P, K, n_q, G, chunk;
+    int tail;               // csa2_tail reading of a partial own block
     uint32_t *ws_keys;
     int64_t ws_stride;
     uint32_t *ws_hist;

@@ -135,13 +135,17 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     const int g = blockIdx.x / p.n_q;
     const int tid = threadIdx.x, part = tid % LPR;
     const int s = p.q_seq[q], t = p.q_pos[q];
-    const int jt = t / p.B, n_elig = jt + 1;
+    const int jt = t / p.B, n_elig = eligible_blocks(t, p.B, p.tail);
     int32_t *ids = p.blk_ids + (size_t)q * p.P;
+    // rows averaged into the own block's key: those at positions <= t, or
+    // (whole-block reading) every row of the block that exists
+    const int own_n = (p.tail == kTailWhole) ? min(p.B, p.T - jt * p.B) : t - jt * p.B + 1;
 
-    // The query's own block (its last eligible one, jt) is scored from the
-    // rows visible to the query, by wave 0 of the workgroup whose range holds
-    // it, one lane per dimension.  A Full layer also stores the key of a block
-    // its query has just completed (t is the block's last position).
+    // The query's own block (jt; its last eligible one unless a partial own
+    // block is excluded, which leaves jt >= n_elig) is scored by wave 0 of the
+    // workgroup whose range holds it, one lane per dimension.  A Full layer
+    // also stores the key of a block its query has just completed (t is the
+    // block's last position).
     const bool store_own = p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk;
     int8_t *own_store = store_own ? p.k_blk_store + ((size_t)s * p.nblk + jt) * DIDX : nullptr;
     const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX;
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
         }
         if (own_pending) {
             own_pending = false;
-            const int kd = block_key_dim<DIDX>(own_rows, t - jt * p.B + 1, tid);
+            const int kd = block_key_dim<DIDX>(own_rows, own_n, tid);
             if (store_own && tid < DIDX) own_store[tid] = (int8_t)kd;
             const int qd = (tid < DIDX) ? (int)p.q_idx[(size_t)q * DIDX + tid] : 0;
             const uint32_t key = (uint32_t)(wave_sum_i32(kd * qd) + (int)kKeyBias);
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(kPoolAllThreads) void k_pool_all(IndexParams p)
         const size_t total = (size_t)p.n_q * P4;
         for (size_t k = id; k < total; k += stride) {
             const int q = (int)(k / P4), j = 4 * (int)(k % P4);
-            const int n = p.q_pos[q] / p.B + 1;
+            const int n = eligible_blocks(p.q_pos[q], p.B, p.tail);
             const int4 v = make_int4(j < n ? j : -1, j + 1 < n ? j + 1 : -1, j + 2 < n ? j + 2 : -1,
                                      j + 3 < n ? j + 3 : -1);
             *reinterpret_cast<int4 *>(p.blk_ids + (size_t)q * p.P + j) = v;
@@ -244,14 +248,14 @@ __global__ __launch_bounds__(kPoolAllThreads) void k_pool_all(IndexParams p)
         const size_t total = (size_t)p.n_q * p.P;
         for (size_t k = id; k < total; k += stride) {
             const int q = (int)(k / p.P), j = (int)(k % p.P);
-            p.blk_ids[k] = (j < p.q_pos[q] / p.B + 1) ? j : -1;
+            p.blk_ids[k] = (j < eligible_blocks(p.q_pos[q], p.B, p.tail)) ? j : -1;
         }
     }
     for (size_t k = id; k < (size_t)p.n_q * DIDX; k += stride) {
         const int q = (int)(k / DIDX), d = (int)(k % DIDX);
         const int s = p.q_seq[q], t = p.q_pos[q];
         const int jt = t / p.B;
-        if (d == 0) p.blk_cnt[q] = jt + 1;
+        if (d == 0) p.blk_cnt[q] = eligible_blocks(t, p.B, p.tail);
         if (p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk) {
             const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX;
             p.k_blk_store[((size_t)s * p.nblk + jt) * DIDX + d] = (int8_t)block_key_dim<DIDX>(own_rows, p.B, d);
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(NT) void k_index_select(IndexParams p)
     const bool fits = p.ws_stride <= NT * IPT;
     if (fits) load_keys_global<IPT>(gkeys, (int)p.ws_stride, k);
     const int t = p.q_pos[q];
-    const int n_elig = t / p.B + 1;
+    const int n_elig = eligible_blocks(t, p.B, p.tail);
     if (n_elig <= p.P) return;   // handled by the scoring launch (nothing was stored)
     store_hist<NT>(hr, ghist, s_hist);
     uint32_t chosen;
@@ -566,7 +570,10 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
     const int qi = q0 + r16;
     const bool qvalid = qi < p.n_q;
     const int sq = qvalid ? p.q_seq[qi] : -1;
-    const int tq = qvalid ? p.q_pos[qi] : -1;
+    // last candidate position of this lane's query: its position, or with a
+    // partial own block excluded the end of its last complete block (-1: no
+    // candidate)
+    const int tq = !qvalid ? -1 : (p.tail == kTailExclude ? (p.q_pos[qi] + 1) / p.B * p.B - 1 : p.q_pos[qi]);
     v4i32 qb = {0, 0, 0, 0};
     if (qvalid && 16 * g < DIDX) qb = *reinterpret_cast<const v4i32 *>(p.q_idx + (size_t)qi * DIDX + 16 * g);
     uint32_t *gt_map = s_buf, *eq_map = s_buf + kDenseQ * MW;   // eq_map doubles as the bin-b1 map
