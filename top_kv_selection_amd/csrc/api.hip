@@ -169,11 +169,11 @@ int32_t do_attend(const csa2_cfg *c, int32_t n_layers, int32_t n_q, const void *
     return hip_status(launch_attend(p, pl, c->head_dim, c->dtype, st));
 }
 
-// ---- fused decode layer group: block scoring -> pool selection -> token
-// scoring -> token Top-K inside the attention launch -> combine (5 launches
-// instead of 6, and no standalone Top-K pass).  Used when the selections are
-// split over workgroups (few queries), the keys of a query fit one
-// workgroup's registers, and the attention takes the MFMA path.
+// ---- fused decode layer group: block scoring -> pool selection and token
+// scoring in one launch -> token Top-K inside the attention launch ->
+// combine (4 launches instead of 6).  Used when the selections are split over
+// workgroups (few queries), the keys of a query fit one workgroup's
+// registers, and the attention takes the MFMA path.
 struct FusedPlan {
     bool ok;
     SelectPlan idx, tok;
@@ -258,10 +258,8 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     ip.nblk = T / c->block;
     ip.ws_keys = blk_keys; ip.ws_stride = f.blk_stride; ip.ws_hist = head;
     ip.blk_ids = blk_ids; ip.blk_cnt = blk_cnt;
-    // block scoring + pool selection (one workgroup per query): a pool stage
-    // fused into the token scoring would redo the pool selection in each of a
-    // query's scoring workgroups, which was measured slower on MI355X
-    if (int32_t e = hip_status(launch_index_blocks(ip, f.idx, c->d_idx, st, true))) return e;
+    // block scoring (keys and histogram to the workspace)
+    if (int32_t e = hip_status(launch_index_blocks(ip, f.idx, c->d_idx, st, false))) return e;
 
     TopkParams tp{};
     tp.q_idx = q_idx; tp.q_seq = q_seq; tp.q_pos = q_pos; tp.k_idx = k_idx;
@@ -270,8 +268,10 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     tp.G = f.tok.G; tp.chunk = f.tok.chunk;
     tp.ws_keys = tok_keys; tp.ws_stride = f.tok_stride; tp.ws_hist = tok_hist;
     tp.topk = topk; tp.topk_cnt = topk_cnt;
-    // token scoring only; the Top-K is taken inside the attention launch
-    if (int32_t e = hip_status(launch_topk_tokens(tp, f.tok, c->d_idx, st, false))) return e;
+    // pool selection + token scoring in one launch (each scoring workgroup
+    // redoes the pool selection); the Top-K is taken inside the attention
+    // launch, whose writer also zeroes the block histogram
+    if (int32_t e = hip_status(launch_pool_tokens(ip, tp, c->d_idx, st))) return e;
 
     AttendParams ap{};
     ap.q = q; ap.q_seq = q_seq; ap.q_pos = q_pos; ap.k_main = k_main; ap.v_main = v_main;
@@ -283,7 +283,7 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     ap.out = out; ap.lse = lse; ap.ws_part = part;
     ap.sel_keys = tok_keys; ap.sel_stride = f.tok_stride; ap.sel_hist = tok_hist;
     ap.sel_pool = blk_ids; ap.sel_pool_cnt = blk_cnt; ap.sel_B = c->block; ap.sel_P = c->pool;
-    ap.topk_out = topk; ap.topk_cnt_out = topk_cnt; ap.blk_hist_clear = nullptr;
+    ap.topk_out = topk; ap.topk_cnt_out = topk_cnt; ap.blk_hist_clear = head;
     return hip_status(launch_attend(ap, f.att, c->head_dim, c->dtype, st, true));
 }
 

@@ -410,6 +410,103 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
     topk_finish<NT, IPT>(p, q, k, n_cand, s_hist, s_pool, s_sm);
 }
 
+// Layer-group decode: the pool selection and the token scoring of a query in
+// one launch.  kPoolTokCand candidates per workgroup; every workgroup of a
+// query first redoes the exact pool selection of k_index_select from the
+// block keys and histogram that the split k_index_blocks launch wrote
+// (workgroup 0 also writes blk_ids / blk_cnt), keeps the pool in LDS, and
+// then scores its candidates like a split k_topk_tokens launch (token keys
+// and the token histogram go to the workspace).  The selection is repeated
+// P*B / kPoolTokCand times per query, but the launch boundary and the round
+// trip of the pool through global memory are gone.  The block histogram is
+// left as read; the caller's next launch zeroes it.  Workgroups are numbered
+// query-fastest over n_q rounded up to 8, so a query's workgroups share one
+// XCD's L2 (round-robin dispatch) and read its block keys from HBM once.
+constexpr int kPoolTokCand = 1024;
+
+template <int DIDX>
+__global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams ip, TopkParams tp, int n_q_pad)
+{
+    constexpr int NT = kSelectWideThreads, IPT = kLdsKeys / NT;
+    constexpr int LPR = DIDX / 16, RPP = NT / LPR;
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
+    __shared__ int32_t s_pool[kFusedPoolLds];
+    __shared__ uint32_t s_sm[NT / 64 + 4];
+    const int q = (int)blockIdx.x % n_q_pad, g = (int)blockIdx.x / n_q_pad;
+    if (q >= ip.n_q) return;
+    const int tid = threadIdx.x, part = tid % LPR;
+    const int B = ip.B, P = ip.P;
+
+    // every load of the pool selection (and the indexer query of the
+    // scoring) is issued before the first is used
+    HistRegs<NT> hr;
+    load_hist<NT>(ip.ws_hist + (size_t)q * kRadixBins, hr);
+    uint32_t k[IPT];
+    load_keys_global<IPT>(ip.ws_keys + (size_t)q * ip.ws_stride, (int)ip.ws_stride, k);
+    const int4 qv = *reinterpret_cast<const int4 *>(tp.q_idx + (size_t)q * DIDX + part * 16);
+    const int s = ip.q_seq[q], t = ip.q_pos[q];
+    const int n_elig = eligible_blocks(t, B, ip.tail);
+    hist_to_lds<NT>(hr, s_hist);
+    int n_pool;
+    if (n_elig <= P) {   // the pool is every eligible block (k_index_blocks wrote it)
+        for (int r = tid; r < n_elig; r += NT) s_pool[r] = r;
+        n_pool = n_elig;
+    } else {
+        mask_keys<IPT>(n_elig, k);
+        const Threshold th = threshold_regs<NT, IPT>(k, n_elig, (uint32_t)P, s_hist, s_sm);
+        int32_t *ids = ip.blk_ids + (size_t)q * P;
+        const bool writer = g == 0;
+        auto emit = [&](uint32_t slot, int i) {
+            if (slot < (uint32_t)P) {
+                s_pool[slot] = i;
+                if (writer) ids[slot] = i;
+            }
+        };
+        const uint32_t chosen = compact_regs<NT, IPT>(k, th, emit, s_sm);
+        n_pool = (int)min(chosen, (uint32_t)P);
+        if (writer) {
+            for (int o = n_pool + tid; o < P; o += NT) ids[o] = -1;
+            if (tid == 0) ip.blk_cnt[q] = n_pool;
+        }
+    }
+    // the pool is complete once this barrier is passed; the histogram memory
+    // is free again and counts this workgroup's token keys
+    lds_barrier();
+    for (int b = tid; b < kHistWords; b += NT) s_hist[b] = 0;
+
+    const int n_cand = n_pool * B;
+    const int lo = g * kPoolTokCand, hi = min(n_cand, lo + kPoolTokCand);
+    uint32_t *gkeys = tp.ws_keys + (size_t)q * tp.ws_stride;
+    const int8_t *seq_rows = tp.k_idx + (size_t)s * tp.T * DIDX + part * 16;
+    for (int base = lo; base < hi; base += RPP * kUnroll) {
+        int pos[kUnroll];
+        bool vis[kUnroll];
+        int4 kv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int c = base + u * RPP + tid / LPR;
+            const int cl = min(c, hi - 1);
+            pos[u] = s_pool[cl / B] * B + cl % B;
+            vis[u] = c < hi && pos[u] <= t;
+            kv[u] = *reinterpret_cast<const int4 *>(seq_rows + (size_t)(vis[u] ? pos[u] : 0) * DIDX);
+        }
+        if (base == lo) lds_barrier();   // the histogram is cleared
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int c = base + u * RPP + tid / LPR;
+            int acc = dot16_i8(kv[u], qv);
+            acc = row_reduce<LPR>(acc);
+            if (c < hi && part == 0) {
+                const uint32_t key = vis[u] ? (uint32_t)(acc + (int)kKeyBias) : 0u;
+                gkeys[c] = key;
+                atomicAdd(&s_hist[hist_pad(key >> kRadixBits)], 1u);
+            }
+        }
+    }
+    lds_barrier();
+    flush_hist<NT>(s_hist, tp.ws_hist + (size_t)q * kRadixBins);
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
 {
@@ -974,6 +1071,21 @@ hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &pl, int d_i
     if (p.n_q <= 0) return hipSuccess;
     if (d_idx == 64) launch_topk_t<64>(p, pl, st, with_select);
     else launch_topk_t<32>(p, pl, st, with_select);
+    return hipGetLastError();
+}
+
+int pool_tokens_groups(int P, int B)
+{
+    return ceil_div((long long)P * B, kPoolTokCand);
+}
+
+hipError_t launch_pool_tokens(const IndexParams &ip, const TopkParams &tp, int d_idx, hipStream_t st)
+{
+    if (ip.n_q <= 0) return hipSuccess;
+    const int n_q_pad = (ip.n_q + 7) / 8 * 8;
+    const dim3 grid((unsigned)(n_q_pad * pool_tokens_groups(ip.P, ip.B)));
+    if (d_idx == 64) hipLaunchKernelGGL(k_pool_tokens<64>, grid, dim3(kSelectWideThreads), 0, st, ip, tp, n_q_pad);
+    else hipLaunchKernelGGL(k_pool_tokens<32>, grid, dim3(kSelectWideThreads), 0, st, ip, tp, n_q_pad);
     return hipGetLastError();
 }
 
