@@ -81,6 +81,21 @@ def test_decode_scaled_ragged_context(lib):
     check(lib, cfg, seed=21)
 
 
+def test_decode_queries_not_in_sequence_order(lib):
+    """Query i of a decode batch reads sequence n_seq - 1 - i: the block pass
+    cannot take its first batch from the sequence numbered like the query and
+    loads it again."""
+    _, pipeline = lib
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=5, ctx=9001, pool=128, top_k=200, window=64,
+                   layers=("full", "reuse"))
+    wl = W.generate(cfg, seed=27)
+    wl.q_seq = np.ascontiguousarray(wl.q_seq[::-1])
+    print(f"case {cfg.name} reversed q_seq {wl.q_seq.tolist()}", flush=True)
+    got = run_gpu(pipeline, wl)
+    ref = oracle.run_layers(wl)
+    compare_run(got, ref, cfg, what="reversed q_seq")
+
+
 def test_decode_scaled_tie_heavy(lib):
     cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=3, ctx=8192, pool=128, top_k=200, window=64,
                    layers=("full", "reuse", "reuse"))
