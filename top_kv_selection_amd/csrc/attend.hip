@@ -121,9 +121,15 @@ __global__ __launch_bounds__(256) void k_attend_generic(AttendParams p)
 
 // ============================================================ MFMA kernel
 constexpr int kWaves = 8;                      // waves per workgroup, 32 keys each per step
-constexpr int kStepKeys = kWaves * 32;         // keys per workgroup step
+constexpr int kStepKeys = kWaves * 32;         // keys per workgroup step (32 keys per wave)
+// With few (query, layer, head group) items the key list is split over
+// workgroups, and a workgroup's gather is bounded by what one CU keeps in
+// flight; waves then take 16 keys per step (one QK tile), which doubles the
+// workgroups that share a key list and halves each one's gather.
+constexpr int kStepKeysHalf = kWaves * 16;
 constexpr int kRowChunk = kAttendRowChunk;     // row codes staged in LDS at once
-static_assert(kRowChunk % (kWaves * 64) == 0 && kRowChunk % kStepKeys == 0, "whole staging rounds and steps");
+static_assert(kRowChunk % (kWaves * 64) == 0 && kRowChunk % kStepKeys == 0 && kRowChunk % kStepKeysHalf == 0,
+              "whole staging rounds and steps");
 constexpr int kVtStride = 40;                  // bf16 per V^T row in LDS (32 keys + pad)
 // After the key loop a wave's V^T buffer holds its partial output, 16 heads x
 // kObStride floats: with 144 floats per head, the 16-byte writes of a wave
@@ -144,10 +150,12 @@ __device__ __forceinline__ int slot_key(int g, int e) { return (e < 4) ? 4 * g +
 // with the query count padded to a multiple of 8, so with round-robin XCD
 // dispatch every layer of a query runs on one XCD and the shared main rows
 // are fetched from HBM once and then hit that XCD's L2.
-template <bool FUSED>
+template <bool FUSED, int KPW>
 __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
 {
+    static_assert(KPW == 16 || KPW == 32, "one or two QK tiles per wave and step");
     constexpr int NT = kWaves * 64, IPT = kLdsKeys / NT;
+    constexpr int NTAU = KPW / 16, STEP = kWaves * KPW;
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[kWaves][128 * kVtStride];
     __shared__ float s_ml[kWaves][16][2];
     __shared__ int s_rows[kRowChunk];
@@ -230,7 +238,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         cnt = p.topk ? p.topk_cnt[i] : 0;
     }
     const int n_keys = cnt + win.nw;
-    // this workgroup's share of the key list (whole steps of kStepKeys keys)
+    // this workgroup's share of the key list (whole steps of STEP keys)
     const int k_begin = min(n_keys, split * p.keys_per_split);
     const int k_end = min(n_keys, k_begin + p.keys_per_split);
 
@@ -248,7 +256,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
     // instead of each waiting under its own branch.
     auto stage_rows = [&](int kc) {
         constexpr int SPT = kRowChunk / (kWaves * 64);
-        const int n_stage = min(kRowChunk, (k_end - kc + kStepKeys - 1) / kStepKeys * kStepKeys);
+        const int n_stage = min(kRowChunk, (k_end - kc + STEP - 1) / STEP * STEP);
         int id[SPT];
 #pragma unroll
         for (int u = 0; u < SPT; u++) {
@@ -278,19 +286,23 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
 
     uint16_t *vt = s_vt[w];
 
-    // K operand rows (keys kw + r16 and kw + 16 + r16) and this lane's 8 V
-    // slots (dims r16*8 .. r16*8+7) of one step, all issued back to back.
+    // K operand rows (keys kw + r16 and, with two tiles, kw + 16 + r16) and
+    // this lane's V slots (dims r16*8 .. r16*8+7) of one step, all issued
+    // back to back.  With one tile the V slots of the absent second tile are
+    // zero, so its columns of V^T are zero (and its P terms are zero too).
     auto load_kv = [&](int kb, bf16x8_t (&ka)[2][4], uint4 (&vv)[8]) {
-        const int *rows = s_rows + ((kb - k_begin + w * 32) % kRowChunk);
+        const int *rows = s_rows + ((kb - k_begin + w * KPW) % kRowChunk);
 #pragma unroll
-        for (int tau = 0; tau < 2; tau++) {
+        for (int tau = 0; tau < NTAU; tau++) {
             const uint16_t *kr = row_ptr(rows[16 * tau + r16], kmain, kswa);
 #pragma unroll
             for (int kk = 0; kk < 4; kk++) ka[tau][kk] = *reinterpret_cast<const bf16x8_t *>(kr + kk * 32 + g * 8);
         }
 #pragma unroll
-        for (int e = 0; e < 8; e++)
+        for (int e = 0; e < 4 * NTAU; e++)
             vv[e] = *reinterpret_cast<const uint4 *>(row_ptr(rows[slot_key(g, e)], vmain, vswa) + r16 * 8);
+#pragma unroll
+        for (int e = 4 * NTAU; e < 8; e++) vv[e] = make_uint4(0u, 0u, 0u, 0u);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -298,12 +310,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
     // left the registers (after QK and the V^T write) and issues the following
     // step's loads into the same registers, overlapping softmax and PV.
     auto compute = [&](int kb, bf16x8_t (&ka)[2][4], uint4 (&vv)[8], auto &&next) {
-        const int kw = kb + w * 32;
+        const int kw = kb + w * KPW;
         // S^T = K Q^T: lane holds keys 4g+ii (tile 0) and 16+4g+ii (tile 1) of head r16
-        f32x4_t st[2];
+        f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int tau = 0; tau < 2; tau++) {
-            st[tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int tau = 0; tau < NTAU; tau++) {
 #pragma unroll
             for (int kk = 0; kk < 4; kk++)
                 st[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tau][kk], qb[kk], st[tau], 0, 0, 0);
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             const int key = kw + slot_key(g, e);
-            sc[e] = (key < k_end) ? st[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+            sc[e] = (e < 4 * NTAU && key < k_end) ? st[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
             mx = fmaxf(mx, sc[e]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -385,8 +396,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
             stage_rows(k_begin);
         }
         load_kv(k_begin, ka, vv);
-        for (int kb = k_begin; kb < k_end; kb += kStepKeys) {
-            const int kn = kb + kStepKeys;
+        for (int kb = k_begin; kb < k_end; kb += STEP) {
+            const int kn = kb + STEP;
             const bool more = kn < k_end;
             const bool restage = more && ((kn - k_begin) % kRowChunk == 0);
             compute(kb, ka, vv, [&] {
@@ -1003,19 +1014,23 @@ static int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b);
 
 AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dtype)
 {
-    AttendPlan pl{(dtype == 1) && (D == 128) && (H % 16 == 0), false, 1, 0, 0};
+    AttendPlan pl{(dtype == 1) && (D == 128) && (H % 16 == 0), false, 1, 0, 0, 32};
     if (!pl.mfma) return pl;
     // Split a key list over several workgroups only when there are too few
     // (query, layer, head group) triples to spread the gather over the chip;
-    // each split then costs a device-scope merge.
-    const int steps = std::max(1, (K + W + kStepKeys - 1) / kStepKeys);
+    // each split then costs a device-scope merge.  Split lists are walked
+    // with 16-key waves (twice the workgroups, half the gather each).
     const long long base = (long long)n_q * n_layers * (H / 16);
+    const bool split_regime = base < kTargetWorkgroups / 2;
+    pl.kpw = split_regime ? 16 : 32;
+    const int step = split_regime ? kStepKeysHalf : kStepKeys;
+    const int steps = std::max(1, (K + W + step - 1) / step);
     int n_splits = 1;
-    if (base < kTargetWorkgroups / 2) n_splits = (int)std::min<long long>(steps, (kTargetWorkgroups / 2 + base - 1) / base);
+    if (split_regime) n_splits = (int)std::min<long long>(steps, (kTargetWorkgroups + base - 1) / base);
     const int steps_per_split = (steps + n_splits - 1) / n_splits;
     n_splits = (steps + steps_per_split - 1) / steps_per_split;
     pl.n_splits = n_splits;
-    pl.keys_per_split = steps_per_split * kStepKeys;
+    pl.keys_per_split = steps_per_split * step;
     pl.part_bytes = n_splits > 1 ? (size_t)base * n_splits * kPartFloats * sizeof(float) : 0;
     // enough items for one wave each to fill the chip (never split then): the
     // row kernel, when the row tables fit its 32-bit buffer offsets
@@ -1046,8 +1061,13 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
         p.n_splits = pl.n_splits;
         p.keys_per_split = pl.keys_per_split;
         const long long n_wg = (long long)p.n_q_pad * pl.n_splits * (p.H / 16) * p.n_layers;
-        if (fused_select) hipLaunchKernelGGL(k_attend_mfma<true>, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
-        else hipLaunchKernelGGL(k_attend_mfma<false>, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+        if (pl.kpw == 16) {
+            if (fused_select) hipLaunchKernelGGL((k_attend_mfma<true, 16>), dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+            else hipLaunchKernelGGL((k_attend_mfma<false, 16>), dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+        } else {
+            if (fused_select) hipLaunchKernelGGL((k_attend_mfma<true, 32>), dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+            else hipLaunchKernelGGL((k_attend_mfma<false, 32>), dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+        }
         if (pl.n_splits > 1) {
             const long long n_rows = (long long)p.n_q * (p.H / 16) * p.n_layers;
             hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)n_rows), dim3(512), 0, st, p);

@@ -95,6 +95,7 @@ struct AttendPlan {
     bool rows;    // many items: one wave per (query, layer, head group), no splits
     int n_splits, keys_per_split;
     size_t part_bytes;
+    int kpw;      // keys per wave and step of the MFMA kernel: 32, or 16 when a list is split
 };
 
 // Workspace head bytes of a selection launch: one 2048-bin histogram per
