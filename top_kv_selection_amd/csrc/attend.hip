@@ -145,11 +145,14 @@ constexpr int kMergeBatch = 8;                 // split records loaded at once b
 // tile 1).  Both PV operands use this same order along the contraction.
 __device__ __forceinline__ int slot_key(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
 
-// One workgroup per (query, head group of 16, layer): no split of the key
-// list, hence no cross-workgroup merge.  Workgroups are numbered query-fastest
-// with the query count padded to a multiple of 8, so with round-robin XCD
-// dispatch every layer of a query runs on one XCD and the shared main rows
-// are fetched from HBM once and then hit that XCD's L2.
+// One workgroup per (query, split of the key list, head group of 16, layer);
+// with several splits each writes a (max, sum, acc) record that
+// k_attend_combine merges.  KPW keys per wave and step (32, or 16 when lists
+// are split).  Workgroups are numbered query-fastest with the query count
+// padded to a multiple of 8, so with round-robin XCD dispatch every layer of
+// a query runs on one XCD and the shared main rows are fetched from HBM once
+// and then hit that XCD's L2.  FUSED: the token Top-K is taken first, from
+// the token keys and histogram (layer-group decode).
 template <bool FUSED, int KPW>
 __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
 {

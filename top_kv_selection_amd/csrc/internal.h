@@ -109,8 +109,7 @@ AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dt
 hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hipStream_t st);
 hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &plan, int d_idx,
                                hipStream_t st, bool with_select = true);
-hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &plan, int d_idx,
-                              hipStream_t st, bool with_select = true);
+hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &plan, int d_idx, hipStream_t st);
 hipError_t launch_attend(const AttendParams &p, const AttendPlan &plan, int D, int dtype,
                          hipStream_t st, bool fused_select = false);
 

@@ -11,10 +11,12 @@
 // Decode has one query per sequence, so a query's scan (up to 1 MiB of block
 // keys or candidate rows at 128K context) is split over G workgroups that
 // write keys and a histogram to the workspace; a second launch with one
-// workgroup per query then selects.  (A last-arriving-workgroup hand-off was
-// measured at ~6 us on MI355X -- an L2 writeback plus a device-scope atomic
-// round trip -- against ~2.5 us for a kernel boundary.)  With many queries
-// (prefill) each workgroup owns one query and keeps its keys in LDS.
+// workgroup per query then selects (in the layer group, the workgroups that
+// score the tokens each redo the pool selection instead, k_pool_tokens).  (A
+// last-arriving-workgroup hand-off was measured at ~6 us on MI355X -- an L2
+// writeback plus a device-scope atomic round trip -- against ~2.5 us for a
+// kernel boundary.)  With many queries (prefill) each workgroup owns one
+// query and keeps its keys in LDS.
 // Loads are 16-byte per lane with DIDX/16 lanes per row, so a wave reads
 // 1 KiB of consecutive rows per instruction.
 #include "device_common.h"
@@ -1048,7 +1050,7 @@ hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &pl, int d
 }
 
 template <int DIDX>
-static void launch_topk_t(const TopkParams &p, const SelectPlan &pl, hipStream_t st, bool with_select)
+static void launch_topk_t(const TopkParams &p, const SelectPlan &pl, hipStream_t st)
 {
     if (pl.dense) {
         hipLaunchKernelGGL((k_topk_dense<DIDX>), dim3((unsigned)((p.n_q + kDenseQ - 1) / kDenseQ)),
@@ -1058,19 +1060,17 @@ static void launch_topk_t(const TopkParams &p, const SelectPlan &pl, hipStream_t
     dim3 grid((unsigned)(p.n_q * pl.G));
     if (pl.split) {
         hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
-        if (with_select)
-            hipLaunchKernelGGL((k_topk_select<kSelectWideThreads>), dim3((unsigned)p.n_q), dim3(kSelectWideThreads), 0, st, p);
+        hipLaunchKernelGGL((k_topk_select<kSelectWideThreads>), dim3((unsigned)p.n_q), dim3(kSelectWideThreads), 0, st, p);
     } else {
         hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
     }
 }
 
-hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &pl, int d_idx, hipStream_t st,
-                              bool with_select)
+hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &pl, int d_idx, hipStream_t st)
 {
     if (p.n_q <= 0) return hipSuccess;
-    if (d_idx == 64) launch_topk_t<64>(p, pl, st, with_select);
-    else launch_topk_t<32>(p, pl, st, with_select);
+    if (d_idx == 64) launch_topk_t<64>(p, pl, st);
+    else launch_topk_t<32>(p, pl, st);
     return hipGetLastError();
 }
 
