@@ -251,16 +251,24 @@ def run_layers(wl, rows=None, threads=None):
     q_seq, q_pos = wl.q_seq[idx], wl.q_pos[idx]
     res = {"rows": idx, "index": {}, "out": [], "lse": []}
     current = None
+    # every Full layer has its own main-KV and indexer cache, which the
+    # layers after it share until the next Full layer (mode table of "CSA2
+    # with cross-layer reuse": a Full layer computes its own keys, Reuse and
+    # Reindex layers share them)
+    n_full = 0
     for layer, mode in enumerate(cfg.layers):
+        if mode == "full":
+            n_full += 1
+        k_idx, k_main, v_main = wl.cache(max(n_full - 1, 0))
         if mode in ("full", "reindex"):
-            sel = select(wl.q_idx[layer][idx], q_seq, q_pos, wl.k_idx, cfg.block, cfg.pool,
+            sel = select(wl.q_idx[layer][idx], q_seq, q_pos, k_idx, cfg.block, cfg.pool,
                          cfg.top_k, threads, cfg.tail)
             res["index"][layer] = dict(zip(("blk_ids", "blk_cnt", "topk", "topk_cnt"), sel))
             current = sel
         elif mode == "reindex_tokens":
             if current is None:
                 raise ValueError("a token-only Reindex layer needs an earlier Full/Reindex layer")
-            topk, cnt = topk_given_pool(wl.q_idx[layer][idx], q_seq, q_pos, wl.k_idx, cfg.block,
+            topk, cnt = topk_given_pool(wl.q_idx[layer][idx], q_seq, q_pos, k_idx, cfg.block,
                                         cfg.top_k, current[0], current[1], threads)
             sel = (current[0], current[1], topk, cnt)
             res["index"][layer] = dict(zip(("blk_ids", "blk_cnt", "topk", "topk_cnt"), sel))
@@ -271,7 +279,7 @@ def run_layers(wl, rows=None, threads=None):
             if current is None:
                 raise ValueError("a Reuse layer needs an earlier Full/Reindex layer")
             topk, cnt = current[2], current[3]
-        o, l = attend(wl.q[layer][idx], q_seq, q_pos, wl.k_main, wl.v_main, wl.k_swa[layer],
+        o, l = attend(wl.q[layer][idx], q_seq, q_pos, k_main, v_main, wl.k_swa[layer],
                       wl.v_swa[layer], cfg.swa_first, topk, cnt, cfg.window, None, threads)
         res["out"].append(o)
         res["lse"].append(l)

@@ -142,6 +142,28 @@ def test_prefill_row_kernel_two_head_groups(lib):
     check(lib, cfg, seed=30)
 
 
+# ------------------------------------------------------------------ encoder-decoder flow
+def test_encoder_pattern_scaled_all_rows(lib):
+    """Window, [Full + Reuse...] with three Full layers, each with its own
+    main-KV and indexer cache, at every position of a prompt."""
+    cfg = W.scaled(W.CONFIGS["encoder_prefill_8k"], ctx=600, pool=32, top_k=64, window=24,
+                   layers=("swa", "full", "reuse", "reuse", "full", "reuse", "full"))
+    check(lib, cfg, seed=50)
+
+
+def test_encoder_prefill_8k_sampled_rows(lib):
+    cfg = W.CONFIGS["encoder_prefill_8k"]
+    rng = np.random.default_rng(6)
+    edges = [0, 1, 7, 8, 127, 128, 1023, 1024, 4095, 8190, 8191]
+    rows = np.unique(np.concatenate([edges, rng.choice(cfg.n_q, 40, replace=False)]))
+    check(lib, cfg, rows=rows)
+
+
+def test_decoder_replay_8k(lib):
+    """The last 128 prompt positions through the 20-layer decoder pattern."""
+    check(lib, W.CONFIGS["decoder_replay_8k"])
+
+
 # ------------------------------------------------------------------ selection variants
 @pytest.mark.parametrize("tail", [W.TAIL_EXCLUDE, W.TAIL_WHOLE])
 def test_tail_reading_prefill_block_pass(lib, tail):

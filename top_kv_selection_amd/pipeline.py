@@ -38,6 +38,7 @@ class Group:
     q_idx: torch.Tensor = None      # [n_q][d] for full/reindex/reindex_tokens
     index_of: int = -1              # group whose indices a reuse group takes
     pool_of: int = -1               # group whose pool a token-only Reindex group reads
+    cache: int = 0                  # main-KV + indexer cache (one per Full layer)
 
 
 @dataclass
@@ -51,12 +52,30 @@ class DeviceWorkload:
     k_main: torch.Tensor
     v_main: torch.Tensor
     groups: list
+    # caches of the second, third, ... Full layer: (k_idx, k_blk, k_main, v_main)
+    extra: list = field(default_factory=list)
     # one index set per indexing group
     blk_ids: dict = field(default_factory=dict)
     blk_cnt: dict = field(default_factory=dict)
     topk: dict = field(default_factory=dict)
     topk_cnt: dict = field(default_factory=dict)
     ws: torch.Tensor = None
+
+
+def group_caches(cfg: Config) -> list:
+    """Cache of each layer group: a Full layer opens its own main-KV and
+    indexer cache, and the groups after it share that cache until the next
+    Full layer (groups before the first Full layer use cache 0)."""
+    out, n_full = [], 0
+    for mode, _ in cfg.groups():
+        n_full += mode == "full"
+        out.append(max(n_full - 1, 0))
+    return out
+
+
+def cache(dw: DeviceWorkload, c: int):
+    """(k_idx, k_blk, k_main, v_main) of cache c (0: the first Full layer's)."""
+    return (dw.k_idx, dw.k_blk, dw.k_main, dw.v_main) if c == 0 else dw.extra[c - 1]
 
 
 def upload(wl: Workload, device="cuda", q_idx=None, q=None) -> DeviceWorkload:
@@ -71,7 +90,12 @@ def upload(wl: Workload, device="cuda", q_idx=None, q=None) -> DeviceWorkload:
     dw = DeviceWorkload(cfg, lcfg, _dev(wl.q_seq, device), _dev(wl.q_pos, device), k_idx,
                         torch.zeros((S, T // cfg.block, d), dtype=torch.int8, device=device),
                         _real(wl.k_main, cfg, device), _real(wl.v_main, cfg, device), [])
+    for c in range(1, cfg.n_caches):
+        ki, km, vm = wl.cache(c)
+        dw.extra.append((_dev(ki, device), torch.zeros((S, T // cfg.block, d), dtype=torch.int8, device=device),
+                         _real(km, cfg, device), _real(vm, cfg, device)))
     tdt = lcfg.torch_dtype
+    caches = group_caches(cfg)
     for mode, layers in cfg.groups():
         grp = Group(mode, layers,
                     _real(np.stack([q[l] for l in layers]), cfg, device),
@@ -79,6 +103,7 @@ def upload(wl: Workload, device="cuda", q_idx=None, q=None) -> DeviceWorkload:
                     _real(np.stack([wl.v_swa[l] for l in layers]), cfg, device),
                     torch.empty((len(layers), cfg.n_q, cfg.n_heads, cfg.head_dim), dtype=tdt, device=device),
                     torch.empty((len(layers), cfg.n_q, cfg.n_heads), dtype=torch.float32, device=device))
+        grp.cache = caches[len(dw.groups)]
         if mode in ("full", "reindex", "reindex_tokens"):
             grp.q_idx = _dev(q_idx[layers[0]], device)
             g = len(dw.groups)
@@ -104,10 +129,13 @@ def upload(wl: Workload, device="cuda", q_idx=None, q=None) -> DeviceWorkload:
 
 
 def build_cache(dw: DeviceWorkload, upto_block=None):
-    """Block keys of every complete block (the state of the cache before a step)."""
+    """Block keys of every complete block of every cache (the state of the
+    caches before a step)."""
     T = dw.k_idx.shape[1]
     end = T // dw.cfg.block if upto_block is None else upto_block
-    B.csa2_build_block_keys(dw.lcfg, dw.k_idx, dw.k_blk, 0, end)
+    for c in range(dw.cfg.n_caches):
+        k_idx, k_blk, _, _ = cache(dw, c)
+        B.csa2_build_block_keys(dw.lcfg, k_idx, k_blk, 0, end)
 
 
 def step_update_begin(dw: DeviceWorkload) -> int:
@@ -125,9 +153,10 @@ def run(dw: DeviceWorkload):
         src = grp.index_of
         idx = src if src >= 0 else None
         pool = grp.pool_of if grp.mode == "reindex_tokens" else idx
+        k_idx, k_blk, k_main, v_main = cache(dw, grp.cache)
         B.csa2_layer_group(
-            dw.lcfg, grp.mode, grp.q_idx, dw.q_seq, dw.q_pos, dw.k_idx, dw.k_blk, begin, grp.q,
-            dw.k_main, dw.v_main, grp.k_swa, grp.v_swa, dw.cfg.swa_first,
+            dw.lcfg, grp.mode, grp.q_idx, dw.q_seq, dw.q_pos, k_idx, k_blk, begin, grp.q,
+            k_main, v_main, grp.k_swa, grp.v_swa, dw.cfg.swa_first,
             dw.blk_ids.get(pool), dw.blk_cnt.get(pool), dw.topk.get(idx), dw.topk_cnt.get(idx),
             grp.out, grp.lse, dw.ws)
 
@@ -158,11 +187,12 @@ def replicate(dw: DeviceWorkload, q_idx=None, q=None) -> DeviceWorkload:
     dev = dw.k_idx.device
     new = DeviceWorkload(cfg, dw.lcfg, dw.q_seq.clone(), dw.q_pos.clone(), dw.k_idx.clone(),
                          dw.k_blk.clone(), dw.k_main.clone(), dw.v_main.clone(), [])
+    new.extra = [tuple(x.clone() for x in c) for c in dw.extra]
     for g, grp in enumerate(dw.groups):
         ng = Group(grp.mode, list(grp.layers),
                    grp.q.clone() if q is None else _real(np.stack([q[l] for l in grp.layers]), cfg, dev),
                    grp.k_swa.clone(), grp.v_swa.clone(), torch.empty_like(grp.out), torch.empty_like(grp.lse),
-                   None, grp.index_of, grp.pool_of)
+                   None, grp.index_of, grp.pool_of, grp.cache)
         if grp.q_idx is not None:
             ng.q_idx = grp.q_idx.clone() if q_idx is None else _dev(q_idx[grp.layers[0]], dev)
             if g in dw.blk_ids:

@@ -15,10 +15,21 @@ patterns of its "CSA2 with cross-layer reuse" section.  Five workloads:
 * ``prefill_8k``          causal prefill of 8,192 tokens + 2 pure sliding-window layers
 * ``decoder_pattern_64k`` batch 8, 64K context, Full + 3 Reuse, [Reindex + 3 Reuse] x 4
 
+and the two halves of the causal encoder-decoder flow of the V4.1 Flash page
+("Asymmetric encoder-decoder (CED)": prompt tokens go through the 20 encoder
+layers only, plus a 128-token decoder replay; the mode table's encoder and
+decoder patterns):
+
+* ``encoder_prefill_8k``  an 8,192-token prompt through window, window,
+  [Full + 5 Reuse] x 3 (every Full layer with its own main-KV and indexer cache)
+* ``decoder_replay_8k``   the last 128 prompt positions through the decoder
+  pattern Full + 3 Reuse, [Reindex + 3 Reuse] x 4
+
 Recipe (both sides read identical bytes):
 * ``numpy.random.Generator(PCG64(1000 + config_number))``;
 * draw order: ``k_idx``, each indexing layer's ``q_idx`` (model order), main K,
-  main V, then per layer (model order) Q, sliding-window K, sliding-window V;
+  main V, then per layer (model order) Q, sliding-window K, sliding-window V,
+  then for every Full layer after the first its own ``k_idx``, main K, main V;
 * int8 values are uniform integers in [-127, 127];
 * real values are standard normal drawn in fp32 and, for bf16 workloads,
   rounded to bf16 with round-to-nearest-even (stored as uint16 bit patterns).
@@ -54,6 +65,7 @@ class Config:
     window: int              # W
     layers: tuple            # per-layer mode, model order
     tail: int = TAIL_VISIBLE  # reading of a partial own block (see TAIL_*)
+    replay: int = 0          # (not decode) queries are only the last `replay` positions
 
     @property
     def seed(self) -> int:
@@ -61,7 +73,14 @@ class Config:
 
     @property
     def n_q(self) -> int:
-        return self.n_seq if self.decode else self.n_seq * self.ctx
+        if self.decode:
+            return self.n_seq
+        return self.n_seq * (self.replay if self.replay > 0 else self.ctx)
+
+    @property
+    def n_caches(self) -> int:
+        """Main-KV + indexer caches: one per Full layer (at least one)."""
+        return max(1, sum(1 for m in self.layers if m == FULL))
 
     @property
     def n_layers(self) -> int:
@@ -94,6 +113,13 @@ class Config:
         return out
 
 
+def _encoder_pattern():
+    pat = [SWA_ONLY, SWA_ONLY]
+    for _ in range(3):
+        pat += [FULL] + [REUSE] * 5
+    return tuple(pat)
+
+
 def _decoder_pattern():
     pat = [FULL, REUSE, REUSE, REUSE]
     for _ in range(4):
@@ -112,6 +138,10 @@ CONFIGS = {
                (FULL, SWA_ONLY, SWA_ONLY)),
         Config("decoder_pattern_64k", 5, "bf16", 8, 65536, True, 16, 128, 64, 8, 2048, 512, 128,
                _decoder_pattern()),
+        Config("encoder_prefill_8k", 6, "bf16", 1, 8192, False, 16, 128, 64, 8, 2048, 512, 128,
+               _encoder_pattern()),
+        Config("decoder_replay_8k", 7, "bf16", 1, 8192, False, 16, 128, 64, 8, 2048, 512, 128,
+               _decoder_pattern(), replay=128),
     ]
 }
 
@@ -145,6 +175,11 @@ class Workload:
     v_swa: list
     q_seq: np.ndarray          # int32 [n_q]
     q_pos: np.ndarray          # int32 [n_q]
+    extra_caches: list = dataclasses.field(default_factory=list)   # (k_idx, k_main, v_main) of Full layers 2, 3, ...
+
+    def cache(self, c: int):
+        """(k_idx, k_main, v_main) of cache c (c = 0: the first Full layer's)."""
+        return (self.k_idx, self.k_main, self.v_main) if c == 0 else self.extra_caches[c - 1]
 
 
 def _real(rng, shape, dtype):
@@ -160,6 +195,9 @@ def query_rows(cfg: Config):
     if cfg.decode:
         q_seq = np.arange(cfg.n_seq, dtype=np.int32)
         q_pos = np.full(cfg.n_seq, cfg.ctx - 1, dtype=np.int32)
+    elif cfg.replay > 0:
+        q_seq = np.repeat(np.arange(cfg.n_seq, dtype=np.int32), cfg.replay)
+        q_pos = np.tile(np.arange(cfg.ctx - cfg.replay, cfg.ctx, dtype=np.int32), cfg.n_seq)
     else:
         q_seq = np.repeat(np.arange(cfg.n_seq, dtype=np.int32), cfg.ctx)
         q_pos = np.tile(np.arange(cfg.ctx, dtype=np.int32), cfg.n_seq)
@@ -181,8 +219,12 @@ def generate(cfg: Config, seed: Optional[int] = None, int_range=(-127, 127)) -> 
         q.append(_real(rng, (cfg.n_q, H, D), cfg.dtype))
         k_swa.append(_real(rng, (S, cfg.swa_len, D), cfg.dtype))
         v_swa.append(_real(rng, (S, cfg.swa_len, D), cfg.dtype))
+    extra = []
+    for _ in range(cfg.n_caches - 1):
+        extra.append((_ints(rng, (S, T, d), lo, hi), _real(rng, (S, T, D), cfg.dtype),
+                      _real(rng, (S, T, D), cfg.dtype)))
     q_seq, q_pos = query_rows(cfg)
-    return Workload(cfg, k_idx, q_idx, k_main, v_main, q, k_swa, v_swa, q_seq, q_pos)
+    return Workload(cfg, k_idx, q_idx, k_main, v_main, q, k_swa, v_swa, q_seq, q_pos, extra)
 
 
 def fresh_queries(cfg: Config, seed: int):
