@@ -1,0 +1,71 @@
+"""Seeded sweep of small random configurations, each through the C ABI and
+compared with the oracle (indices exact, outputs within the tolerance of
+parity.py).  The draws span the sizes the library accepts: blocks of 1 to 16
+tokens, pools smaller or larger than the eligible blocks, Top-K from 0 to
+over 500, windows from 0 to 200, d_idx 32/64, one or two head groups, fp32
+with D = 64 (generic kernel) and bf16 with D = 128, the three tail readings,
+decode batches and prompts, and layer patterns with Reuse, Reindex,
+token-only Reindex, window-only layers and several Full layers; every
+fourth case draws int8 values in [-2, 2] so that scores tie often."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import compare_run
+from top_kv_selection_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+PATTERNS = [
+    ("full",),
+    ("full", "reuse"),
+    ("full", "reindex", "reuse"),
+    ("full", "reuse", "reindex_tokens", "reuse"),
+    ("swa", "full", "reuse"),
+    ("full", "reuse", "full", "reuse"),
+]
+
+
+def random_cfg(k: int):
+    rng = np.random.default_rng(9000 + k)
+    decode = bool(rng.integers(0, 2))
+    B = int(rng.choice([1, 2, 4, 8, 16]))
+    fp32 = rng.random() < 0.25
+    big = rng.random() < 0.15
+    ctx = int(rng.integers(60, 70000 if big else 20000)) if decode else int(rng.integers(20, 3000 if big else 900))
+    n_seq = int(rng.integers(1, 7)) if decode else int(rng.integers(1, 3))
+    P = int(rng.integers(1, min(400, 16384 // B) + 1))
+    K = int(rng.integers(0, min(P * B, 600) + 1))
+    layers = PATTERNS[int(rng.integers(0, len(PATTERNS)))]
+    # a window-only layer, or K = 0, needs a window (W = 0 is rejected there)
+    Wn = int(rng.integers(0 if K > 0 and "swa" not in layers else 1, 201))
+    return W.scaled(W.CONFIGS["decode_full_32k" if decode else "prefill_8k"],
+                    name=f"sweep{k}", n_seq=n_seq, ctx=ctx, block=B, pool=P, top_k=K, window=Wn,
+                    d_idx=int(rng.choice([32, 64])), n_heads=16 if fp32 else int(rng.choice([16, 32])),
+                    head_dim=64 if fp32 else 128, dtype="f32" if fp32 else "bf16", layers=layers,
+                    tail=int(rng.integers(0, 3)))
+
+
+@pytest.fixture(scope="module")
+def pipeline():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from top_kv_selection_amd import pipeline as pl
+    return pl
+
+
+@pytest.mark.parametrize("k", range(48))
+def test_random_configuration_matches_the_oracle(pipeline, k):
+    cfg = random_cfg(k)
+    ties = k % 4 == 3                      # narrow int8 draws: long runs of equal scores
+    print(f"case {cfg.name}: decode={cfg.decode} S={cfg.n_seq} T={cfg.ctx} B={cfg.block} P={cfg.pool} "
+          f"K={cfg.top_k} W={cfg.window} d={cfg.d_idx} H={cfg.n_heads} D={cfg.head_dim} {cfg.dtype} "
+          f"tail={cfg.tail} layers={cfg.layers} ties={ties}", flush=True)
+    wl = W.generate(cfg, seed=9000 + k, int_range=(-2, 2) if ties else (-127, 127))
+    dw = pipeline.upload(wl)
+    pipeline.build_cache(dw)
+    pipeline.run(dw)
+    torch.cuda.synchronize()
+    got = pipeline.outputs(dw)
+    ref = oracle.run_layers(wl)
+    compare_run(got, ref, cfg, what=cfg.name)
