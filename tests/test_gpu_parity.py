@@ -250,6 +250,24 @@ def test_prefill_window_layer_chunks_and_mixed_tiles(lib):
     check(lib, cfg, seed=35)
 
 
+def test_prefill_window_runs_of_tiles(lib):
+    """Enough window-layer tiles that each workgroup walks a run of them: a
+    tile continuing the previous one adds only its new rows to the ring; runs
+    cross the two head groups and the edges of three 1,501-token prompts,
+    where tiles mix sequences and the next tile is staged whole."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], n_seq=3, ctx=1501, pool=128, top_k=200, window=128, n_heads=32,
+                   layers=("full", "swa"))
+    check(lib, cfg, seed=38)
+
+
+def test_prefill_window_long_runs(lib):
+    """Two 9,001-token prompts: nine tiles per workgroup, more than one load of
+    query positions covers, so the run reloads them midway."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], n_seq=2, ctx=9001, pool=256, top_k=128, window=64,
+                   layers=("full", "swa"))
+    check(lib, cfg, seed=39)
+
+
 def test_token_only_reindex_decode(lib):
     """A token-only Reindex group reads the Full group's pool and writes its
     own Top-K; the Reuse layer after it takes those indices."""
