@@ -138,6 +138,31 @@ int32_t csa2_workspace_init(void *ws, size_t bytes, void *stream);
 int32_t csa2_build_block_keys(const csa2_cfg *cfg, const int8_t *k_idx, int32_t n_seq, int32_t T,
                               int32_t blk_begin, int32_t blk_end, int8_t *k_blk, void *stream);
 
+/* Token append: the cache write before a Full layer's step ("CSA2 with
+ * cross-layer reuse" mode table: a Full layer computes its own main KV and
+ * indexer keys, which later layers of its group reuse).  For each new token
+ * i < n_new, with s = seq[i] and t = pos[i] (0 <= s < n_seq, 0 <= t < T):
+ *     k_idx[s][t]  = new_k_idx[i]    (d_idx int8)
+ *     k_main[s][t] = new_k[i]        (head_dim elements of cfg->dtype)
+ *     v_main[s][t] = new_v[i]
+ * then, after every row of the call is written, for each token that completes
+ * its block ((t + 1) % B == 0) the key of that block j = t / B, as in
+ * csa2_build_block_keys (the "Hierarchical indexer" key fact's block level):
+ *     k_blk[s][j][c] = round_half_even(mean over p in [jB, jB+B) of k_idx[s][p][c])
+ *   seq, pos    : device int32 [n_new]; distinct (s, t) pairs (two new rows
+ *                 for one position race); values trusted like q_seq/q_pos
+ *   new_k_idx   : device int8 [n_new][d_idx], 16-byte aligned
+ *   new_k/new_v : device [n_new][head_dim] of cfg->dtype, 16-byte aligned
+ *   k_idx       : device int8 [n_seq][T][d_idx]         (in/out)
+ *   k_main/v_main : device [n_seq][T][head_dim]         (in/out)
+ *   k_blk       : device int8 [n_seq][T/B][d_idx], or NULL to leave block keys
+ *                 to a later csa2_build_block_keys / Full layer group
+ * n_new = 0 launches nothing and accepts empty (NULL) arrays.  No workspace. */
+int32_t csa2_append_tokens(const csa2_cfg *cfg, int32_t n_new, const int32_t *seq, const int32_t *pos,
+                           const int8_t *new_k_idx, const void *new_k, const void *new_v, int8_t *k_idx,
+                           void *k_main, void *v_main, int8_t *k_blk, int32_t n_seq, int32_t T,
+                           void *stream);
+
 /* Hierarchical block pass.  For query row i at position t = q_pos[i] in
  * sequence s = q_seq[i], the eligible blocks are j = 0 .. t/B (each holds at
  * least one visible token).  If there are at most P of them, all are pooled;

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("csa2_index_blocks", "csa2_topk_tokens", "csa2_attend", "csa2_attend_group",
-              "csa2_layer_group", "csa2_build_block_keys", "csa2_workspace_bytes"):
+              "csa2_layer_group", "csa2_build_block_keys", "csa2_append_tokens", "csa2_workspace_bytes"):
         assert n in names
 
 
@@ -158,3 +158,26 @@ def test_reuse_and_attend_argument_errors(B):
     assert f(swa_first=-1) == 2
     assert f(swa_len=0) == 2
     assert f(out=FAKE + 8) == 5
+
+
+def test_append_argument_errors(B):
+    """Token append: missing or misaligned arrays and bad sizes fail before any
+    launch; an empty call succeeds whatever its pointers."""
+    cfg = B.Cfg()
+    P = ctypes.c_void_p
+    names = ("seq", "pos", "new_k_idx", "new_k", "new_v", "k_idx", "k_main", "v_main", "k_blk")
+    def f(n=4, S=2, T=64, **kw):
+        ptrs = [P(kw.get(k, FAKE)) for k in names]
+        return B._lib.csa2_append_tokens(ctypes.byref(cfg.c()), n, *ptrs, S, T, None)
+    assert f(seq=None) == 1
+    assert f(v_main=None) == 1
+    assert f(new_k=FAKE + 8) == 5
+    assert f(pos=FAKE + 2) == 5
+    assert f(k_blk=FAKE + 4) == 5
+    assert f(n=-1) == 2
+    assert f(T=0) == 2
+    assert f(S=0) == 2
+    assert f(n=0) == 0
+    assert f(n=0, seq=None, k_idx=None) == 0
+    bad = dataclasses.replace(cfg, d_idx=48)
+    assert B._lib.csa2_append_tokens(ctypes.byref(bad.c()), 4, *[P(FAKE)] * 9, 2, 64, None) == 4

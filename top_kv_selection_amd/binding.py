@@ -29,7 +29,7 @@ STATUS = {0: "CSA2_OK", 1: "CSA2_E_NULL", 2: "CSA2_E_SHAPE", 3: "CSA2_E_DTYPE",
           8: "CSA2_E_MODE"}
 
 EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_workspace_bytes", "csa2_workspace_init",
-           "csa2_build_block_keys", "csa2_index_blocks", "csa2_topk_tokens", "csa2_attend_group",
+           "csa2_build_block_keys", "csa2_append_tokens", "csa2_index_blocks", "csa2_topk_tokens", "csa2_attend_group",
            "csa2_attend", "csa2_layer_group"]
 
 
@@ -80,6 +80,7 @@ def _load():
         "csa2_workspace_bytes": (I, [C, I, I, I, ctypes.POINTER(ctypes.c_size_t)]),
         "csa2_workspace_init": (I, [P, Z, P]),
         "csa2_build_block_keys": (I, [C, P, I, I, I, I, P, P]),
+        "csa2_append_tokens": (I, [C, I, P, P, P, P, P, P, P, P, P, I, I, P]),
         "csa2_index_blocks": (I, [C, I, P, P, P, P, P, I, I, P, P, P, Z, P]),
         "csa2_topk_tokens": (I, [C, I, P, P, P, P, I, I, P, P, P, P, P, Z, P]),
         "csa2_attend_group": (I, [C, I, I, P, P, P, P, P, I, I, P, P, I, I, P, P, P, P, P, Z, P]),
@@ -159,6 +160,30 @@ def csa2_build_block_keys(cfg: Cfg, k_idx, k_blk, blk_begin=0, blk_end=None):
         blk_end = T // cfg.block
     _check("csa2_build_block_keys", _lib.csa2_build_block_keys(
         ctypes.byref(cfg.c()), _p(k_idx), S, T, blk_begin, blk_end, _p(k_blk), _stream(k_idx.device)))
+
+
+def csa2_append_tokens(cfg: Cfg, seq, pos, new_k_idx, new_k, new_v, k_idx, k_main, v_main, k_blk=None):
+    """Writes n_new tokens' rows into the caches; with k_blk, also the key of
+    every block a new token completes."""
+    for t, n, d in ((seq, "seq", torch.int32), (pos, "pos", torch.int32), (new_k_idx, "new_k_idx", torch.int8),
+                    (k_idx, "k_idx", torch.int8)):
+        _need(t, n, d)
+    for t, n in ((new_k, "new_k"), (new_v, "new_v"), (k_main, "k_main"), (v_main, "v_main")):
+        _need(t, n, cfg.torch_dtype)
+    if k_blk is not None:
+        _need(k_blk, "k_blk", torch.int8, 3)
+    S, T, _ = k_idx.shape
+    n_new = seq.shape[0]
+    if not (pos.shape[0] == new_k_idx.shape[0] == new_k.shape[0] == new_v.shape[0] == n_new):
+        raise ValueError("seq, pos, new_k_idx, new_k and new_v need one row per new token")
+    if (tuple(new_k_idx.shape[1:]) != (cfg.d_idx,) or tuple(new_k.shape[1:]) != (cfg.head_dim,)
+            or tuple(new_v.shape[1:]) != (cfg.head_dim,) or k_idx.shape[2] != cfg.d_idx
+            or tuple(k_main.shape) != (S, T, cfg.head_dim) or tuple(v_main.shape) != (S, T, cfg.head_dim)
+            or (k_blk is not None and tuple(k_blk.shape) != (S, T // cfg.block, cfg.d_idx))):
+        raise ValueError("cache or row shapes disagree with the config")
+    _check("csa2_append_tokens", _lib.csa2_append_tokens(
+        ctypes.byref(cfg.c()), n_new, _p(seq), _p(pos), _p(new_k_idx), _p(new_k), _p(new_v), _p(k_idx),
+        _p(k_main), _p(v_main), _p(k_blk), S, T, _stream(k_idx.device)))
 
 
 def csa2_index_blocks(cfg: Cfg, q_idx, q_seq, q_pos, k_idx, k_blk, blk_ids, blk_cnt, ws):

@@ -342,6 +342,25 @@ int32_t csa2_build_block_keys(const csa2_cfg *c, const int8_t *k_idx, int32_t n_
     return do_block_keys(c, k_idx, n_seq, T, blk_begin, blk_end, k_blk, (hipStream_t)stream, true);
 }
 
+int32_t csa2_append_tokens(const csa2_cfg *c, int32_t n_new, const int32_t *seq, const int32_t *pos,
+                           const int8_t *new_k_idx, const void *new_k, const void *new_v, int8_t *k_idx,
+                           void *k_main, void *v_main, int8_t *k_blk, int32_t n_seq, int32_t T, void *stream)
+{
+    if (int32_t e = check_cfg(c)) return e;
+    if (int32_t e = check_sizes(n_new, n_seq, T)) return e;
+    if (n_new == 0) return CSA2_OK;          // nothing to write (the arrays may be empty)
+    if (!seq || !pos || !new_k_idx || !new_k || !new_v || !k_idx || !k_main || !v_main) return CSA2_E_NULL;
+    if (!aligned4(seq) || !aligned4(pos) || !aligned16(new_k_idx) || !aligned16(new_k) || !aligned16(new_v) ||
+        !aligned16(k_idx) || !aligned16(k_main) || !aligned16(v_main) || (k_blk && !aligned16(k_blk)))
+        return CSA2_E_ALIGN;
+    AppendParams p{};
+    p.seq = seq; p.pos = pos; p.new_k_idx = new_k_idx; p.new_k = new_k; p.new_v = new_v;
+    p.k_idx = k_idx; p.k_main = k_main; p.v_main = v_main; p.k_blk = k_blk;
+    p.n_new = n_new; p.T = T; p.B = c->block; p.nblk = T / c->block; p.d_idx = c->d_idx;
+    p.row_bytes = c->head_dim * (c->dtype == CSA2_BF16 ? 2 : 4);
+    return hip_status(launch_append(p, (hipStream_t)stream));
+}
+
 
 int32_t csa2_index_blocks(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32_t *q_seq,
                           const int32_t *q_pos, const int8_t *k_idx, const int8_t *k_blk,

@@ -27,6 +27,17 @@ struct BlockKeysParams {
     int T, B, nblk, blk_begin, blk_end;
 };
 
+// New tokens written into the caches (row i: sequence seq[i], position pos[i]).
+struct AppendParams {
+    const int32_t *seq, *pos;
+    const int8_t *new_k_idx;
+    const void *new_k, *new_v;
+    int8_t *k_idx;
+    void *k_main, *v_main;
+    int8_t *k_blk;                 // nullptr: no block keys
+    int n_new, T, B, nblk, d_idx, row_bytes;
+};
+
 struct IndexParams {
     const int8_t *q_idx;
     const int32_t *q_seq, *q_pos;
@@ -107,6 +118,7 @@ SelectPlan plan_topk(int n_q, int T, int B, int P, int K, int d_idx);
 AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dtype);
 
 hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hipStream_t st);
+hipError_t launch_append(const AppendParams &p, hipStream_t st);
 hipError_t launch_index_blocks(const IndexParams &p, const SelectPlan &plan, int d_idx,
                                hipStream_t st, bool with_select = true);
 hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &plan, int d_idx, hipStream_t st);

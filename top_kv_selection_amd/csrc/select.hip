@@ -118,6 +118,41 @@ __global__ __launch_bounds__(256) void k_block_keys(BlockKeysParams p)
     *reinterpret_cast<int4 *>(p.k_blk + ((size_t)s * p.nblk + j) * DIDX + part * 16) = key;
 }
 
+// ---------------------------------------------------------------- token append
+// The rows of new tokens go to their cache positions: one workgroup of 64
+// threads per token, 16-byte pieces.  A second launch, after every row of the
+// call has landed, stores the key of each block a new token completes.
+__global__ __launch_bounds__(64) void k_append_rows(AppendParams p)
+{
+    const int i = blockIdx.x, lane = threadIdx.x;
+    const size_t row = (size_t)p.seq[i] * p.T + p.pos[i];
+    if (lane < p.d_idx / 16)
+        reinterpret_cast<int4 *>(p.k_idx + row * p.d_idx)[lane] =
+            reinterpret_cast<const int4 *>(p.new_k_idx + (size_t)i * p.d_idx)[lane];
+    const int pieces = p.row_bytes / 16;
+    const int4 *nk = reinterpret_cast<const int4 *>((const uint8_t *)p.new_k + (size_t)i * p.row_bytes);
+    const int4 *nv = reinterpret_cast<const int4 *>((const uint8_t *)p.new_v + (size_t)i * p.row_bytes);
+    int4 *k = reinterpret_cast<int4 *>((uint8_t *)p.k_main + row * p.row_bytes);
+    int4 *v = reinterpret_cast<int4 *>((uint8_t *)p.v_main + row * p.row_bytes);
+    for (int x = lane; x < pieces; x += 64) {
+        k[x] = nk[x];
+        v[x] = nv[x];
+    }
+}
+
+template <int DIDX>
+__global__ __launch_bounds__(64) void k_append_block_keys(AppendParams p)
+{
+    constexpr int LPR = DIDX / 16;
+    const int i = blockIdx.x * (64 / LPR) + threadIdx.x / LPR, part = threadIdx.x % LPR;
+    if (i >= p.n_new) return;
+    const int t = p.pos[i];
+    if ((t + 1) % p.B != 0) return;          // the token leaves its block incomplete
+    const int s = p.seq[i], j = t / p.B;
+    const int8_t *rows = p.k_idx + ((size_t)s * p.T + (size_t)j * p.B) * DIDX + part * 16;
+    *reinterpret_cast<int4 *>(p.k_blk + ((size_t)s * p.nblk + j) * DIDX + part * 16) = block_key_part<DIDX>(rows, p.B);
+}
+
 // ---------------------------------------------------------------- block pass
 // Scoring: thread group (DIDX/16 lanes) per block, U rows in flight per lane.
 // Every key also lands in a per-workgroup histogram of its top 11 bits; split
@@ -1018,6 +1053,19 @@ hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hip
     dim3 grid(ceil_div(n, 256), n_seq);
     if (d_idx == 64) hipLaunchKernelGGL(k_block_keys<64>, grid, dim3(256), 0, st, p);
     else hipLaunchKernelGGL(k_block_keys<32>, grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendParams &p, hipStream_t st)
+{
+    if (p.n_new <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_append_rows, dim3((unsigned)p.n_new), dim3(64), 0, st, p);
+    if (p.k_blk) {
+        const unsigned per = 64 / (p.d_idx / 16);   // tokens per workgroup
+        const dim3 grid((unsigned)((p.n_new + per - 1) / per));
+        if (p.d_idx == 64) hipLaunchKernelGGL(k_append_block_keys<64>, grid, dim3(64), 0, st, p);
+        else hipLaunchKernelGGL(k_append_block_keys<32>, grid, dim3(64), 0, st, p);
+    }
     return hipGetLastError();
 }
 
