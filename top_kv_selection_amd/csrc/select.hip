@@ -1,4 +1,5 @@
-// select.hip -- block keys, hierarchical block pass and token Top-K (gfx950).
+// select.hip -- block keys, token append, hierarchical block pass and token
+// Top-K (gfx950).
 //
 // The hierarchical indexer of the DeepSeek V4.1 Flash page (k-a.in,
 // "Hierarchical indexer": at most 16,384 candidates are scored whatever the
