@@ -190,7 +190,7 @@ FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
     f.tok = plan_topk(n_q, T, c->block, c->pool, c->top_k, c->d_idx);
     f.att = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
     f.ok = c->top_k >= 1 && f.idx.split && f.tok.split && n_elig_max <= kMaxCandidates && f.att.mfma && !f.att.rows &&
-           f.att.keys_per_split <= kAttendRowChunk && c->pool <= kFusedPoolLds;
+           (f.att.chunks || f.att.keys_per_split <= kAttendRowChunk) && c->pool <= kFusedPoolLds;
     f.blk_stride = (n_elig_max + 3) / 4 * 4;
     f.tok_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
     f.head = (size_t)n_q * 2048 * sizeof(uint32_t);

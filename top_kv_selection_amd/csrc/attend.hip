@@ -7,17 +7,20 @@
 // window K/V) while the main K/V and the indices may be shared by a group of
 // layers.
 //
-// Two kernels:
-//  * k_attend_mfma (bf16, D = 128, heads in groups of 16).  A wave takes 32
-//    keys per step: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (keys x heads),
-//    online softmax in fp32 (one head per lane column), then O^T += V^T P^T.
-//    K rows go straight from HBM into MFMA operands (16 B per lane, each row
-//    read once); V rows are written transposed into LDS so that the PV operand
-//    is two 8-byte LDS reads per lane.  One workgroup of 8 waves owns a
-//    (query, layer, head group) and a share of its key list; with few such
-//    triples (decode) the list is split over several workgroups that write
-//    (max, sum, acc) records, merged by k_attend_combine in a second launch.
-//  * k_attend_generic (fp32 or bf16, any H, D in {64, 128}): one wave per head,
+// Kernels, chosen by how many (query, layer, head group of 16) items a call
+// has (bf16, D = 128); all of them run S^T = K Q^T and O^T += V^T P^T on
+// v_mfma_f32_16x16x32_bf16 with 16 heads as the MFMA N dimension and an fp32
+// online softmax (one head per lane column):
+//  * k_attend_chunks + k_attend_combine (few items, as in decode): the key
+//    lists are cut into 64-key chunks taken by different workgroups; a main
+//    chunk's rows are brought into LDS once for every layer of a group; each
+//    (item, chunk) writes a (max, sum, acc) record and a second launch merges
+//    an item's records;
+//  * k_attend_mfma (a few hundred items): one workgroup of 8 waves per item;
+//  * k_attend_rows (many items, as in prefill): one wave per item;
+//  * k_attend_window (window-only layers with many queries): the windows of 8
+//    neighbouring queries staged in LDS once;
+//  * k_attend_generic (fp32, or any H and D in {64, 128}): one wave per head,
 //    keys in sequence, fp32 online softmax on the vector ALU.
 #include <math.h>
 
@@ -122,43 +125,37 @@ __global__ __launch_bounds__(256) void k_attend_generic(AttendParams p)
 // ============================================================ MFMA kernel
 constexpr int kWaves = 8;                      // waves per workgroup, 32 keys each per step
 constexpr int kStepKeys = kWaves * 32;         // keys per workgroup step (32 keys per wave)
-// With few (query, layer, head group) items the key list is split over
-// workgroups, and a workgroup's gather is bounded by what one CU keeps in
-// flight; waves then take 16 keys per step (one QK tile), which doubles the
-// workgroups that share a key list and halves each one's gather.
-constexpr int kStepKeysHalf = kWaves * 16;
 constexpr int kRowChunk = kAttendRowChunk;     // row codes staged in LDS at once
-static_assert(kRowChunk % (kWaves * 64) == 0 && kRowChunk % kStepKeys == 0 && kRowChunk % kStepKeysHalf == 0,
-              "whole staging rounds and steps");
+static_assert(kRowChunk % (kWaves * 64) == 0 && kRowChunk % kStepKeys == 0, "whole staging rounds and steps");
 constexpr int kVtStride = 40;                  // bf16 per V^T row in LDS (32 keys + pad)
 // After the key loop a wave's V^T buffer holds its partial output, 16 heads x
 // kObStride floats: with 144 floats per head, the 16-byte writes of a wave
 // (lane -> head r16, dims 16m + 4g) cover every bank equally.
 constexpr int kObStride = 144;
 static_assert(16 * kObStride * 4 <= 128 * kVtStride * 2, "a wave's partial output fits its V^T buffer");
-constexpr int kHeadRec = 4 + 128;              // split record per head: max, sum, 2 pad, acc[128]
-constexpr int kPartFloats = 16 * kHeadRec;     // one split record (16 heads), 16-byte aligned
-constexpr int kMergeBatch = 8;                 // split records loaded at once by the merge
+constexpr int kHeadRec = 4 + 128;              // chunk record per head: max, sum, 2 pad, acc[128]
+constexpr int kPartFloats = 16 * kHeadRec;     // one chunk record (16 heads), 16-byte aligned
+constexpr int kMergeBatch = 16;                // chunk records loaded at once by the merge
 
 // Key slot e (0..7) of lane group g inside a 32-key step: the keys whose
 // scores this lane holds after the QK MFMA (rows 4g..4g+3 of tile 0 and of
 // tile 1).  Both PV operands use this same order along the contraction.
 __device__ __forceinline__ int slot_key(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
 
-// One workgroup per (query, split of the key list, head group of 16, layer);
-// with several splits each writes a (max, sum, acc) record that
-// k_attend_combine merges.  KPW keys per wave and step (32, or 16 when lists
-// are split).  Workgroups are numbered query-fastest with the query count
-// padded to a multiple of 8, so with round-robin XCD dispatch every layer of
-// a query runs on one XCD and the shared main rows are fetched from HBM once
-// and then hit that XCD's L2.  FUSED: the token Top-K is taken first, from
-// the token keys and histogram (layer-group decode).
-template <bool FUSED, int KPW>
+// One workgroup per (query, head group of 16, layer), walking the whole key
+// list.  K rows go straight from memory into the MFMA A operand (16 B per
+// lane, each row read once); V rows are written transposed into LDS so that
+// the PV operand is two 8-byte LDS reads per lane.  Workgroups are numbered
+// query-fastest with the query count padded to a multiple of 8, so with
+// round-robin XCD dispatch every layer of a query runs on one XCD and the
+// shared main rows are fetched from HBM once and then hit that XCD's L2.
+// FUSED: the token Top-K is taken first, from the token keys and histogram
+// (layer-group decode).
+template <bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
 {
-    static_assert(KPW == 16 || KPW == 32, "one or two QK tiles per wave and step");
     constexpr int NT = kWaves * 64, IPT = kLdsKeys / NT;
-    constexpr int NTAU = KPW / 16, STEP = kWaves * KPW;
+    constexpr int KPW = 32, NTAU = 2, STEP = kWaves * KPW;   // keys per wave and step: two QK tiles
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[kWaves][128 * kVtStride];
     __shared__ float s_ml[kWaves][16][2];
     __shared__ int s_rows[kRowChunk];
@@ -170,9 +167,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
     const int HG = p.H / 16;
     const int id = blockIdx.x;
     const int i = id % p.n_q_pad;
-    int rest = id / p.n_q_pad;
-    const int split = rest % p.n_splits;
-    rest /= p.n_splits;
+    const int rest = id / p.n_q_pad;
     const int hg = rest % HG;
     const int l = rest / HG;
     if (i >= p.n_q) return;
@@ -205,29 +200,25 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         hist_to_lds<NT>(hr, s_hist);
         const int n_cand = n_pool * B;
         // The selection's size is known from the histogram (bin 0 holds the
-        // positions past t), so the window codes of this workgroup's slots,
-        // and the padding past the list when it ends with a window key, are
-        // written now, off the selection's critical path.
+        // positions past t), so the window codes, and the padding past the
+        // list when it ends with a window key, are written now, off the
+        // selection's critical path.
         {
             const int cnt_pre = min(p.K, n_cand - (int)s_hist[0]);
-            const int nk = cnt_pre + win.nw;
-            const int kb = min(nk, split * p.keys_per_split), ke = min(nk, kb + p.keys_per_split);
+            const int ke = min(cnt_pre + win.nw, p.keys_per_split);
             for (int x = threadIdx.x; x < p.keys_per_split; x += NT) {
-                const int kk = kb + x;
-                if (kk >= cnt_pre && kk < ke) s_rows[x] = -(win.w0 + (kk - cnt_pre) - p.swa_first) - 1;
-                else if (kk >= ke && ke > kb && win.nw > 0) s_rows[x] = -(win.w0 + (ke - 1 - cnt_pre) - p.swa_first) - 1;
+                if (x >= cnt_pre && x < ke) s_rows[x] = -(win.w0 + (x - cnt_pre) - p.swa_first) - 1;
+                else if (x >= ke && ke > 0 && win.nw > 0) s_rows[x] = -(win.w0 + (ke - 1 - cnt_pre) - p.swa_first) - 1;
             }
         }
         mask_keys<IPT>(n_cand, k);
         const Threshold th = threshold_regs<NT, IPT>(k, n_cand, (uint32_t)p.K, s_hist, s_sm);
-        const bool writer = (l == 0 && hg == 0 && split == 0);
+        const bool writer = (l == 0 && hg == 0);
         int32_t *out_tk = p.topk_out + (size_t)i * p.K;
-        const int kb0 = split * p.keys_per_split;
         auto emit = [&](uint32_t slot, int c) {
             const int r = c / B;
             const int pos = s_pool[r] * B + (c - r * B);
-            const int x = (int)slot - kb0;
-            if (x >= 0 && x < p.keys_per_split) s_rows[x] = pos;
+            if ((int)slot < p.keys_per_split) s_rows[slot] = pos;
             if (writer && (int)slot < p.K) out_tk[slot] = pos;
         };
         cnt = (int)compact_regs<NT, IPT>(k, th, emit, s_sm);
@@ -241,9 +232,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         cnt = p.topk ? p.topk_cnt[i] : 0;
     }
     const int n_keys = cnt + win.nw;
-    // this workgroup's share of the key list (whole steps of STEP keys)
-    const int k_begin = min(n_keys, split * p.keys_per_split);
-    const int k_end = min(n_keys, k_begin + p.keys_per_split);
+    const int k_begin = 0;
+    const int k_end = min(n_keys, p.keys_per_split);
 
     const uint16_t *qrow = (const uint16_t *)p.q + (((size_t)l * p.n_q + i) * p.H + hg * 16 + r16) * 128;
     const uint16_t *kmain = (const uint16_t *)p.k_main + (size_t)s * p.T * 128;
@@ -440,17 +430,6 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
         o[0] += f * v.x; o[1] += f * v.y; o[2] += f * v.z; o[3] += f * v.w;
     }
     const size_t row_id = ((size_t)l * p.n_q + i) * p.H + hg * 16 + hh;
-    if (p.n_splits > 1) {
-        // this split's (max, sum, acc) record; k_attend_combine merges them
-        const size_t rec0 = (((size_t)l * p.n_q + i) * HG + hg) * p.n_splits;
-        float *rec = p.ws_part + (rec0 + split) * kPartFloats + hh * kHeadRec;
-        if ((threadIdx.x & 31) == 0) {
-            rec[0] = M;
-            rec[1] = L;
-        }
-        *reinterpret_cast<float4 *>(rec + 4 + d0) = make_float4(o[0], o[1], o[2], o[3]);
-        return;
-    }
     const float inv = 1.f / L;
     const uint32_t lo = (uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
@@ -458,15 +437,20 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
     if (p.lse && (threadIdx.x & 31) == 0) p.lse[row_id] = (M + log2f(L)) * kLn2;
 }
 
-// Merge of the split records of one (query, layer, head group): thread ->
-// (head, 4 dims); all records' loads are issued before use.
-__global__ __launch_bounds__(512) void k_attend_combine(AttendParams p)
+// Merge of the chunk records of one (query, layer, head group): one
+// workgroup per pair of heads, thread -> (head, 4 dims), so that the records
+// (16 heads x 132 floats each) are read by many CUs at once; every record's
+// loads of a batch are issued before use.
+constexpr int kCombineHeads = 2;   // heads per combine workgroup
+__global__ __launch_bounds__(32 * kCombineHeads) void k_attend_combine(AttendParams p)
 {
     const int HG = p.H / 16;
-    const int i = blockIdx.x % p.n_q;
-    const int rest = blockIdx.x / p.n_q;
+    const int hq = blockIdx.x % (16 / kCombineHeads);
+    const int row = blockIdx.x / (16 / kCombineHeads);
+    const int i = row % p.n_q;
+    const int rest = row / p.n_q;
     const int hg = rest % HG, l = rest / HG;
-    const int hh = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 4;
+    const int hh = hq * kCombineHeads + (int)(threadIdx.x >> 5), d0 = (threadIdx.x & 31) * 4;
     const size_t rec0 = (((size_t)l * p.n_q + i) * HG + hg) * p.n_splits;
     float M = -INFINITY, L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < p.n_splits; c0 += kMergeBatch) {
@@ -739,6 +723,226 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
         *reinterpret_cast<uint2 *>(orow + 16 * m + 4 * g) = make_uint2(lo, hi);
     }
     if (p.lse && g == 0) p.lse[row_id] = (m_run + log2f(L)) * kLn2;
+}
+
+// ============================================================ chunk kernel
+// Few (query, layer, head group) items, as in decode: the key lists are cut
+// into chunks of kCkKeys keys taken by different workgroups, so the gather is
+// spread over the chip (a CU keeps only a few tens of KB of loads in flight,
+// so what one workgroup gathers sets its time).  A chunk of the main (Top-K)
+// list serves every layer of the group: its workgroup brings the chunk's K and
+// V rows into LDS once, and each wave runs one (layer, head group) item over
+// them, with the row kernel's operand reads (K in the A layout, V^T by the
+// transposing read).  Window chunks belong to one layer.  Each (item, chunk)
+// writes a (max, sum, acc) record; k_attend_combine merges an item's records.
+// FUSED (layer-group decode): the main-chunk workgroups first take the token
+// Top-K from the token keys and histogram, and the workgroup of chunk 0 writes
+// it; window-chunk workgroups need no selection and start at once.
+// Workgroups: main chunks (query fastest, the query count padded to 8, so the
+// chunks of a query, which load the same token keys, share one XCD), then
+// window chunks.
+constexpr int kCkWaves = 16;
+constexpr int kCkTiles = 2;                   // 32-key tiles per chunk
+constexpr int kCkKeys = 32 * kCkTiles;        // keys per chunk
+static_assert(kCkKeys * 16 == kCkWaves * 64, "one 16-byte K piece and one V piece per thread");
+
+template <bool FUSED>
+__global__ __launch_bounds__(kCkWaves * 64) void k_attend_chunks(AttendParams p)
+{
+    constexpr int NT = kCkWaves * 64, IPT = kLdsKeys / NT;
+    __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kCkTiles][2][kTileBytes];   // K, V
+    __shared__ int s_rows[kCkKeys];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[FUSED ? kHist2Words : 4];
+    __shared__ int32_t s_pool[FUSED ? kFusedPoolLds : 4];
+    static_assert(!FUSED || kFusedPoolLds % NT == 0, "whole pool loads per thread");
+    __shared__ uint32_t s_sm[NT / 64 + 4];
+
+    const int HG = p.H / 16;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+    const int n_main_wg = p.n_q_pad * p.n_mc;
+    const bool is_main = (int)blockIdx.x < n_main_wg;
+    int i, c, lw = 0;
+    if (is_main) {
+        i = blockIdx.x % p.n_q_pad;
+        c = blockIdx.x / p.n_q_pad;
+    } else {
+        const int b = blockIdx.x - n_main_wg;
+        i = b % p.n_q_pad;
+        c = (b / p.n_q_pad) % p.n_wc;
+        lw = (b / p.n_q_pad) / p.n_wc;
+    }
+    if (i >= p.n_q) return;   // whole workgroup
+    const int s = p.q_seq[i], t = p.q_pos[i];
+    const Window win = window_of(t, p.W, p.swa_first, p.swa_len);
+    const int n_items = is_main ? p.n_layers * HG : HG;
+    const int split = is_main ? c : p.n_mc + c;
+    // item j: (layer, head group) = (j / HG, j % HG) for a main chunk, (lw, j) for a window chunk
+    auto item_q = [&](int j, bf16x8_t (&qb)[4]) {
+        const int l = is_main ? j / HG : lw, hg = is_main ? j % HG : j;
+        const uint16_t *qrow = (const uint16_t *)p.q + (((size_t)l * p.n_q + i) * p.H + hg * 16 + r16) * 128;
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) qb[kk] = *reinterpret_cast<const bf16x8_t *>(qrow + kk * 32 + g * 8);
+    };
+    // this wave's first item's Q is loaded before anything else waits
+    bf16x8_t qb[4];
+    if (w < n_items) item_q(w, qb);
+
+    int n_valid;   // keys of this chunk
+    if (is_main) {
+        int cnt;
+        if constexpr (FUSED) {
+            HistRegs<NT> hr;
+            load_hist<NT>(p.sel_hist + (size_t)i * kRadixBins, hr);
+            uint32_t k[IPT];
+            load_keys_global<IPT>(p.sel_keys + (size_t)i * p.sel_stride, (int)p.sel_stride, k);
+            constexpr int PPT = kFusedPoolLds / NT;
+            int32_t pv[PPT];
+#pragma unroll
+            for (int u = 0; u < PPT; u++) {
+                const int r = u * NT + (int)threadIdx.x;
+                pv[u] = (r < p.sel_P) ? p.sel_pool[(size_t)i * p.sel_P + r] : -1;
+            }
+            const int n_pool = p.sel_pool_cnt[i];
+            const int B = p.sel_B;
+#pragma unroll
+            for (int u = 0; u < PPT; u++) s_pool[u * NT + threadIdx.x] = pv[u];
+            hist_to_lds<NT>(hr, s_hist);
+            const int n_cand = n_pool * B;
+            mask_keys<IPT>(n_cand, k);
+            const Threshold th = threshold_regs<NT, IPT>(k, n_cand, (uint32_t)p.K, s_hist, s_sm);
+            // each main chunk writes its own slots of topk (and their -1
+            // padding), so only this chunk's keys look up their positions
+            int32_t *out_tk = p.topk_out + (size_t)i * p.K;
+            const int kb0 = c * kCkKeys;
+            auto emit = [&](uint32_t slot, int cc) {
+                const int x = (int)slot - kb0;
+                if (x >= 0 && x < kCkKeys) {
+                    const int r = cc / B;
+                    const int pos = s_pool[r] * B + (cc - r * B);
+                    s_rows[x] = pos;
+                    out_tk[slot] = pos;
+                }
+            };
+            cnt = (int)compact_regs<NT, IPT>(k, th, emit, s_sm);
+            for (int o = max(cnt, kb0) + (int)threadIdx.x; o < min(p.K, kb0 + kCkKeys); o += NT) out_tk[o] = -1;
+            if (c == 0) {
+                if (threadIdx.x == 0) p.topk_cnt_out[i] = cnt;
+                if (p.blk_hist_clear)
+                    for (int b = threadIdx.x; b < kRadixBins; b += NT) p.blk_hist_clear[(size_t)i * kRadixBins + b] = 0u;
+            }
+            n_valid = min(max(cnt - c * kCkKeys, 0), kCkKeys);
+            lds_barrier();
+        } else {
+            cnt = p.topk_cnt[i];
+            n_valid = min(max(cnt - c * kCkKeys, 0), kCkKeys);
+            if (threadIdx.x < kCkKeys && n_valid > 0)
+                s_rows[threadIdx.x] = p.topk[(size_t)i * p.K + c * kCkKeys + min((int)threadIdx.x, n_valid - 1)];
+            lds_barrier();
+        }
+    } else {
+        n_valid = min(max(win.nw - c * kCkKeys, 0), kCkKeys);
+    }
+
+    // ---- the chunk's K and V rows into the tiles: thread -> (slot, 16-byte
+    // piece); slots past the chunk's keys repeat its last key (masked later)
+    if (n_valid > 0) {
+        const int slot = threadIdx.x >> 4, part = threadIdx.x & 15;
+        const int sl = min(slot, n_valid - 1);
+        const uint16_t *krow, *vrow;
+        if (is_main) {
+            const size_t r = (size_t)s * p.T + s_rows[sl];
+            krow = (const uint16_t *)p.k_main + r * 128;
+            vrow = (const uint16_t *)p.v_main + r * 128;
+        } else {
+            const size_t r = ((size_t)lw * p.n_seq + s) * p.swa_len + (win.w0 - p.swa_first) + c * kCkKeys + sl;
+            krow = (const uint16_t *)p.k_swa + r * 128;
+            vrow = (const uint16_t *)p.v_swa + r * 128;
+        }
+        const uint4 kv = *reinterpret_cast<const uint4 *>(krow + part * 8);
+        const uint4 vv = *reinterpret_cast<const uint4 *>(vrow + part * 8);
+        const int tau = slot >> 5, rr = slot & 31;
+        const int off = kTileInst * (rr & 7) + 256 * (rr >> 3) + 16 * part;
+        *reinterpret_cast<uint4 *>(&s_tiles[tau][0][off]) = kv;
+        *reinterpret_cast<uint4 *>(&s_tiles[tau][1][off]) = vv;
+    }
+    lds_barrier();
+
+    // ---- each wave: its items over the chunk's tiles
+    //   K, A layout: tile row 16 h + r16, bytes 64 kk + 16 g
+    const int ka_off = kTileInst * (r16 & 7) + 256 * (r16 >> 3) + 16 * g;
+    //   V^T via the transposing read: lane r16 of group g addresses tile row
+    //   16 h + 4 g + r16 / 4, dims 16 m + 4 (r16 % 4) .. +3
+    const int vr = 4 * g + (r16 >> 2);
+    const int va_off = kTileInst * (vr & 7) + 256 * (vr >> 3) + 8 * (r16 & 3);
+    for (int j = w; j < n_items; j += kCkWaves) {
+        if (j != w) item_q(j, qb);
+        const int l = is_main ? j / HG : lw, hg = is_main ? j % HG : j;
+        float m_run = -INFINITY, l_part = 0.f;
+        f32x4_t acc[8];
+#pragma unroll
+        for (int m = 0; m < 8; m++) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tau = 0; tau < kCkTiles; tau++) {
+            const int nv = n_valid - 32 * tau;   // keys in this tile (uniform)
+            if (nv <= 0) break;
+            const uint8_t *kt = s_tiles[tau][0], *vt = s_tiles[tau][1];
+            bf16x8_t ka[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+#pragma unroll
+                for (int kk = 0; kk < 4; kk++)
+                    ka[h][kk] = *reinterpret_cast<const bf16x8_t *>(kt + ka_off + 512 * h + 64 * kk);
+            f32x4_t sk[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+                for (int h = 0; h < 2; h++)
+                    sk[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][kk], qb[kk], sk[h], 0, 0, 0);
+            // lane holds keys 4g+ii (tile half 0) and 16+4g+ii (half 1) of head r16
+            float sc[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                sc[e] = sk[e >> 2][e & 3] * p.scale_log2;
+                if (slot_key(g, e) >= nv) sc[e] = -INFINITY;
+            }
+            const float mx = max_groups(fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                                              fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))));
+            const float m_new = fmaxf(m_run, mx);      // finite: the tile has a key
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
+            l_part *= alpha;
+#pragma unroll
+            for (int m = 0; m < 8; m++) acc[m] *= alpha;
+            m_run = m_new;
+            bf16x8_t pb;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float pr = __builtin_amdgcn_exp2f(sc[e] - m_run);
+                l_part += pr;
+                pb[e] = (__bf16)pr;
+            }
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(vt + va_off + 32 * m));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(vt + va_off + 512 + 32 * m));
+                const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                           __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u), pb, acc[m], 0, 0, 0);
+            }
+        }
+        // the record of (item, chunk): per head max and sum (log2 domain) and
+        // the unnormalised acc; an empty chunk writes (-inf, 0, 0)
+        const float L = sum_groups(l_part);
+        const size_t rec0 = (((size_t)l * p.n_q + i) * HG + hg) * p.n_splits;
+        float *rec = p.ws_part + (rec0 + split) * kPartFloats + r16 * kHeadRec;
+#pragma unroll
+        for (int m = 0; m < 8; m++)
+            *reinterpret_cast<float4 *>(rec + 4 + 16 * m + 4 * g) = make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
+        if (g == 0) {
+            rec[0] = m_run;
+            rec[1] = L;
+        }
+    }
 }
 
 // ============================================================ window kernel
@@ -1017,27 +1221,24 @@ static int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b);
 
 AttendPlan plan_attend(int n_q, int n_layers, int H, int D, int K, int W, int dtype)
 {
-    AttendPlan pl{(dtype == 1) && (D == 128) && (H % 16 == 0), false, 1, 0, 0, 32};
+    AttendPlan pl{(dtype == 1) && (D == 128) && (H % 16 == 0), false, 1, 0, 0, 32, false, 0, 0};
     if (!pl.mfma) return pl;
-    // Split a key list over several workgroups only when there are too few
-    // (query, layer, head group) triples to spread the gather over the chip;
-    // each split then costs a device-scope merge.  Split lists are walked
-    // with 16-key waves (twice the workgroups, half the gather each).
     const long long base = (long long)n_q * n_layers * (H / 16);
-    const bool split_regime = base < kTargetWorkgroups / 2;
-    pl.kpw = split_regime ? 16 : 32;
-    const int step = split_regime ? kStepKeysHalf : kStepKeys;
-    const int steps = std::max(1, (K + W + step - 1) / step);
-    int n_splits = 1;
-    if (split_regime) n_splits = (int)std::min<long long>(steps, (kTargetWorkgroups + base - 1) / base);
-    const int steps_per_split = (steps + n_splits - 1) / n_splits;
-    n_splits = (steps + steps_per_split - 1) / steps_per_split;
-    pl.n_splits = n_splits;
-    pl.keys_per_split = steps_per_split * step;
-    pl.part_bytes = n_splits > 1 ? (size_t)base * n_splits * kPartFloats * sizeof(float) : 0;
-    // enough items for one wave each to fill the chip (never split then): the
-    // row kernel, when the row tables fit its 32-bit buffer offsets
-    pl.rows = base >= kRowItemsMin && n_splits == 1;
+    if (base < kTargetWorkgroups / 2) {
+        // too few (query, layer, head group) items to spread the gather over
+        // the chip: cut the key lists into chunks, one workgroup each, and
+        // merge each item's chunk records
+        pl.chunks = true;
+        pl.n_mc = (K + kCkKeys - 1) / kCkKeys;
+        pl.n_wc = (W + kCkKeys - 1) / kCkKeys;
+        pl.n_splits = pl.n_mc + pl.n_wc;
+        pl.part_bytes = (size_t)base * pl.n_splits * kPartFloats * sizeof(float);
+        return pl;
+    }
+    const int steps = std::max(1, (K + W + kStepKeys - 1) / kStepKeys);
+    pl.keys_per_split = steps * kStepKeys;
+    // enough items for one wave each to fill the chip: the row kernel
+    pl.rows = base >= kRowItemsMin;
     return pl;
 }
 
@@ -1059,22 +1260,26 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
         hipLaunchKernelGGL(k_attend_rows, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kRowWaves * 64), 0, st, p);
         return hipGetLastError();
     }
+    if (pl.chunks) {
+        p.n_q_pad = (p.n_q + 7) / 8 * 8;
+        p.n_mc = (fused_select || p.topk != nullptr) ? pl.n_mc : 0;
+        p.n_wc = pl.n_wc;
+        p.n_splits = p.n_mc + p.n_wc;
+        const long long n_wg = (long long)p.n_q_pad * (p.n_mc + (long long)p.n_layers * p.n_wc);
+        if (fused_select) hipLaunchKernelGGL(k_attend_chunks<true>, dim3((unsigned)n_wg), dim3(kCkWaves * 64), 0, st, p);
+        else hipLaunchKernelGGL(k_attend_chunks<false>, dim3((unsigned)n_wg), dim3(kCkWaves * 64), 0, st, p);
+        const long long n_rows = (long long)p.n_q * (p.H / 16) * p.n_layers;
+        hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(n_rows * (16 / kCombineHeads))),
+                           dim3(32 * kCombineHeads), 0, st, p);
+        return hipGetLastError();
+    }
     if (pl.mfma) {
         p.n_q_pad = (p.n_q + 7) / 8 * 8;
-        p.n_splits = pl.n_splits;
+        p.n_splits = 1;
         p.keys_per_split = pl.keys_per_split;
-        const long long n_wg = (long long)p.n_q_pad * pl.n_splits * (p.H / 16) * p.n_layers;
-        if (pl.kpw == 16) {
-            if (fused_select) hipLaunchKernelGGL((k_attend_mfma<true, 16>), dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
-            else hipLaunchKernelGGL((k_attend_mfma<false, 16>), dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
-        } else {
-            if (fused_select) hipLaunchKernelGGL((k_attend_mfma<true, 32>), dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
-            else hipLaunchKernelGGL((k_attend_mfma<false, 32>), dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
-        }
-        if (pl.n_splits > 1) {
-            const long long n_rows = (long long)p.n_q * (p.H / 16) * p.n_layers;
-            hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)n_rows), dim3(512), 0, st, p);
-        }
+        const long long n_wg = (long long)p.n_q_pad * (p.H / 16) * p.n_layers;
+        if (fused_select) hipLaunchKernelGGL(k_attend_mfma<true>, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+        else hipLaunchKernelGGL(k_attend_mfma<false>, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
         return hipGetLastError();
     }
     dim3 grid((unsigned)p.n_q, (unsigned)p.n_layers, (unsigned)ceil_div_i(p.H, 4));

@@ -77,7 +77,7 @@ struct AttendParams {
     float scale_log2;       // logit scale times log2(e)
     void *out;
     float *lse;
-    float *ws_part;         // split records (n_splits > 1)
+    float *ws_part;         // chunk records [L][n_q][H/16][n_splits] (chunk kernel)
     // fused token selection (layer-group decode path): the key list comes from
     // the token keys instead of topk, and topk/topk_cnt are written
     const uint32_t *sel_keys;   // [n_q][sel_stride] token keys
@@ -88,8 +88,10 @@ struct AttendParams {
     int sel_B, sel_P;
     int32_t *topk_out, *topk_cnt_out;
     uint32_t *blk_hist_clear;   // optional: [n_q][2048] histograms to zero once read
-    int n_splits, keys_per_split;
+    int n_splits;           // chunk kernel: records per item (main chunks + window chunks)
+    int keys_per_split;     // MFMA kernel: key-list slots staged (whole steps)
     int n_q_pad;            // n_q rounded up to a multiple of 8 (XCD-aware numbering)
+    int n_mc, n_wc;         // chunk kernel: main-list chunks per query, window chunks per (query, layer)
 };
 
 // Work split of one selection launch: G workgroups per query, `chunk` items each.
@@ -104,9 +106,11 @@ struct SelectPlan {
 struct AttendPlan {
     bool mfma;    // bf16, D = 128, H a multiple of 16: an MFMA kernel; else the generic one
     bool rows;    // many items: one wave per (query, layer, head group), no splits
-    int n_splits, keys_per_split;
+    int n_splits, keys_per_split;   // as in AttendParams
     size_t part_bytes;
-    int kpw;      // keys per wave and step of the MFMA kernel: 32, or 16 when a list is split
+    int kpw;      // keys per wave and step of the MFMA kernel
+    bool chunks;  // few items: key lists cut into chunks (k_attend_chunks + k_attend_combine)
+    int n_mc, n_wc;   // main-list chunks per query, window chunks per (query, layer)
 };
 
 // Workspace head bytes of a selection launch: one 2048-bin histogram per
