@@ -207,6 +207,22 @@ def test_flat_topk_blocks_of_one_token_prefill(lib):
     check(lib, cfg, seed=46)
 
 
+@pytest.mark.parametrize("B", [3, 5, 7, 12])
+def test_decode_block_sizes_not_a_power_of_two(lib, B):
+    """Blocks of 3 to 12 tokens in the decode layer group: each pool/token
+    scoring workgroup takes a whole number of pool slots, so its candidate
+    range is not a power of two; the query's own block is partial for most B."""
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=9001, block=B, pool=300, top_k=256, window=64,
+                   layers=("full", "reuse", "reuse"))
+    check(lib, cfg, seed=60 + B)
+
+
+def test_prefill_block_size_not_a_power_of_two(lib):
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=700, block=5, pool=40, top_k=64, window=32,
+                   layers=("full", "reuse"))
+    check(lib, cfg, seed=59)
+
+
 def test_prefill_dense_topk_two_sequences(lib):
     """Pool covering every block: the MFMA tile Top-K, with a workgroup tile
     that holds queries of both sequences (1,000 is not a multiple of 16)."""

@@ -449,18 +449,20 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
 }
 
 // Layer-group decode: the pool selection and the token scoring of a query in
-// one launch.  kPoolTokCand candidates per workgroup; every workgroup of a
+// one launch.  Each workgroup takes kPoolTokCand / B pool slots (at most
+// kPoolTokCand candidates); every workgroup of a
 // query first redoes the exact pool selection of k_index_select from the
-// block keys and histogram that the split k_index_blocks launch wrote
-// (workgroup 0 also writes blk_ids / blk_cnt), keeps the pool in LDS, and
-// then scores its candidates like a split k_topk_tokens launch (token keys
-// and the token histogram go to the workspace).  The selection is repeated
+// block keys and histogram that the split k_index_blocks launch wrote, keeps
+// the pool slots its candidates come from (kPoolTokCand / B of them) in LDS
+// and writes them to blk_ids (workgroup 0 also writes blk_cnt), and then
+// scores its candidates like a split k_topk_tokens launch (token keys and the
+// token histogram go to the workspace).  The selection is repeated
 // P*B / kPoolTokCand times per query, but the launch boundary and the round
 // trip of the pool through global memory are gone.  The block histogram is
 // left as read; the caller's next launch zeroes it.  Workgroups are numbered
 // query-fastest over n_q rounded up to 8, so a query's workgroups share one
 // XCD's L2 (round-robin dispatch) and read its block keys from HBM once.
-constexpr int kPoolTokCand = 1024;
+constexpr int kPoolTokCand = 512;
 
 template <int DIDX>
 __global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams ip, TopkParams tp, int n_q_pad)
@@ -485,27 +487,27 @@ __global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams 
     const int s = ip.q_seq[q], t = ip.q_pos[q];
     const int n_elig = eligible_blocks(t, B, ip.tail);
     hist_to_lds<NT>(hr, s_hist);
+    // this workgroup's pool slots [s0, s0 + n_slots): s_pool[x] holds slot s0 + x
+    const int n_slots = kPoolTokCand / B, s0 = g * n_slots;
     int n_pool;
     if (n_elig <= P) {   // the pool is every eligible block (k_index_blocks wrote it)
-        for (int r = tid; r < n_elig; r += NT) s_pool[r] = r;
+        for (int x = tid; x < n_slots; x += NT) s_pool[x] = s0 + x;
         n_pool = n_elig;
     } else {
         mask_keys<IPT>(n_elig, k);
         const Threshold th = threshold_regs<NT, IPT>(k, n_elig, (uint32_t)P, s_hist, s_sm);
         int32_t *ids = ip.blk_ids + (size_t)q * P;
-        const bool writer = g == 0;
         auto emit = [&](uint32_t slot, int i) {
-            if (slot < (uint32_t)P) {
-                s_pool[slot] = i;
-                if (writer) ids[slot] = i;
+            const int x = (int)slot - s0;
+            if (x >= 0 && x < n_slots && (int)slot < P) {
+                s_pool[x] = i;
+                ids[slot] = i;
             }
         };
         const uint32_t chosen = compact_regs<NT, IPT>(k, th, emit, s_sm);
         n_pool = (int)min(chosen, (uint32_t)P);
-        if (writer) {
-            for (int o = n_pool + tid; o < P; o += NT) ids[o] = -1;
-            if (tid == 0) ip.blk_cnt[q] = n_pool;
-        }
+        for (int o = max(n_pool, s0) + tid; o < min(P, s0 + n_slots); o += NT) ids[o] = -1;
+        if (g == 0 && tid == 0) ip.blk_cnt[q] = n_pool;
     }
     // the pool is complete once this barrier is passed; the histogram memory
     // is free again and counts this workgroup's token keys
@@ -513,7 +515,7 @@ __global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams 
     for (int b = tid; b < kHistWords; b += NT) s_hist[b] = 0;
 
     const int n_cand = n_pool * B;
-    const int lo = g * kPoolTokCand, hi = min(n_cand, lo + kPoolTokCand);
+    const int lo = s0 * B, hi = min(n_cand, (s0 + n_slots) * B);
     uint32_t *gkeys = tp.ws_keys + (size_t)q * tp.ws_stride;
     const int8_t *seq_rows = tp.k_idx + (size_t)s * tp.T * DIDX + part * 16;
     for (int base = lo; base < hi; base += RPP * kUnroll) {
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams 
         for (int u = 0; u < kUnroll; u++) {
             const int c = base + u * RPP + tid / LPR;
             const int cl = min(c, hi - 1);
-            pos[u] = s_pool[cl / B] * B + cl % B;
+            pos[u] = s_pool[cl / B - s0] * B + cl % B;
             vis[u] = c < hi && pos[u] <= t;
             kv[u] = *reinterpret_cast<const int4 *>(seq_rows + (size_t)(vis[u] ? pos[u] : 0) * DIDX);
         }
@@ -1125,7 +1127,7 @@ hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &pl, int d_i
 
 int pool_tokens_groups(int P, int B)
 {
-    return ceil_div((long long)P * B, kPoolTokCand);
+    return ceil_div(P, kPoolTokCand / B);
 }
 
 hipError_t launch_pool_tokens(const IndexParams &ip, const TopkParams &tp, int d_idx, hipStream_t st)
