@@ -440,16 +440,18 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend_mfma(AttendParams p)
 // Merge of the chunk records of one (query, layer, head group): one
 // workgroup per pair of heads, thread -> (head, 4 dims), so that the records
 // (16 heads x 132 floats each) are read by many CUs at once; every record's
-// loads of a batch are issued before use.
+// loads of a batch are issued before use.  Workgroups are numbered
+// query-fastest over the query count padded to 8, as in k_attend_chunks, so
+// a query's records are read on the XCD that wrote them.
 constexpr int kCombineHeads = 2;   // heads per combine workgroup
 __global__ __launch_bounds__(32 * kCombineHeads) void k_attend_combine(AttendParams p)
 {
     const int HG = p.H / 16;
-    const int hq = blockIdx.x % (16 / kCombineHeads);
-    const int row = blockIdx.x / (16 / kCombineHeads);
-    const int i = row % p.n_q;
-    const int rest = row / p.n_q;
-    const int hg = rest % HG, l = rest / HG;
+    const int i = blockIdx.x % p.n_q_pad;
+    const int rest = blockIdx.x / p.n_q_pad;
+    const int hq = rest % (16 / kCombineHeads);
+    const int hg = (rest / (16 / kCombineHeads)) % HG, l = (rest / (16 / kCombineHeads)) / HG;
+    if (i >= p.n_q) return;
     const int hh = hq * kCombineHeads + (int)(threadIdx.x >> 5), d0 = (threadIdx.x & 31) * 4;
     const size_t rec0 = (((size_t)l * p.n_q + i) * HG + hg) * p.n_splits;
     float M = -INFINITY, L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1268,7 +1270,7 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
         const long long n_wg = (long long)p.n_q_pad * (p.n_mc + (long long)p.n_layers * p.n_wc);
         if (fused_select) hipLaunchKernelGGL(k_attend_chunks<true>, dim3((unsigned)n_wg), dim3(kCkWaves * 64), 0, st, p);
         else hipLaunchKernelGGL(k_attend_chunks<false>, dim3((unsigned)n_wg), dim3(kCkWaves * 64), 0, st, p);
-        const long long n_rows = (long long)p.n_q * (p.H / 16) * p.n_layers;
+        const long long n_rows = (long long)p.n_q_pad * (p.H / 16) * p.n_layers;
         hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(n_rows * (16 / kCombineHeads))),
                            dim3(32 * kCombineHeads), 0, st, p);
         return hipGetLastError();
