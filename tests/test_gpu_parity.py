@@ -446,6 +446,9 @@ def test_full_mode_stores_the_block_a_query_completes(lib):
     ("decode_full_32k", dict(n_seq=3, ctx=5001, pool=300, top_k=700, window=100)),
     ("decode_full_32k", dict(n_seq=2, ctx=900, pool=2048)),            # pool covers every block
     ("decode_group_128k", dict(n_seq=3, ctx=12000, pool=256, layers=("reindex", "reuse"))),
+    # 48 queries x 6 layers: enough items for one attention workgroup per
+    # (query, layer) instead of key-list chunks
+    ("decode_group_128k", dict(n_seq=48, ctx=3000, pool=128)),
 ])
 def test_fused_layer_group_equals_separate_calls(lib, name, kw):
     """The layer-group call (fused decode launches) and the separate calls
