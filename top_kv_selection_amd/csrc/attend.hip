@@ -738,8 +738,9 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
 // transposing read).  Window chunks belong to one layer.  Each (item, chunk)
 // writes a (max, sum, acc) record; k_attend_combine merges an item's records.
 // FUSED (layer-group decode): the main-chunk workgroups first take the token
-// Top-K from the token keys and histogram, and the workgroup of chunk 0 writes
-// it; window-chunk workgroups need no selection and start at once.
+// Top-K from the token keys and histogram, and each writes its own slots of
+// topk (chunk 0 also the count); window-chunk workgroups need no selection and
+// start at once.
 // Workgroups: main chunks (query fastest, the query count padded to 8, so the
 // chunks of a query, which load the same token keys, share one XCD), then
 // window chunks.
@@ -836,7 +837,7 @@ __global__ __launch_bounds__(kCkWaves * 64) void k_attend_chunks(AttendParams p)
             n_valid = min(max(cnt - c * kCkKeys, 0), kCkKeys);
             lds_barrier();
         } else {
-            cnt = p.topk_cnt[i];
+            cnt = min(p.topk_cnt[i], p.K);
             n_valid = min(max(cnt - c * kCkKeys, 0), kCkKeys);
             if (threadIdx.x < kCkKeys && n_valid > 0)
                 s_rows[threadIdx.x] = p.topk[(size_t)i * p.K + c * kCkKeys + min((int)threadIdx.x, n_valid - 1)];

@@ -263,6 +263,7 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
 // is needed.  A grid-stride kernel writes the ids (then -1 padding), 16 bytes
 // per store when the rows allow it, and the counts; a Full layer also stores
 // the key of the block its query completes.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPoolAllThreads = 256;
 constexpr int kPoolAllBlocks = 2048;
 
@@ -280,7 +281,11 @@ __global__ __launch_bounds__(kPoolAllThreads) void k_pool_all(IndexParams p)
             const int n = eligible_blocks(p.q_pos[q], p.B, p.tail);
             const int4 v = make_int4(j < n ? j : -1, j + 1 < n ? j + 1 : -1, j + 2 < n ? j + 2 : -1,
                                      j + 3 < n ? j + 3 : -1);
-            *reinterpret_cast<int4 *>(p.blk_ids + (size_t)q * p.P + j) = v;
+            // nontemporal: the ids are not read again in this step, and
+            // streaming them past the caches keeps the keys and K/V rows the
+            // following launches read resident
+            const i32x4 vn = {v.x, v.y, v.z, v.w};
+            __builtin_nontemporal_store(vn, reinterpret_cast<i32x4 *>(p.blk_ids + (size_t)q * p.P + j));
         }
     } else {
         const size_t total = (size_t)p.n_q * p.P;
