@@ -34,6 +34,15 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// A 16-byte load that streams past the caches: the many-query kernels read
+// each query row once, and keeping those rows out of L2 and the MALL leaves
+// room for the K/V rows that other workgroups gather again.
+typedef int i32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t load_nt_bf16x8(const uint16_t *src)
+{
+    return __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(reinterpret_cast<const i32x4_nt *>(src)));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
@@ -631,7 +640,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
 
     bf16x8_t qb[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) qb[kk] = *reinterpret_cast<const bf16x8_t *>(qrow + kk * 32 + g * 8);
+    for (int kk = 0; kk < 4; kk++) qb[kk] = load_nt_bf16x8(qrow + kk * 32 + g * 8);
 
     // operand addresses in the tiles (per lane; tau, kk, m, h are immediates)
     //   K, A layout: tile row 16 tau + r16, bytes 64 kk + 16 g
@@ -1053,7 +1062,7 @@ void k_attend_window(AttendParams p)
     auto begin = [&](State &st, int i) {
         const uint16_t *qrow = (const uint16_t *)p.q + (((size_t)l * p.n_q + i) * p.H + hg * 16 + r16) * 128;
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) st.qb[kk] = *reinterpret_cast<const bf16x8_t *>(qrow + kk * 32 + g * 8);
+        for (int kk = 0; kk < 4; kk++) st.qb[kk] = load_nt_bf16x8(qrow + kk * 32 + g * 8);
 #pragma unroll
         for (int m = 0; m < 8; m++) st.acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         st.m_run = -INFINITY;
