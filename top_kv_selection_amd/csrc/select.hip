@@ -169,8 +169,8 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     __shared__ uint32_t s_keys[SPLIT ? 4 : kLdsKeysPadded];
     __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
     __shared__ uint32_t s_sm[NT / 64 + 4];
-    const int q = blockIdx.x % p.n_q;
-    const int g = blockIdx.x / p.n_q;
+    const int q = blockIdx.x / p.G;   // a query's workgroups are consecutive: spread over the XCDs
+    const int g = blockIdx.x % p.G;
     const int tid = threadIdx.x, part = tid % LPR;
     const int s = p.q_seq[q], t = p.q_pos[q];
     const int jt = t / p.B, n_elig = eligible_blocks(t, p.B, p.tail);
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
     __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
     __shared__ int32_t s_pool[SPLIT ? 4 : kPoolLds];
     __shared__ uint32_t s_sm[NT / 64 + 4];
-    const int q = blockIdx.x % p.n_q;
+    const int q = blockIdx.x % p.n_q;   // query-fastest: k_topk_select reads a query's keys on its XCD
     const int g = blockIdx.x / p.n_q;
     const int tid = threadIdx.x, part = tid % LPR;
     const int s = p.q_seq[q], t = p.q_pos[q];
