@@ -136,9 +136,9 @@ constexpr int kAttendRowChunk = 2048;   // key-list entries one attention workgr
 constexpr int kFusedPoolLds = 2048;     // pooled block ids the fused attention keeps in LDS
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t st);
 // Layer-group decode: pool selection (from a split block pass's keys and
-// histogram) and token scoring in one launch; pool_tokens_groups workgroups
-// per query.  Requires n_elig_max <= kLdsKeys and P <= kFusedPoolLds.
-int pool_tokens_groups(int P, int B);
+// histogram) and token scoring in one launch; ceil(P / pool_tokens_slots)
+// workgroups per query.  Requires n_elig_max <= kLdsKeys and P <= kFusedPoolLds.
+int pool_tokens_slots(int n_q, int P, int B);
 hipError_t launch_pool_tokens(const IndexParams &ip, const TopkParams &tp, int d_idx, hipStream_t st);
 
 }  // namespace csa2

@@ -454,11 +454,12 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
 }
 
 // Layer-group decode: the pool selection and the token scoring of a query in
-// one launch.  Each workgroup takes kPoolTokCand / B pool slots (at most
-// kPoolTokCand candidates); every workgroup of a
+// one launch.  Each workgroup takes n_slots consecutive pool slots
+// (pool_tokens_slots: kPoolTokCand / B, or more when that many workgroups
+// would not all fit on the chip at once); every workgroup of a
 // query first redoes the exact pool selection of k_index_select from the
 // block keys and histogram that the split k_index_blocks launch wrote, keeps
-// the pool slots its candidates come from (kPoolTokCand / B of them) in LDS
+// the pool slots its candidates come from in LDS
 // and writes them to blk_ids (workgroup 0 also writes blk_cnt), and then
 // scores its candidates like a split k_topk_tokens launch (token keys and the
 // token histogram go to the workspace).  The selection is repeated
@@ -470,9 +471,10 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
 // workgroups on one XCD; the attention launch, whose workgroups share the
 // token keys, is the other way round).
 constexpr int kPoolTokCand = 512;
+constexpr int kPoolTokMaxWorkgroups = 256;   // one 1,024-thread workgroup per CU
 
 template <int DIDX>
-__global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams ip, TopkParams tp)
+__global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams ip, TopkParams tp, int n_slots)
 {
     constexpr int NT = kSelectWideThreads, IPT = kLdsKeys / NT;
     constexpr int LPR = DIDX / 16, RPP = NT / LPR;
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams 
     const int n_elig = eligible_blocks(t, B, ip.tail);
     hist_to_lds<NT>(hr, s_hist);
     // this workgroup's pool slots [s0, s0 + n_slots): s_pool[x] holds slot s0 + x
-    const int n_slots = kPoolTokCand / B, s0 = g * n_slots;
+    const int s0 = g * n_slots;
     int n_pool;
     if (n_elig <= P) {   // the pool is every eligible block (k_index_blocks wrote it)
         for (int x = tid; x < n_slots; x += NT) s_pool[x] = s0 + x;
@@ -1132,17 +1134,21 @@ hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &pl, int d_i
     return hipGetLastError();
 }
 
-int pool_tokens_groups(int P, int B)
+// Pool slots per workgroup of k_pool_tokens: kPoolTokCand candidates' worth,
+// or more, so that the launch needs no second round of workgroups.
+int pool_tokens_slots(int n_q, int P, int B)
 {
-    return ceil_div(P, kPoolTokCand / B);
+    const int per_query = std::max(1, kPoolTokMaxWorkgroups / std::max(n_q, 1));
+    return std::max(kPoolTokCand / B, ceil_div(P, per_query));
 }
 
 hipError_t launch_pool_tokens(const IndexParams &ip, const TopkParams &tp, int d_idx, hipStream_t st)
 {
     if (ip.n_q <= 0) return hipSuccess;
-    const dim3 grid((unsigned)(ip.n_q * pool_tokens_groups(ip.P, ip.B)));
-    if (d_idx == 64) hipLaunchKernelGGL(k_pool_tokens<64>, grid, dim3(kSelectWideThreads), 0, st, ip, tp);
-    else hipLaunchKernelGGL(k_pool_tokens<32>, grid, dim3(kSelectWideThreads), 0, st, ip, tp);
+    const int n_slots = pool_tokens_slots(ip.n_q, ip.P, ip.B);
+    const dim3 grid((unsigned)(ip.n_q * ceil_div(ip.P, n_slots)));
+    if (d_idx == 64) hipLaunchKernelGGL(k_pool_tokens<64>, grid, dim3(kSelectWideThreads), 0, st, ip, tp, n_slots);
+    else hipLaunchKernelGGL(k_pool_tokens<32>, grid, dim3(kSelectWideThreads), 0, st, ip, tp, n_slots);
     return hipGetLastError();
 }
 
