@@ -16,7 +16,9 @@ token-only Reindex layer (the page's Reindex "recomputes only the Top-K"
 reading) keeps the pool of the most recent index set and reselects the tokens
 with its own indexer query.
 Sliding-window-only layers (the page's first two encoder layers) attend to the
-window alone.
+window alone.  These sequencing rules are pinned by tests that recompute every
+layer of small multi-layer workloads from scratch (selection by enumeration,
+attention by fp64 SDPA over the gathered rows).
 """
 from __future__ import annotations
 

@@ -1,14 +1,19 @@
 """Planted mistakes in a copy of the oracle (CPU only) must each fail a pin.
 
-Each mutant is the oracle's C source with one plausible slip (a wrong rounding
-tie, a leaked future row, a flipped tie-break, an off-by-one window, a dropped
-scale, a wrong sign ...).  The copy is compiled to a temporary library and the
-pin suite is run against it; at least one pin must fail.  This shows the pins
-are strong enough to notice such a slip in the real oracle.
+Each C mutant is the oracle's C source with one plausible slip (a wrong
+rounding tie, a leaked future row, a flipped tie-break, an off-by-one window, a
+dropped scale, a wrong sign ...).  The copy is compiled to a temporary library
+and the pin suite is run against it; at least one pin must fail.  Each Python
+mutant is a copy of the oracle package's layer-mode rules (``run_layers``) with
+one slip (a Reindex layer that keeps the earlier indices, a window-only layer
+that also attends to the main set, every layer on the first cache ...), loaded
+as a module in place of the oracle for the pin suite.  This shows the pins are
+strong enough to notice such a slip in the real oracle.
 """
 import inspect
 import os
 import subprocess
+import types
 
 import pytest
 
@@ -16,6 +21,7 @@ import oracle
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "csa2_oracle.c")
+PY_SRC = oracle.__file__
 
 MUTANTS = {
     "rounding ties away from zero": ("return (q % 2 == 0) ? q : q + 1;", "return q + 1;"),
@@ -52,6 +58,7 @@ def _pin_calls():
             argnames, values = params[0].args
             argnames = [a.strip() for a in argnames.split(",")]
             for v in values:
+                v = v if len(argnames) > 1 else (v,)
                 yield name, (lambda fn=fn, v=v, a=argnames: fn(**dict(zip(a, v))))
         else:
             yield name, fn
@@ -71,7 +78,45 @@ def test_pins_catch_planted_mistake(mutant, tmp_path):
         for name, call in _pin_calls():
             try:
                 call()
-            except Exception:            # assertion or rejected input: the pin noticed
+            except (AssertionError, ValueError):   # a failed check or a rejected input: the pin noticed
                 caught.append(name)
                 break
+    assert caught, f"no pin noticed the planted mistake: {mutant}"
+
+
+# Slips in the layer-mode rules of oracle/__init__.py (run_layers).
+PY_MUTANTS = {
+    "a Reindex layer keeps the earlier indices": (
+        "            current = sel\n        elif mode == \"reindex_tokens\":",
+        "            current = sel if mode == \"full\" else current\n        elif mode == \"reindex_tokens\":"),
+    "window-only layers after a Full layer attend to the main set too": (
+        'if mode == "swa":', 'if mode == "swa" and current is None:'),
+    "every layer reads the first cache": (
+        "k_idx, k_main, v_main = wl.cache(max(n_full - 1, 0))", "k_idx, k_main, v_main = wl.cache(0)"),
+    "a Full layer after the first reads the previous cache": (
+        "k_idx, k_main, v_main = wl.cache(max(n_full - 1, 0))", "k_idx, k_main, v_main = wl.cache(max(n_full - 2, 0))"),
+    "Reuse layers attend to the window alone": (
+        "            topk, cnt = current[2], current[3]", "            topk, cnt = None, None"),
+    "a token-only Reindex layer does not pass its selection on": (
+        "            sel = (current[0], current[1], topk, cnt)\n            res[\"index\"][layer] = dict(zip((\"blk_ids\", \"blk_cnt\", \"topk\", \"topk_cnt\"), sel))\n            current = sel",
+        "            sel = (current[0], current[1], topk, cnt)\n            res[\"index\"][layer] = dict(zip((\"blk_ids\", \"blk_cnt\", \"topk\", \"topk_cnt\"), sel))"),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(PY_MUTANTS))
+def test_pins_catch_planted_mode_rule_mistake(mutant, monkeypatch):
+    old, new = PY_MUTANTS[mutant]
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique/found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = PY_SRC          # the mutant loads the same compiled C oracle
+    exec(compile(src.replace(old, new), PY_SRC, "exec"), mod.__dict__)
+    monkeypatch.setattr(pins, "oracle", mod)
+    caught = []
+    for name, call in _pin_calls():
+        try:
+            call()
+        except (AssertionError, ValueError):   # a failed check or a rejected input: the pin noticed
+            caught.append(name)
+            break
     assert caught, f"no pin noticed the planted mistake: {mutant}"

@@ -12,7 +12,11 @@
   attended values, one-hot values recovering the attended set, and the toy's
   470/7;
 * modes: Reuse equals attention with the Full layer's indices; Reindex with the
-  Full layer's indexer query reproduces its indices.
+  Full layer's indexer query reproduces its indices; and the layer sequencing
+  of ``run_layers`` (a Reuse layer after a Reindex or token-only Reindex layer
+  takes that layer's fresh indices, window-only layers attend to their window
+  alone wherever they sit, each Full layer opens its own cache) against each
+  layer recomputed from scratch by enumeration and fp64 SDPA.
 """
 import json
 import math
@@ -457,3 +461,118 @@ def test_hierarchy_changes_selection_only_through_the_pool():
         s = wl.k_idx[i, :t + 1].astype(np.int64) @ wl.q_idx[0][i].astype(np.int64)
         want = np.sort(np.lexsort((np.arange(t + 1), -s))[:24])
         assert (tk_f[i, :tc_f[i]] == want).all()
+
+
+# ---------------------------------------------------------------- layer-mode rules
+# The mode table of "CSA2 with cross-layer reuse" (page "DeepSeek V4.1
+# Flash"): a Full layer selects with its own indexer query over its own keys
+# and opens its own main-KV/indexer cache, a Reindex layer selects afresh with
+# its own query over the shared keys, a Reuse layer takes the indices of the
+# most recent Full/Reindex layer, and every layer attends with its own Q and
+# window K/V; window-only layers attend to the window alone.  These pins
+# compute each layer's expected result from scratch (selection by enumeration,
+# attention by torch's fp64 SDPA over the gathered rows) and compare
+# run_layers with it, so a slip in the mode sequencing fails here.
+def _mode_workload(layers, seed):
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=2, ctx=16, n_heads=2, head_dim=8, d_idx=32,
+                   block=2, pool=4, top_k=3, window=4, layers=layers)
+    return cfg, W.generate(cfg, seed=seed)
+
+
+def _brute_sets(wl, layer, c):
+    """(pool, Top-K) of indexing layer `layer` over cache c, per query, by enumeration."""
+    cfg = wl.cfg
+    k_idx = wl.cache(c)[0]
+    return [select_brute(wl.q_idx[layer][i], k_idx[wl.q_seq[i]], int(wl.q_pos[i]), cfg.block, cfg.pool,
+                         cfg.top_k, cfg.tail) for i in range(cfg.n_q)]
+
+
+def _sdpa_layer(wl, layer, c, sets):
+    """Output of layer `layer`: softmax attention of its Q over the main rows
+    sets[i][1] of cache c (none when sets is None) and its own window rows."""
+    cfg = wl.cfg
+    f = (lambda a: _f64(W.bf16_bits_to_f32(a))) if cfg.dtype == "bf16" else _f64
+    _, k_main, v_main = wl.cache(c)
+    out = np.empty((cfg.n_q, cfg.n_heads, cfg.head_dim))
+    for i in range(cfg.n_q):
+        s, t = int(wl.q_seq[i]), int(wl.q_pos[i])
+        rows = [] if sets is None else list(sets[i][1])
+        win = [p - cfg.swa_first for p in range(max(0, t - cfg.window + 1), t + 1)]
+        K = torch.cat([f(k_main[s])[rows], f(wl.k_swa[layer][s])[win]], 0)
+        V = torch.cat([f(v_main[s])[rows], f(wl.v_swa[layer][s])[win]], 0)
+        Q = f(wl.q[layer][i])[:, None, :]                                 # [H][1][D]
+        H = cfg.n_heads
+        o = torch.nn.functional.scaled_dot_product_attention(Q, K[None].expand(H, -1, -1),
+                                                             V[None].expand(H, -1, -1))
+        out[i] = o[:, 0, :].numpy()
+    return out
+
+
+def _assert_index(got, sets):
+    for i, (pool, top) in enumerate(sets):
+        assert got["blk_ids"][i, :got["blk_cnt"][i]].tolist() == pool
+        assert got["topk"][i, :got["topk_cnt"][i]].tolist() == top
+        assert (got["topk"][i, got["topk_cnt"][i]:] == -1).all()
+
+
+def test_reuse_after_reindex_takes_the_reindex_indices():
+    """Full, Reuse, Reindex, Reuse with a Reindex indexer query of its own:
+    the second Reuse layer attends over the Reindex layer's fresh selection,
+    not the Full layer's."""
+    cfg, wl = _mode_workload(("full", "reuse", "reindex", "reuse"), seed=31)
+    res = oracle.run_layers(wl)
+    full, reidx = _brute_sets(wl, 0, 0), _brute_sets(wl, 2, 0)
+    assert any(f[1] != r[1] for f, r in zip(full, reidx)), "the two index sets must differ"
+    _assert_index(res["index"][0], full)
+    _assert_index(res["index"][2], reidx)
+    for layer, sets in ((0, full), (1, full), (2, reidx), (3, reidx)):
+        np.testing.assert_allclose(res["out"][layer], _sdpa_layer(wl, layer, 0, sets), rtol=1e-12, atol=1e-12)
+    assert not np.allclose(res["out"][3], _sdpa_layer(wl, 3, 0, full))
+
+
+def test_window_only_layers_attend_to_their_window_alone():
+    """Window-only layers before the first Full layer (the encoder's first two
+    layers) and after a Full layer attend to their own window only, whatever
+    index set is current."""
+    cfg, wl = _mode_workload(("swa", "full", "reuse", "swa"), seed=32)
+    res = oracle.run_layers(wl)
+    full = _brute_sets(wl, 1, 0)
+    _assert_index(res["index"][1], full)
+    for layer, sets in ((0, None), (1, full), (2, full), (3, None)):
+        np.testing.assert_allclose(res["out"][layer], _sdpa_layer(wl, layer, 0, sets), rtol=1e-12, atol=1e-12)
+    assert not np.allclose(res["out"][3], _sdpa_layer(wl, 3, 0, full))
+
+
+def test_each_full_layer_opens_its_own_cache():
+    """Full, Reuse, Full, Reuse: the second Full layer selects over its own
+    indexer keys and both it and the Reuse layer after it read its own main
+    K/V, while the first pair keeps reading the first cache."""
+    cfg, wl = _mode_workload(("full", "reuse", "full", "reuse"), seed=33)
+    assert cfg.n_caches == 2
+    res = oracle.run_layers(wl)
+    first, second = _brute_sets(wl, 0, 0), _brute_sets(wl, 2, 1)
+    _assert_index(res["index"][0], first)
+    _assert_index(res["index"][2], second)
+    for layer, c, sets in ((0, 0, first), (1, 0, first), (2, 1, second), (3, 1, second)):
+        np.testing.assert_allclose(res["out"][layer], _sdpa_layer(wl, layer, c, sets), rtol=1e-12, atol=1e-12)
+    assert not np.allclose(res["out"][3], _sdpa_layer(wl, 3, 0, second))
+
+
+def test_reuse_after_token_only_reindex_takes_its_fresh_topk():
+    """Full, Reuse, token-only Reindex, Reuse: the token-only Reindex layer
+    keeps the Full layer's pool, reselects the tokens with its own indexer
+    query, and the Reuse layer after it attends over that new selection."""
+    cfg, wl = _mode_workload(("full", "reuse", "reindex_tokens", "reuse"), seed=34)
+    res = oracle.run_layers(wl)
+    full = _brute_sets(wl, 0, 0)
+    tok = []
+    for i, (pool, _) in enumerate(full):
+        t, s = int(wl.q_pos[i]), int(wl.q_seq[i])
+        cands = [(dot(wl.q_idx[2][i], wl.k_idx[s][p]), p) for j in pool
+                 for p in range(j * cfg.block, j * cfg.block + cfg.block) if p <= t]
+        tok.append((pool, top_n_by_enumeration(cands, cfg.top_k)))
+    assert any(f[1] != r[1] for f, r in zip(full, tok)), "the two selections must differ"
+    _assert_index(res["index"][0], full)
+    _assert_index(res["index"][2], tok)
+    for layer, sets in ((0, full), (1, full), (2, tok), (3, tok)):
+        np.testing.assert_allclose(res["out"][layer], _sdpa_layer(wl, layer, 0, sets), rtol=1e-12, atol=1e-12)
