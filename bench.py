@@ -7,23 +7,31 @@ cache; 16 heads x 128, int8 indexer of dim 64, blocks of 8, pool 2,048,
 Top-512 plus a 128-token window.  A step is one pass of the whole path: block
 pass (storing the key of the block the newest token completes), token Top-K
 and the attention of all 6 layers (48 queries).  Its roofline is HBM bandwidth.
-
-``--workload prefill_8k``: one 8,192-token prompt, a Full layer and two
-window-only layers (24,576 queries per step); its roofline is the MFMA peak
-(int8 indexer, bf16 attention).
+The default run also times ``prefill_8k`` (one 8,192-token prompt, a Full
+layer and two window-only layers; 24,576 queries per step; MFMA roofline) and
+reports it under the key ``prefill``.
 
 Inputs are resident in HBM before timing starts.  Steps rotate over R device
 replicas of the caches (each with fresh queries) so that the working set of
 consecutive steps is not served from the 256 MB last-level cache.  Steps are
-replayed from a HIP graph (captured through torch on the stream the library
-launches on), so host launch overhead is not timed.
+replayed from HIP graphs (captured through torch on the stream the library
+launches on), each graph replayed once before the timed region, so host
+launch overhead and first-replay costs are not timed.
+
+Per-kernel durations come from the library's own timing hook
+(csa2_profile_begin): after the timed region, steps run eagerly on the same
+stream with every kernel launched with HIP start/stop events, which hold that
+kernel's execution interval.  ``roofline`` is the kernel of the step with the
+largest time per step, its algorithmic bytes (decode) or operations (prefill)
+per launch over its average duration; ``roofline_step`` is the whole step's
+algorithmic work over the step time.  ``launch_floor_us`` is the time per step
+of a graph holding as many near-empty launches as the step has kernels.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -32,40 +40,254 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse-attn queries/sec + achieved HBM GB/s, decode at 128K ctx (1 GPU)"
-METRIC_PREFILL = "sparse-attn queries/sec + MFMA utilisation, prefill of 8K tokens (1 GPU)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, MI355X
 INT8_PEAK_TOPS = 5000.0
-KERNEL_SOURCES = {
-    "index_blocks": ["select.hip", "device_common.h"],
-    "topk_tokens": ["select.hip", "device_common.h"],
-    "attend": ["attend.hip", "device_common.h"],
-}
+KERNEL_SOURCES = ["select.hip", "attend.hip", "device_common.h", "internal.h"]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_sha(kernel):
+def source_sha():
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "top_kv_selection_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
-    when there are none or the kernel source changed since they were taken."""
+    """Calibrated HBM bytes per launch from committed rocprofv3 counter
+    summaries, or None when there are none or the kernel sources changed since
+    they were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_sha") != source_sha(kernel):
+    if rec.get("source_sha") != source_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_seconds):
+    import numpy as np
+    import torch
+
+    from top_kv_selection_amd import binding as B
+    from top_kv_selection_amd import pipeline
+    from top_kv_selection_amd import workloads as W
+
+    cfg = W.CONFIGS[name]
+    R, NS = max(1, replicas), max(1, streams)
+    if R % NS or steps % NS or warmup % NS:
+        raise SystemExit("--replicas, --steps and --warmup must be multiples of --streams")
+    n_queries = cfg.n_q * cfg.n_layers
+
+    log(f"{name}: generating (seed {cfg.seed})")
+    t0 = time.time()
+    wl = W.generate(cfg)
+    log(f"{name}: generated in {time.time() - t0:.1f}s; uploading {R} replicas")
+    base = pipeline.upload(wl)
+    pipeline.build_cache(base)
+    dws = [base]
+    for r in range(1, R):
+        q_idx, q = W.fresh_queries(cfg, seed=cfg.seed * 1000 + r)
+        dws.append(pipeline.replicate(base, q_idx, q))
+    torch.cuda.synchronize()
+    log(f"{name}: {R} replicas resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+
+    # ---- graphs of whole steps, one set per stream (each stream owns R/NS replicas)
+    def capture(fn, reps, stream=None):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for dw in reps:
+                fn(dw)
+        return g
+
+    for dw in dws:                      # eager pass: every launch checked once
+        pipeline.run(dw)
+    torch.cuda.synchronize()
+    RS = R // NS
+    side = [torch.cuda.Stream() for _ in range(NS)]
+    own = [dws[k * RS:(k + 1) * RS] for k in range(NS)]
+    step_graphs = [dict() for _ in range(NS)]
+
+    def graphs_for(n):
+        """Graphs for n steps per stream: full cycles over the stream's replicas
+        plus one shorter tail; every new graph is replayed once."""
+        for k in range(NS):
+            for m in (RS if n >= RS else 0, n % RS):
+                if m and m not in step_graphs[k]:
+                    step_graphs[k][m] = capture(pipeline.run, own[k][:m], side[k])
+                    step_graphs[k][m].replay()
+        torch.cuda.synchronize()
+
+    def run_steps(n_total):
+        n = n_total // NS
+        full, rest = divmod(n, RS)
+        main = torch.cuda.current_stream()
+        for k in range(NS):
+            side[k].wait_stream(main)
+            with torch.cuda.stream(side[k]):
+                for _ in range(full):
+                    step_graphs[k][RS].replay()
+                if rest:
+                    step_graphs[k][rest].replay()
+        for k in range(NS):
+            main.wait_stream(side[k])
+
+    graphs_for(warmup // NS)
+    graphs_for(steps // NS)             # every graph of the timed region exists and has run once
+    run_steps(warmup)
+    torch.cuda.synchronize()
+    log(f"{name}: warmup {warmup} steps done; timing {steps} steps on {NS} stream(s)")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    run_steps(steps)
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / steps
+    value = n_queries * steps / (ms_total / 1e3)
+    log(f"{name}: {ms_per_step * 1e3:.2f} us/step, {value / 1e6:.3f} M queries/s")
+
+    # ---- per-kernel durations: eager steps with the library's timing hook
+    n_prof = profile_rounds * R
+    B.csa2_profile_begin("", 64 * n_prof)
+    for k in range(n_prof):
+        pipeline.run(dws[k % R])
+    recs = B.csa2_profile_end()
+    per = {}
+    for kname, ms in recs:
+        d = per.setdefault(kname, {"launches": 0, "ms": 0.0})
+        d["launches"] += 1
+        d["ms"] += ms
+    n_kernels_per_step = sum(d["launches"] for d in per.values()) / n_prof
+
+    # ---- fixed cost of the step's launches: a graph of as many near-empty
+    # launches (a one-word workspace fill) per step
+    tiny = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    n_empty = max(1, round(n_kernels_per_step))
+
+    def empty_step(_):
+        for _ in range(n_empty):
+            B.csa2_workspace_init(tiny[:4])
+
+    g_empty = capture(empty_step, list(range(R)))
+    g_empty.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, steps // R)
+    s.record()
+    for _ in range(reps):
+        g_empty.replay()
+    e.record()
+    torch.cuda.synchronize()
+    floor_us = s.elapsed_time(e) * 1e3 / (reps * R)
+    log(f"{name}: {n_empty} near-empty launches per step take {floor_us:.2f} us in a graph")
+
+    # ---- rooflines
+    work = pipeline.kernel_work(cfg)   # kernel -> (unit, algorithmic amount per step)
+    kernels = {}
+    for kname, d in sorted(per.items(), key=lambda kv: -kv[1]["ms"]):
+        launches_per_step = d["launches"] / n_prof
+        us_per_launch = d["ms"] * 1e3 / d["launches"]
+        rec = {"us_per_launch": round(us_per_launch, 3), "launches_per_step": round(launches_per_step, 3),
+               "us_per_step": round(us_per_launch * launches_per_step, 3)}
+        if kname in work:
+            unit, amount = work[kname]
+            per_launch = amount / launches_per_step
+            rate = per_launch / (us_per_launch * 1e-6)
+            if unit == "bytes":
+                rec.update(algorithmic_bytes_per_launch=int(per_launch), achieved_gbs=round(rate / 1e9, 1))
+            else:
+                rec.update({f"algorithmic_{unit}_per_launch": int(per_launch), "achieved_tops": round(rate / 1e12, 1)})
+        kernels[kname] = rec
+        log(f"{name}: kernel {kname}: {us_per_launch:.2f} us x {launches_per_step:g} per step")
+
+    known = [k for k in kernels if k in work]
+    if not known:
+        raise SystemExit(f"no work model for the kernels of {name}: {sorted(kernels)}")
+    dom = max(known, key=lambda k: kernels[k]["us_per_step"])
+    unit, _ = work[dom]
+    if unit == "bytes":
+        ach = kernels[dom]["achieved_gbs"]
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, name)}
+        step_bytes = sum(a for u, a in work.values() if u == "bytes")
+        step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+        step = {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(step_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": step_bytes}
+    else:
+        peak = INT8_PEAK_TOPS if unit == "int8_ops" else BF16_PEAK_TFLOPS
+        ach = kernels[dom]["achieved_tops"]
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": peak,
+                    "unit": "TOP/s" if unit == "int8_ops" else "TFLOP/s", "frac": round(ach / peak, 4),
+                    "traffic": measured_traffic(dom, name)}
+        int8 = sum(a for u, a in work.values() if u == "int8_ops")
+        bf16 = sum(a for u, a in work.values() if u == "bf16_flops")
+        ideal_us = int8 / (INT8_PEAK_TOPS * 1e6) + bf16 / (BF16_PEAK_TFLOPS * 1e6)
+        step = {"bound": "mfma", "frac": round(ideal_us / (ms_per_step * 1e3), 4), "int8_ops": int8,
+                "bf16_flops": bf16, "ideal_us_at_peak": round(ideal_us, 3)}
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same step
+    cpu = None
+    if cpu_seconds > 0:
+        import oracle
+
+        threads = oracle.default_threads()
+        log(f"{name}: cpu baseline, oracle on {threads} threads for ~{cpu_seconds:.0f}s")
+        n = 0
+        t0 = time.time()
+        if cfg.decode:
+            while True:
+                oracle.run_layers(wl, threads=threads)
+                n += 1
+                if time.time() - t0 >= cpu_seconds:
+                    break
+            dt = time.time() - t0
+            cpu = {"value": round(n * n_queries / dt, 2), "unit": "queries/s", "cores": threads, "kind": "oracle",
+                   "sample": f"{n} full steps of {name} ({n_queries} queries each) on replica 0, {dt:.1f}s"}
+        else:
+            rng = np.random.default_rng(0)
+            rows_done = 0
+            while True:
+                rows = np.sort(rng.choice(cfg.n_q, min(256, cfg.n_q), replace=False))
+                oracle.run_layers(wl, rows=rows, threads=threads)
+                rows_done += len(rows)
+                if time.time() - t0 >= cpu_seconds:
+                    break
+            dt = time.time() - t0
+            cpu = {"value": round(rows_done * cfg.n_layers / dt, 2), "unit": "queries/s", "cores": threads,
+                   "kind": "oracle",
+                   "sample": f"{rows_done} random query rows of {name}, all {cfg.n_layers} layers, {dt:.1f}s"}
+        log(f"{name}: cpu baseline {cpu['value']} queries/s")
+
+    res = {
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "config": {"workload": name, "batch": cfg.n_seq, "context": cfg.ctx, "layers": "+".join(cfg.layers),
+                   "queries_per_step": n_queries, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
+                   "d_idx": cfg.d_idx, "block": cfg.block, "pool": cfg.pool, "top_k": cfg.top_k,
+                   "window": cfg.window, "replicas": R, "streams": NS, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "roofline_step": step,
+        "launch_floor_us": round(floor_us, 3),
+        "kernels_per_step": round(n_kernels_per_step, 3),
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    del dws, base, own, step_graphs, g_empty
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -78,8 +300,9 @@ def main():
     ap.add_argument("--streams", type=int, default=1,
                     help="independent steps in flight on separate streams (micro-batch overlap); "
                          "each stream owns replicas/streams replicas")
-    ap.add_argument("--workload", default="decode_group_128k")
-    ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
+    ap.add_argument("--workload", default=None,
+                    help="one workload only (default: decode_group_128k, plus prefill_8k under 'prefill')")
+    ap.add_argument("--profile-rounds", type=int, default=2, help="eager passes over the replicas with kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -105,228 +328,46 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from top_kv_selection_amd import binding as B
-    from top_kv_selection_amd import pipeline
     from top_kv_selection_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = W.CONFIGS[args.workload]
-    if args.steps is None:
-        args.steps = 3200 if cfg.decode else 200
-    if args.warmup is None:
-        args.warmup = 320 if cfg.decode else 20
-    if args.replicas is None:
-        args.replicas = 32 if cfg.decode else 2
-    R = max(1, args.replicas)
-    NS = max(1, args.streams)
-    if R % NS:
-        raise SystemExit("--replicas must be a multiple of --streams")
-    K, Wm = args.steps, args.warmup
-    if K % NS or Wm % NS:
-        raise SystemExit("--steps and --warmup must be multiples of --streams")
-    n_queries = cfg.n_q * cfg.n_layers
+    main_name = args.workload or "decode_group_128k"
+    cfg = W.CONFIGS[main_name]
+    steps = args.steps if args.steps is not None else (3200 if cfg.decode else 200)
+    warmup = args.warmup if args.warmup is not None else (320 if cfg.decode else 20)
+    replicas = args.replicas if args.replicas is not None else (32 if cfg.decode else 2)
+    cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    res = run_workload(main_name, steps, warmup, replicas, args.streams, args.profile_rounds, cpu_s)
 
-    log(f"generating {cfg.name} (seed {cfg.seed})")
-    t0 = time.time()
-    wl = W.generate(cfg)
-    log(f"generated in {time.time() - t0:.1f}s; uploading {R} replicas")
-    base = pipeline.upload(wl)
-    pipeline.build_cache(base)
-    dws = [base]
-    for r in range(1, R):
-        q_idx, q = W.fresh_queries(cfg, seed=cfg.seed * 1000 + r)
-        dws.append(pipeline.replicate(base, q_idx, q))
-    torch.cuda.synchronize()
-    log(f"{R} replicas resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
-
-    # ---- graphs of whole steps, one set per stream (each stream owns R/NS replicas)
-    def capture(fn, reps, stream=None):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for dw in reps:
-                fn(dw)
-        return g
-
-    for dw in dws:                      # eager pass: every launch checked once
-        pipeline.run(dw)
-    torch.cuda.synchronize()
-    RS = R // NS
-    streams = [torch.cuda.Stream() for _ in range(NS)]
-    own = [dws[k * RS:(k + 1) * RS] for k in range(NS)]
-    step_graphs = [dict() for _ in range(NS)]
-
-    def graphs_for(n):
-        """Graphs for n steps per stream: full cycles over the stream's replicas
-        plus one shorter tail."""
-        for k in range(NS):
-            for m in (RS if n >= RS else 0, n % RS):
-                if m and m not in step_graphs[k]:
-                    step_graphs[k][m] = capture(pipeline.run, own[k][:m], streams[k])
-
-    def run_steps(n_total):
-        n = n_total // NS
-        full, rest = divmod(n, RS)
-        graphs_for(n)
-        main = torch.cuda.current_stream()
-        for k in range(NS):
-            streams[k].wait_stream(main)
-            with torch.cuda.stream(streams[k]):
-                for _ in range(full):
-                    step_graphs[k][RS].replay()
-                if rest:
-                    step_graphs[k][rest].replay()
-        for k in range(NS):
-            main.wait_stream(streams[k])
-
-    run_steps(Wm)
-    torch.cuda.synchronize()
-    log(f"warmup {Wm} steps done; timing {K} steps on {NS} stream(s)")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    graphs_for(K // NS)                 # every graph the timed region needs, built before it
-    torch.cuda.synchronize()
-    start.record()
-    run_steps(K)
-    end.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_per_step = ms_total / K
-    value = n_queries * K / (ms_total / 1e3)
-    log(f"{ms_per_step * 1e3:.2f} us/step, {value / 1e6:.3f} M queries/s")
-
-    # ---- per-kernel launch durations (graph of R back-to-back launches each)
-    lc = base.lcfg
-
-    def k_index(dw):
-        for g, grp in enumerate(dw.groups):
-            if grp.q_idx is not None:
-                B.csa2_index_blocks(lc, grp.q_idx, dw.q_seq, dw.q_pos, dw.k_idx, dw.k_blk, dw.blk_ids[g],
-                                    dw.blk_cnt[g], dw.ws)
-
-    def k_topk(dw):
-        for g, grp in enumerate(dw.groups):
-            if grp.q_idx is not None:
-                B.csa2_topk_tokens(lc, grp.q_idx, dw.q_seq, dw.q_pos, dw.k_idx, dw.blk_ids[g], dw.blk_cnt[g],
-                                   dw.topk[g], dw.topk_cnt[g], dw.ws)
-
-    def k_attend(dw):
-        for grp in dw.groups:
-            src = grp.index_of
-            B.csa2_attend_group(lc, grp.q, dw.q_seq, dw.q_pos, dw.k_main, dw.v_main, grp.k_swa, grp.v_swa,
-                                cfg.swa_first, dw.topk.get(src), dw.topk_cnt.get(src), grp.out, grp.lse, dw.ws)
-
-    if cfg.decode:
-        work = pipeline.algorithmic_bytes(cfg)            # bytes per launch
-    else:
-        work = pipeline.algorithmic_ops(cfg)              # int8 ops / bf16 flops per launch
-    kernels = {}
-    for name, fn in (("index_blocks", k_index), ("topk_tokens", k_topk), ("attend", k_attend)):
-        launches = len(work[name])
-        if launches == 0:
-            continue
-        g = capture(fn, dws)
-        g.replay()
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(args.kernel_reps):
-            g.replay()
-        e.record()
-        torch.cuda.synchronize()
-        us = s.elapsed_time(e) * 1e3 / (args.kernel_reps * R * launches)
-        per_launch = sum(work[name]) / launches
-        rec = {"us_per_launch": round(us, 3), "launches_per_step": launches}
-        if cfg.decode:
-            rec["algorithmic_bytes_per_launch"] = int(per_launch)
-            rec["achieved_gbs"] = round(per_launch / (us * 1e-6) / 1e9, 1)
-            log(f"kernel {name}: {us:.2f} us/launch, {rec['achieved_gbs']} GB/s algorithmic")
-        else:
-            unit = "int8_ops" if name != "attend" else "bf16_flops"
-            rec[f"algorithmic_{unit}_per_launch"] = int(per_launch)
-            rec["achieved_tops"] = round(per_launch / (us * 1e-6) / 1e12, 1)
-            log(f"kernel {name}: {us:.2f} us/launch, {rec['achieved_tops']} T{unit.split('_')[0]}/s")
-        kernels[name] = rec
-
-    dom = max(kernels, key=lambda k: kernels[k]["us_per_launch"] * kernels[k]["launches_per_step"])
     extra = {}
-    if cfg.decode:
-        ach = kernels[dom]["achieved_gbs"]
-        roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, cfg.name)}
-        step_bytes = sum(sum(v) for v in work.values())
-        extra = {"hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-                 "step_algorithmic_bytes": step_bytes}
-    else:
-        peak = BF16_PEAK_TFLOPS if dom == "attend" else INT8_PEAK_TOPS
-        ach = kernels[dom]["achieved_tops"]
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": peak,
-                    "unit": "TFLOP/s" if dom == "attend" else "TOP/s", "frac": round(ach / peak, 4),
-                    "traffic": measured_traffic(dom, cfg.name)}
-        int8_ops = sum(work["index_blocks"]) + sum(work["topk_tokens"])
-        bf16_flops = sum(work["attend"])
-        ideal_us = int8_ops / (INT8_PEAK_TOPS * 1e6) + bf16_flops / (BF16_PEAK_TFLOPS * 1e6)
-        extra = {"step_int8_ops": int8_ops, "step_bf16_flops": bf16_flops,
-                 "mfma_fraction_step": round(ideal_us / (ms_per_step * 1e3), 4)}
+    if args.workload is None:
+        pre = run_workload("prefill_8k", 200, 20, 2, 1, 4, 0.0 if args.no_cpu_baseline else 5.0)
+        extra["prefill"] = pre
 
-    # ---- CPU baseline: the oracle on a bounded sample of the same step
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-
-        threads = oracle.default_threads()
-        log(f"cpu baseline: oracle steps on {threads} threads for ~{args.cpu_seconds:.0f}s")
-        n = 0
-        t0 = time.time()
-        if cfg.decode:
-            while True:
-                oracle.run_layers(wl, threads=threads)
-                n += 1
-                if time.time() - t0 >= args.cpu_seconds:
-                    break
-            dt = time.time() - t0
-            cpu = {"value": round(n * n_queries / dt, 2), "unit": "queries/s", "cores": threads, "kind": "oracle",
-                   "sample": f"{n} full steps of {cfg.name} ({n_queries} queries each) on replica 0, {dt:.1f}s"}
-        else:
-            # prefill: every layer of an evenly spaced sample of query rows
-            rng = np.random.default_rng(0)
-            rows_done = 0
-            while True:
-                rows = np.sort(rng.choice(cfg.n_q, min(256, cfg.n_q), replace=False))
-                oracle.run_layers(wl, rows=rows, threads=threads)
-                rows_done += len(rows)
-                if time.time() - t0 >= args.cpu_seconds:
-                    break
-            dt = time.time() - t0
-            cpu = {"value": round(rows_done * cfg.n_layers / dt, 2), "unit": "queries/s", "cores": threads,
-                   "kind": "oracle",
-                   "sample": f"{rows_done} random query rows of {cfg.name}, all {cfg.n_layers} layers, {dt:.1f}s"}
-        log(f"cpu baseline {cpu['value']} queries/s")
-
+    metric = METRIC if cfg.decode else f"sparse-attn queries/sec + MFMA utilisation, {main_name} (1 GPU)"
     out = {
-        "metric": METRIC if cfg.decode else (METRIC_PREFILL if cfg.name == "prefill_8k" else
-                                             f"sparse-attn queries/sec + MFMA utilisation, {cfg.name} (1 GPU)"),
-        "value": round(value, 1),
+        "metric": metric,
+        "value": res["value"],
         "unit": "queries/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": Wm,
-        "ms_per_step": round(ms_per_step, 6),
+        "steps": res["steps"],
+        "warmup": res["warmup"],
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": res["dtype"],
         "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": cfg.n_seq, "context": cfg.ctx,
-                   "layers": "+".join(cfg.layers), "queries_per_step": n_queries, "heads": cfg.n_heads,
-                   "head_dim": cfg.head_dim, "d_idx": cfg.d_idx, "block": cfg.block, "pool": cfg.pool,
-                   "top_k": cfg.top_k, "window": cfg.window, "replicas": R, "streams": NS,
-                   "parallelism": "none (1 GPU)"},
+        "config": res["config"],
+        "roofline": res["roofline"],
+        "roofline_step": res["roofline_step"],
+        "launch_floor_us": res["launch_floor_us"],
+        "kernels_per_step": res["kernels_per_step"],
+        "kernels": res["kernels"],
+        "cpu_baseline": res["cpu_baseline"],
         **extra,
-        "roofline": roofline,
-        "kernels": kernels,
-        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

@@ -117,6 +117,23 @@ typedef struct {
 int32_t csa2_abi_version(void);
 const char *csa2_status_str(int32_t status);
 
+/* Measurement aid; no call above needs it.  csa2_profile_begin arms a list of
+ * max_launches (0 .. 65536) pairs of HIP events: while armed, each library
+ * kernel launch whose kernel name contains kernel_filter (NULL or "" = every
+ * kernel) takes the next pair, launched with hipExtLaunchKernel so that the
+ * pair records that kernel's own execution interval.  Launches beyond the
+ * list, and launches into a stream that is capturing a graph, are not timed.
+ * csa2_profile_end disarms, waits for every timed launch and writes their
+ * number; csa2_profile_record then reads back launch i (in launch order): its
+ * kernel name (truncated to name_len - 1 bytes) and its duration in
+ * milliseconds.  The records stay readable until the next csa2_profile_begin.
+ * Process-wide state; calls are serialised by a mutex.  Errors: CSA2_E_SHAPE
+ * for a bad count, filter or index (or reading while armed), CSA2_E_HIP when
+ * an event cannot be created or read. */
+int32_t csa2_profile_begin(const char *kernel_filter, int32_t max_launches);
+int32_t csa2_profile_end(int32_t *n_timed);
+int32_t csa2_profile_record(int32_t i, char *name, int32_t name_len, float *ms);
+
 /* Bytes of workspace needed by any call below for n_q query rows against
  * caches of T positions and n_layers layers per group call.  Writes *bytes. */
 int32_t csa2_workspace_bytes(const csa2_cfg *cfg, int32_t n_q, int32_t T, int32_t n_layers,

@@ -64,6 +64,21 @@ def test_workspace_bytes_follow_the_work_split(B):
     assert _ws(B, small, 256, 256) < 1 << 20
 
 
+def test_workspace_bytes_grow_with_every_size(B):
+    """A workspace sized for (n_q, T, n_layers) must hold the head and scratch
+    of every smaller call, so the size never shrinks as a size grows."""
+    for cfg in (B.Cfg(), B.Cfg(pool=64, top_k=100, window=37), B.Cfg(n_heads=32),
+                B.Cfg(pool=8, top_k=32, window=16, d_idx=32, n_heads=4, head_dim=64, dtype=B.F32)):
+        for T in (300, 5003, 32768, 131072, 262144):
+            prev = 0
+            for n_q in (1, 7, 8, 64, 255, 256, 511, 512, 2048, 8192):
+                cur = _ws(B, cfg, n_q, T, 6)
+                assert cur >= prev, (cfg, T, n_q)
+                assert _ws(B, cfg, n_q, T, 1) <= cur
+                assert T < 300 or _ws(B, cfg, n_q, T // 2, 6) <= cur
+                prev = cur
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("d_idx", 48, 4), ("head_dim", 96, 4), ("block", 0, 2), ("block", 17, 2), ("pool", 0, 2),
     ("top_k", -1, 2), ("window", 2000, 2), ("dtype", 7, 3), ("n_heads", 0, 2),

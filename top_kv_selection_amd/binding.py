@@ -28,9 +28,9 @@ STATUS = {0: "CSA2_OK", 1: "CSA2_E_NULL", 2: "CSA2_E_SHAPE", 3: "CSA2_E_DTYPE",
           4: "CSA2_E_UNSUPPORTED", 5: "CSA2_E_ALIGN", 6: "CSA2_E_WORKSPACE", 7: "CSA2_E_HIP",
           8: "CSA2_E_MODE"}
 
-EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_workspace_bytes", "csa2_workspace_init",
-           "csa2_build_block_keys", "csa2_append_tokens", "csa2_index_blocks", "csa2_topk_tokens", "csa2_attend_group",
-           "csa2_attend", "csa2_layer_group"]
+EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_profile_begin", "csa2_profile_end", "csa2_profile_record",
+           "csa2_workspace_bytes", "csa2_workspace_init", "csa2_build_block_keys", "csa2_append_tokens",
+           "csa2_index_blocks", "csa2_topk_tokens", "csa2_attend_group", "csa2_attend", "csa2_layer_group"]
 
 
 class Csa2Error(RuntimeError):
@@ -77,6 +77,9 @@ def _load():
     sig = {
         "csa2_abi_version": (I, []),
         "csa2_status_str": (ctypes.c_char_p, [I]),
+        "csa2_profile_begin": (I, [ctypes.c_char_p, I]),
+        "csa2_profile_end": (I, [ctypes.POINTER(I)]),
+        "csa2_profile_record": (I, [I, ctypes.c_char_p, I, ctypes.POINTER(ctypes.c_float)]),
         "csa2_workspace_bytes": (I, [C, I, I, I, ctypes.POINTER(ctypes.c_size_t)]),
         "csa2_workspace_init": (I, [P, Z, P]),
         "csa2_build_block_keys": (I, [C, P, I, I, I, I, P, P]),
@@ -130,6 +133,26 @@ def _need(t, name, dtype, ndim=None):
 
 def csa2_abi_version() -> int:
     return int(_lib.csa2_abi_version())
+
+
+def csa2_profile_begin(kernel_filter: str = "", max_launches: int = 4096):
+    """Arms the library's per-kernel timing: the next max_launches kernel
+    launches whose name contains kernel_filter carry HIP start/stop events."""
+    _check("csa2_profile_begin", _lib.csa2_profile_begin(kernel_filter.encode(), int(max_launches)))
+
+
+def csa2_profile_end():
+    """Disarms the timing and returns [(kernel name, milliseconds)] of every
+    timed launch, in launch order."""
+    n = ctypes.c_int32(0)
+    _check("csa2_profile_end", _lib.csa2_profile_end(ctypes.byref(n)))
+    out = []
+    buf = ctypes.create_string_buffer(64)
+    ms = ctypes.c_float(0.0)
+    for i in range(n.value):
+        _check("csa2_profile_record", _lib.csa2_profile_record(i, buf, 64, ctypes.byref(ms)))
+        out.append((buf.value.decode(), float(ms.value)))
+    return out
 
 
 def csa2_workspace_bytes(cfg: Cfg, n_q: int, T: int, n_layers: int = 1) -> int:

@@ -6,12 +6,60 @@
 // kernels leave the head zeroed again, so a zero-filled workspace sized by
 // csa2_workspace_bytes for the largest call serves every call in stream order.
 #include <math.h>
+#include <string.h>
 #include <algorithm>
+#include <atomic>
+#include <mutex>
+#include <vector>
 
 #include "csa2.h"
+#include "device_common.h"
 #include "internal.h"
 
 using namespace csa2;
+
+// ---- measurement hook of csa2_profile_begin / csa2_profile_end: a bounded
+// list of HIP event pairs handed to matching launches (see launch() in
+// internal.h), in launch order.
+namespace csa2 {
+namespace {
+struct ProfRec {
+    char name[32];
+    hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_armed{false};
+char g_prof_filter[64];
+std::vector<ProfRec> g_prof;
+size_t g_prof_used = 0;
+
+void prof_release()
+{
+    for (ProfRec &r : g_prof) {
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
+    g_prof.clear();
+    g_prof_used = 0;
+}
+}  // namespace
+
+bool profile_events(const char *name, hipStream_t st, hipEvent_t &start, hipEvent_t &stop)
+{
+    if (!g_prof_armed.load(std::memory_order_relaxed)) return false;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_armed.load(std::memory_order_relaxed) || g_prof_used >= g_prof.size()) return false;
+    if (g_prof_filter[0] && !strstr(name, g_prof_filter)) return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+    ProfRec &r = g_prof[g_prof_used++];
+    strncpy(r.name, name, sizeof(r.name) - 1);
+    r.name[sizeof(r.name) - 1] = 0;
+    start = r.start;
+    stop = r.stop;
+    return true;
+}
+}  // namespace csa2
 
 namespace {
 
@@ -45,6 +93,18 @@ int32_t check_sizes(int32_t n_q, int32_t n_seq, int32_t T)
 }
 
 
+
+// Workspace layout.  Every call keeps the state that must be zero between
+// calls at the head of the workspace and its scratch at the tail end, and
+// leaves its head zero again:
+//   head: [0, hist_bytes(n_q)), per-query 2048-bin selection histograms (split
+//         selections and the fused layer group);
+//   tail: the last round_up(scratch) bytes (keys, token histograms, chunk
+//         records).
+// csa2_workspace_bytes(N, T, L) is an upper bound of every head plus an upper
+// bound of every scratch that a call with n_q <= N, T' <= T and n_layers <= L
+// may use, so that no call's scratch reaches into another call's head.
+size_t hist_bytes(int n_q) { return round_up((size_t)n_q * kRadixBins * sizeof(uint32_t)); }
 
 struct Region {
     uint32_t *ctr;     // head: zero between calls
@@ -179,7 +239,8 @@ struct FusedPlan {
     SelectPlan idx, tok;
     AttendPlan att;
     int64_t blk_stride, tok_stride;
-    size_t head, blk_off, tok_off, tok_hist_off, part_off, tail;
+    size_t head;                                    // block histograms
+    size_t blk_off, tok_off, tok_hist_off, part_off, tail;   // scratch (at the tail end)
 };
 
 FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
@@ -193,7 +254,7 @@ FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
            (f.att.chunks || f.att.keys_per_split <= kAttendRowChunk) && c->pool <= kFusedPoolLds;
     f.blk_stride = (n_elig_max + 3) / 4 * 4;
     f.tok_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
-    f.head = (size_t)n_q * 2048 * sizeof(uint32_t);
+    f.head = hist_bytes(n_q);
     size_t off = 0;
     f.blk_off = off;      off += round_up((size_t)n_q * f.blk_stride * 4);
     f.tok_off = off;      off += round_up((size_t)n_q * f.tok_stride * 4);
@@ -216,6 +277,70 @@ int32_t do_block_keys(const csa2_cfg *c, const int8_t *k_idx, int32_t n_seq, int
     return hip_status(launch_block_keys(p, n_seq, c->d_idx, st));
 }
 
+// Whether some call at a context of at most T positions may take the fused
+// decode path (its other conditions only narrow it further).
+bool fused_possible(const csa2_cfg *c, int T)
+{
+    const AttendPlan one = plan_attend(1, 1, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
+    const long long n_elig_max = (long long)(T - 1) / c->block + 1;
+    return one.chunks && c->top_k >= 1 && c->pool <= kFusedPoolLds && n_elig_max > c->pool;
+}
+
+// Upper bound of the scratch of every call with n_q' <= n_q, T' <= T and
+// n_layers' <= n_layers (each term is monotone in the sizes within the regime
+// that uses it):
+//  * split selections: keys of n_q' queries; a launch splits only below
+//    kTargetWorkgroups queries, or (block pass) beyond kLdsKeys eligible blocks,
+//    and the token Top-K of kDenseMinQueries or more prompt queries whose pools
+//    are whole prefixes keeps no keys;
+//  * chunked attention: records of fewer than kTargetWorkgroups / 2 items;
+//  * fused layer group: block and token keys, token histograms and records of
+//    fewer than kTargetWorkgroups / 2 items, at contexts up to kMaxCandidates
+//    blocks.
+size_t scratch_bound(const csa2_cfg *c, int n_q, int T, int n_layers)
+{
+    const int n_items = kTargetWorkgroups / 2 - 1;
+    size_t b = 0;
+    // the regimes change at kDenseMinQueries (dense token Top-K) and at
+    // kTargetWorkgroups (no split below it)
+    for (int n : {n_q, std::min(n_q, kTargetWorkgroups - 1), std::min(n_q, kDenseMinQueries - 1)}) {
+        b = std::max(b, plan_index(n, T, c->block, c->pool, c->d_idx).key_bytes);
+        b = std::max(b, plan_topk(n, T, c->block, c->pool, c->top_k, c->d_idx).key_bytes);
+    }
+    const AttendPlan one = plan_attend(1, 1, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
+    const int HG = std::max(1, c->n_heads / 16);
+    const long long att_items = std::min<long long>((long long)n_q * n_layers * HG, n_items);
+    const size_t records = one.chunks ? round_up(one.part_bytes / HG * (size_t)att_items) : 0;
+    b = std::max(b, records);
+    const long long n_elig_max = (long long)(T - 1) / c->block + 1;
+    if (fused_possible(c, T)) {
+        const int n_f = std::min(n_q, n_items);
+        const long long blk_stride = (std::min<long long>(n_elig_max, kMaxCandidates) + 3) / 4 * 4;
+        const long long tok_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
+        const size_t fused = round_up((size_t)n_f * blk_stride * 4) + round_up((size_t)n_f * tok_stride * 4) +
+                             round_up((size_t)n_f * kRadixBins * 4) + records;
+        b = std::max(b, fused);
+    }
+    return round_up(b);
+}
+
+// Upper bound of the head of every call with n_q' <= n_q, T' <= T and
+// n_layers' <= n_layers: the histograms of the queries of a split selection
+// (splits happen below kTargetWorkgroups queries -- for the token Top-K of a
+// prompt whose pools are whole prefixes, only below kDenseMinQueries -- or at
+// any count beyond kLdsKeys eligible blocks, and less often at smaller T'),
+// and of a fused layer group (fewer than kTargetWorkgroups / 2 queries).
+size_t head_bound(const csa2_cfg *c, int n_q, int T)
+{
+    size_t b = 0;
+    for (int n : {n_q, std::min(n_q, kTargetWorkgroups - 1), std::min(n_q, kDenseMinQueries - 1)})
+        if (plan_index(n, T, c->block, c->pool, c->d_idx).split ||
+            plan_topk(n, T, c->block, c->pool, c->top_k, c->d_idx).split)
+            b = std::max(b, hist_bytes(n));
+    if (fused_possible(c, T)) b = std::max(b, hist_bytes(std::min(n_q, kTargetWorkgroups / 2 - 1)));
+    return b;
+}
+
 int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int32_t n_q,
                           const int8_t *q_idx, const int32_t *q_seq, const int32_t *q_pos,
                           const int8_t *k_idx, int8_t *k_blk, int32_t blk_update_begin,
@@ -223,7 +348,7 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
                           const void *v_main, const void *k_swa, const void *v_swa,
                           int32_t swa_first, int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt,
                           int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *ws,
-                          size_t ws_bytes, hipStream_t st, const FusedPlan &f)
+                          size_t ws_bytes, hipStream_t st, const FusedPlan &f, bool launch)
 {
     // the argument checks of the separate stages (nothing launched)
     if (int32_t e = do_index(c, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, n_seq, T, blk_ids, blk_cnt,
@@ -238,9 +363,11 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     if (mode == CSA2_FULL)
         if (int32_t e = do_block_keys(c, k_idx, n_seq, T, blk_update_begin, T / c->block, k_blk, st, false))
             return e;
-    if (!aligned16(ws)) return CSA2_E_ALIGN;
-    uint32_t *head = (uint32_t *)ws;
-    char *tail = (char *)ws + round_up(f.head);
+    Region r;
+    if (int32_t e = carve(ws, ws_bytes, f.head, f.tail, r)) return e;
+    if (!launch) return CSA2_OK;
+    uint32_t *head = r.ctr;
+    char *tail = (char *)r.data;
     uint32_t *blk_keys = (uint32_t *)(tail + f.blk_off);
     uint32_t *tok_keys = (uint32_t *)(tail + f.tok_off);
     uint32_t *tok_hist = (uint32_t *)(tail + f.tok_hist_off);
@@ -287,11 +414,120 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     return hip_status(launch_attend(ap, f.att, c->head_dim, c->dtype, st, true));
 }
 
+// csa2_layer_group with the stream given; launch = false only checks every
+// argument and the workspace of every stage (nothing is launched).
+int32_t layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int32_t n_q, const int8_t *q_idx,
+                    const int32_t *q_seq, const int32_t *q_pos, const int8_t *k_idx, int8_t *k_blk,
+                    int32_t blk_update_begin, int32_t n_seq, int32_t T, const void *q, const void *k_main,
+                    const void *v_main, const void *k_swa, const void *v_swa, int32_t swa_first,
+                    int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt,
+                    void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t st, bool launch_all)
+{
+    if (int32_t e = check_cfg(c)) return e;
+    if (int32_t e = check_sizes(n_q, n_seq, T)) return e;
+    if (mode < CSA2_FULL || mode > CSA2_REINDEX_TOKENS) return CSA2_E_MODE;
+    if (n_layers < 1) return CSA2_E_SHAPE;
+    if (mode != CSA2_SWA && c->top_k < 1) return CSA2_E_MODE;
+    if (n_q == 0) return CSA2_OK;
+    const bool selects = mode == CSA2_FULL || mode == CSA2_REINDEX;
+    const bool tokens_only = mode == CSA2_REINDEX_TOKENS;
+    const bool window_only = mode == CSA2_SWA;
+    if (mode == CSA2_REUSE && (!topk || !topk_cnt)) return CSA2_E_NULL;
+    if (selects) {
+        const FusedPlan f = plan_fused(c, n_q, T, n_layers);
+        if (f.ok && ws && ws_bytes >= f.head + f.tail)
+            return fused_layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk,
+                                     blk_update_begin, n_seq, T, q, k_main, v_main, k_swa, v_swa,
+                                     swa_first, swa_len, blk_ids, blk_cnt, topk, topk_cnt, out, lse,
+                                     ws, ws_bytes, st, f, launch_all);
+    }
+    // every stage is checked before the first launch, then all are launched
+    for (int pass = 0; pass < (launch_all ? 2 : 1); pass++) {
+        const bool launch = pass == 1;
+        if (mode == CSA2_FULL) {
+            if (int32_t e = do_block_keys(c, k_idx, n_seq, T, blk_update_begin, T / c->block,
+                                          k_blk, st, launch))
+                return e;
+        }
+        if (selects) {
+            if (int32_t e = do_index(c, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, n_seq, T, blk_ids,
+                                     blk_cnt, ws, ws_bytes, st, launch,
+                                     mode == CSA2_FULL ? k_blk : nullptr))
+                return e;
+            if (int32_t e = do_topk(c, n_q, q_idx, q_seq, q_pos, k_idx, T, blk_ids, blk_cnt, topk,
+                                    topk_cnt, ws, ws_bytes, st, launch))
+                return e;
+        }
+        if (tokens_only) {   // the shared pool is read, only the token Top-K is fresh
+            if (int32_t e = do_topk(c, n_q, q_idx, q_seq, q_pos, k_idx, T, blk_ids, blk_cnt, topk,
+                                    topk_cnt, ws, ws_bytes, st, launch))
+                return e;
+        }
+        if (int32_t e = do_attend(c, n_layers, n_q, q, q_seq, q_pos, k_main, v_main, n_seq, T,
+                                  k_swa, v_swa, swa_first, swa_len, window_only ? nullptr : topk,
+                                  window_only ? nullptr : topk_cnt, out, lse, ws, ws_bytes, st,
+                                  launch))
+            return e;
+    }
+    return CSA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+int32_t csa2_profile_begin(const char *kernel_filter, int32_t max_launches)
+{
+    if (max_launches < 0 || max_launches > (1 << 16)) return CSA2_E_SHAPE;
+    if (kernel_filter && strlen(kernel_filter) >= sizeof(g_prof_filter)) return CSA2_E_SHAPE;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_armed.store(false);
+    prof_release();
+    strcpy(g_prof_filter, kernel_filter ? kernel_filter : "");
+    g_prof.resize((size_t)max_launches);
+    for (size_t i = 0; i < g_prof.size(); i++) {
+        ProfRec &r = g_prof[i];
+        r.name[0] = 0;
+        if (hipEventCreate(&r.start) != hipSuccess) {
+            g_prof.resize(i);
+            prof_release();
+            return CSA2_E_HIP;
+        }
+        if (hipEventCreate(&r.stop) != hipSuccess) {
+            hipEventDestroy(r.start);
+            g_prof.resize(i);
+            prof_release();
+            return CSA2_E_HIP;
+        }
+    }
+    g_prof_armed.store(true);
+    return CSA2_OK;
+}
+
+int32_t csa2_profile_end(int32_t *n_timed)
+{
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_armed.store(false);
+    for (size_t i = 0; i < g_prof_used; i++)
+        if (hipEventSynchronize(g_prof[i].stop) != hipSuccess) return CSA2_E_HIP;
+    if (n_timed) *n_timed = (int32_t)g_prof_used;
+    return CSA2_OK;
+}
+
+int32_t csa2_profile_record(int32_t i, char *name, int32_t name_len, float *ms)
+{
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_armed.load() || i < 0 || (size_t)i >= g_prof_used) return CSA2_E_SHAPE;
+    const ProfRec &r = g_prof[(size_t)i];
+    if (name && name_len > 0) {
+        strncpy(name, r.name, (size_t)name_len - 1);
+        name[name_len - 1] = 0;
+    }
+    if (ms && hipEventElapsedTime(ms, r.start, r.stop) != hipSuccess) return CSA2_E_HIP;
+    return CSA2_OK;
+}
 
 const char *csa2_status_str(int32_t s)
 {
@@ -314,15 +550,7 @@ int32_t csa2_workspace_bytes(const csa2_cfg *c, int32_t n_q, int32_t T, int32_t 
     if (!bytes) return CSA2_E_NULL;
     if (int32_t e = check_cfg(c)) return e;
     if (n_q < 0 || T < 1 || T > (1 << 24) || n_layers < 1) return CSA2_E_SHAPE;
-    const SelectPlan pi = plan_index(n_q, T, c->block, c->pool, c->d_idx);
-    const SelectPlan pt = plan_topk(n_q, T, c->block, c->pool, c->top_k, c->d_idx);
-    const AttendPlan pa = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
-    const size_t ctr = std::max(select_head_bytes(n_q, pi.split), select_head_bytes(n_q, pt.split));
-    const size_t data = std::max({pi.key_bytes, pt.key_bytes, pa.part_bytes});
-    size_t need = round_up(ctr) + round_up(data);
-    const FusedPlan f = plan_fused(c, n_q, T, n_layers);
-    if (f.ok) need = std::max(need, round_up(f.head) + f.tail);
-    *bytes = need;
+    *bytes = head_bound(c, n_q, T) + scratch_bound(c, n_q, T, n_layers);
     return CSA2_OK;
 }
 
@@ -420,54 +648,9 @@ int32_t csa2_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int3
                          int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *ws,
                          size_t ws_bytes, void *stream)
 {
-    if (int32_t e = check_cfg(c)) return e;
-    if (int32_t e = check_sizes(n_q, n_seq, T)) return e;
-    if (mode < CSA2_FULL || mode > CSA2_REINDEX_TOKENS) return CSA2_E_MODE;
-    if (n_layers < 1) return CSA2_E_SHAPE;
-    if (mode != CSA2_SWA && c->top_k < 1) return CSA2_E_MODE;
-    if (n_q == 0) return CSA2_OK;
-    hipStream_t st = (hipStream_t)stream;
-    const bool selects = mode == CSA2_FULL || mode == CSA2_REINDEX;
-    const bool tokens_only = mode == CSA2_REINDEX_TOKENS;
-    const bool window_only = mode == CSA2_SWA;
-    if (mode == CSA2_REUSE && (!topk || !topk_cnt)) return CSA2_E_NULL;
-    if (selects) {
-        const FusedPlan f = plan_fused(c, n_q, T, n_layers);
-        if (f.ok && ws && ws_bytes >= round_up(f.head) + f.tail)
-            return fused_layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk,
-                                     blk_update_begin, n_seq, T, q, k_main, v_main, k_swa, v_swa,
-                                     swa_first, swa_len, blk_ids, blk_cnt, topk, topk_cnt, out, lse,
-                                     ws, ws_bytes, st, f);
-    }
-    // every stage is checked before the first launch, then all are launched
-    for (int pass = 0; pass < 2; pass++) {
-        const bool launch = pass == 1;
-        if (mode == CSA2_FULL) {
-            if (int32_t e = do_block_keys(c, k_idx, n_seq, T, blk_update_begin, T / c->block,
-                                          k_blk, st, launch))
-                return e;
-        }
-        if (selects) {
-            if (int32_t e = do_index(c, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, n_seq, T, blk_ids,
-                                     blk_cnt, ws, ws_bytes, st, launch,
-                                     mode == CSA2_FULL ? k_blk : nullptr))
-                return e;
-            if (int32_t e = do_topk(c, n_q, q_idx, q_seq, q_pos, k_idx, T, blk_ids, blk_cnt, topk,
-                                    topk_cnt, ws, ws_bytes, st, launch))
-                return e;
-        }
-        if (tokens_only) {   // the shared pool is read, only the token Top-K is fresh
-            if (int32_t e = do_topk(c, n_q, q_idx, q_seq, q_pos, k_idx, T, blk_ids, blk_cnt, topk,
-                                    topk_cnt, ws, ws_bytes, st, launch))
-                return e;
-        }
-        if (int32_t e = do_attend(c, n_layers, n_q, q, q_seq, q_pos, k_main, v_main, n_seq, T,
-                                  k_swa, v_swa, swa_first, swa_len, window_only ? nullptr : topk,
-                                  window_only ? nullptr : topk_cnt, out, lse, ws, ws_bytes, st,
-                                  launch))
-            return e;
-    }
-    return CSA2_OK;
+    return layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, blk_update_begin, n_seq, T, q,
+                       k_main, v_main, k_swa, v_swa, swa_first, swa_len, blk_ids, blk_cnt, topk, topk_cnt, out,
+                       lse, ws, ws_bytes, (hipStream_t)stream, true);
 }
 
 }  // extern "C"

@@ -1263,13 +1263,13 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
     if (pl.rows && !fused_select && p0.topk == nullptr) {
         // window-only layer with many queries: shared windows in LDS
         const long long n_wg = (long long)((p.n_q + kWinQ - 1) / kWinQ) * (p.H / 16) * p.n_layers;
-        hipLaunchKernelGGL(k_attend_window, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kWinWaves * 64), 0, st, p);
+        launch("k_attend_window", k_attend_window, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kWinWaves * 64), st, p);
         return hipGetLastError();
     }
     if (pl.rows && !fused_select && rows_fit) {
         const long long items = (long long)p.n_q * p.n_layers * (p.H / 16);
         const long long n_wg = (items + kRowWaves - 1) / kRowWaves;
-        hipLaunchKernelGGL(k_attend_rows, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kRowWaves * 64), 0, st, p);
+        launch("k_attend_rows", k_attend_rows, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kRowWaves * 64), st, p);
         return hipGetLastError();
     }
     if (pl.chunks) {
@@ -1278,11 +1278,10 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
         p.n_wc = pl.n_wc;
         p.n_splits = p.n_mc + p.n_wc;
         const long long n_wg = (long long)p.n_q_pad * (p.n_mc + (long long)p.n_layers * p.n_wc);
-        if (fused_select) hipLaunchKernelGGL(k_attend_chunks<true>, dim3((unsigned)n_wg), dim3(kCkWaves * 64), 0, st, p);
-        else hipLaunchKernelGGL(k_attend_chunks<false>, dim3((unsigned)n_wg), dim3(kCkWaves * 64), 0, st, p);
+        if (fused_select) launch("k_attend_chunks", k_attend_chunks<true>, dim3((unsigned)n_wg), dim3(kCkWaves * 64), st, p);
+        else launch("k_attend_chunks", k_attend_chunks<false>, dim3((unsigned)n_wg), dim3(kCkWaves * 64), st, p);
         const long long n_rows = (long long)p.n_q_pad * (p.H / 16) * p.n_layers;
-        hipLaunchKernelGGL(k_attend_combine, dim3((unsigned)(n_rows * (16 / kCombineHeads))),
-                           dim3(32 * kCombineHeads), 0, st, p);
+        launch("k_attend_combine", k_attend_combine, dim3((unsigned)(n_rows * (16 / kCombineHeads))), dim3(32 * kCombineHeads), st, p);
         return hipGetLastError();
     }
     if (pl.mfma) {
@@ -1290,17 +1289,17 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
         p.n_splits = 1;
         p.keys_per_split = pl.keys_per_split;
         const long long n_wg = (long long)p.n_q_pad * (p.H / 16) * p.n_layers;
-        if (fused_select) hipLaunchKernelGGL(k_attend_mfma<true>, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
-        else hipLaunchKernelGGL(k_attend_mfma<false>, dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st, p);
+        if (fused_select) launch("k_attend_mfma", k_attend_mfma<true>, dim3((unsigned)n_wg), dim3(kWaves * 64), st, p);
+        else launch("k_attend_mfma", k_attend_mfma<false>, dim3((unsigned)n_wg), dim3(kWaves * 64), st, p);
         return hipGetLastError();
     }
     dim3 grid((unsigned)p.n_q, (unsigned)p.n_layers, (unsigned)ceil_div_i(p.H, 4));
     if (dtype == 0) {
-        if (D == 64) hipLaunchKernelGGL((k_attend_generic<float, 64>), grid, dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((k_attend_generic<float, 128>), grid, dim3(256), 0, st, p);
+        if (D == 64) launch("k_attend_generic", (k_attend_generic<float, 64>), grid, dim3(256), st, p);
+        else launch("k_attend_generic", (k_attend_generic<float, 128>), grid, dim3(256), st, p);
     } else {
-        if (D == 64) hipLaunchKernelGGL((k_attend_generic<uint16_t, 64>), grid, dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((k_attend_generic<uint16_t, 128>), grid, dim3(256), 0, st, p);
+        if (D == 64) launch("k_attend_generic", (k_attend_generic<uint16_t, 64>), grid, dim3(256), st, p);
+        else launch("k_attend_generic", (k_attend_generic<uint16_t, 128>), grid, dim3(256), st, p);
     }
     return hipGetLastError();
 }

@@ -1,11 +1,40 @@
 // internal.h -- host-side declarations shared by the CSA2 translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace csa2 {
+
+// ---- kernel launches
+// Every kernel of the library is launched through launch(), which carries the
+// measurement hook of csa2_profile_begin: while it is armed, launches whose
+// name matches are given HIP start/stop events (hipExtLaunchKernel records
+// the kernel's own execution interval in them).  Launches into a stream that
+// is capturing a graph are never timed.
+bool profile_events(const char *name, hipStream_t st, hipEvent_t &start, hipEvent_t &stop);
+
+// Errors of the launch itself are left for the caller's hipGetLastError().
+template <typename... KArgs, typename... Args>
+inline void launch(const char *name, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                   Args &&...args)
+{
+    std::tuple<KArgs...> held(static_cast<KArgs>(args)...);
+    void *argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    std::apply([&](auto &...a) {
+        int k = 0;
+        ((argv[k++] = (void *)&a), ...);
+    }, held);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (profile_events(name, st, e0, e1))
+        (void)hipExtLaunchKernel((const void *)kernel, grid, block, argv, 0, st, e0, e1, 0);
+    else
+        (void)hipLaunchKernel((const void *)kernel, grid, block, argv, 0, st);
+}
 
 constexpr int kSelectThreads = 512;     // threads of a scoring or many-query selection workgroup
 constexpr int kSelectWideThreads = 1024; // threads of a one-query-per-workgroup select launch (16 keys each)

@@ -1063,20 +1063,20 @@ hipError_t launch_block_keys(const BlockKeysParams &p, int n_seq, int d_idx, hip
     const int n = (p.blk_end - p.blk_begin) * (d_idx / 16);
     if (n <= 0 || n_seq <= 0) return hipSuccess;
     dim3 grid(ceil_div(n, 256), n_seq);
-    if (d_idx == 64) hipLaunchKernelGGL(k_block_keys<64>, grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL(k_block_keys<32>, grid, dim3(256), 0, st, p);
+    if (d_idx == 64) launch("k_block_keys", k_block_keys<64>, grid, dim3(256), st, p);
+    else launch("k_block_keys", k_block_keys<32>, grid, dim3(256), st, p);
     return hipGetLastError();
 }
 
 hipError_t launch_append(const AppendParams &p, hipStream_t st)
 {
     if (p.n_new <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_append_rows, dim3((unsigned)p.n_new), dim3(64), 0, st, p);
+    launch("k_append_rows", k_append_rows, dim3((unsigned)p.n_new), dim3(64), st, p);
     if (p.k_blk) {
         const unsigned per = 64 / (p.d_idx / 16);   // tokens per workgroup
         const dim3 grid((unsigned)((p.n_new + per - 1) / per));
-        if (p.d_idx == 64) hipLaunchKernelGGL(k_append_block_keys<64>, grid, dim3(64), 0, st, p);
-        else hipLaunchKernelGGL(k_append_block_keys<32>, grid, dim3(64), 0, st, p);
+        if (p.d_idx == 64) launch("k_append_block_keys", k_append_block_keys<64>, grid, dim3(64), st, p);
+        else launch("k_append_block_keys", k_append_block_keys<32>, grid, dim3(64), st, p);
     }
     return hipGetLastError();
 }
@@ -1087,16 +1087,16 @@ static void launch_index_t(const IndexParams &p, const SelectPlan &pl, hipStream
     if (pl.all) {
         const long long work = (long long)p.n_q * std::max(p.P / 4, 1);
         const unsigned blocks = (unsigned)std::min<long long>((work + kPoolAllThreads - 1) / kPoolAllThreads, kPoolAllBlocks);
-        hipLaunchKernelGGL((k_pool_all<DIDX>), dim3(std::max(blocks, 1u)), dim3(kPoolAllThreads), 0, st, p);
+        launch("k_pool_all", (k_pool_all<DIDX>), dim3(std::max(blocks, 1u)), dim3(kPoolAllThreads), st, p);
         return;
     }
     dim3 grid((unsigned)(p.n_q * pl.G));
     if (pl.split) {
-        hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
+        launch("k_index_blocks", (k_index_blocks<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), st, p);
         if (with_select)
-            hipLaunchKernelGGL((k_index_select<kSelectWideThreads>), dim3((unsigned)p.n_q), dim3(kSelectWideThreads), 0, st, p);
+            launch("k_index_select", (k_index_select<kSelectWideThreads>), dim3((unsigned)p.n_q), dim3(kSelectWideThreads), st, p);
     } else {
-        hipLaunchKernelGGL((k_index_blocks<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
+        launch("k_index_blocks", (k_index_blocks<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), st, p);
     }
 }
 
@@ -1113,16 +1113,15 @@ template <int DIDX>
 static void launch_topk_t(const TopkParams &p, const SelectPlan &pl, hipStream_t st)
 {
     if (pl.dense) {
-        hipLaunchKernelGGL((k_topk_dense<DIDX>), dim3((unsigned)((p.n_q + kDenseQ - 1) / kDenseQ)),
-                           dim3(kDenseWaves * 64), 0, st, p);
+        launch("k_topk_dense", (k_topk_dense<DIDX>), dim3((unsigned)((p.n_q + kDenseQ - 1) / kDenseQ)), dim3(kDenseWaves * 64), st, p);
         return;
     }
     dim3 grid((unsigned)(p.n_q * pl.G));
     if (pl.split) {
-        hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), 0, st, p);
-        hipLaunchKernelGGL((k_topk_select<kSelectWideThreads>), dim3((unsigned)p.n_q), dim3(kSelectWideThreads), 0, st, p);
+        launch("k_topk_tokens", (k_topk_tokens<kSelectThreads, DIDX, true>), grid, dim3(kSelectThreads), st, p);
+        launch("k_topk_select", (k_topk_select<kSelectWideThreads>), dim3((unsigned)p.n_q), dim3(kSelectWideThreads), st, p);
     } else {
-        hipLaunchKernelGGL((k_topk_tokens<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), 0, st, p);
+        launch("k_topk_tokens", (k_topk_tokens<kSelectThreads, DIDX, false>), grid, dim3(kSelectThreads), st, p);
     }
 }
 
@@ -1147,8 +1146,8 @@ hipError_t launch_pool_tokens(const IndexParams &ip, const TopkParams &tp, int d
     if (ip.n_q <= 0) return hipSuccess;
     const int n_slots = pool_tokens_slots(ip.n_q, ip.P, ip.B);
     const dim3 grid((unsigned)(ip.n_q * ceil_div(ip.P, n_slots)));
-    if (d_idx == 64) hipLaunchKernelGGL(k_pool_tokens<64>, grid, dim3(kSelectWideThreads), 0, st, ip, tp, n_slots);
-    else hipLaunchKernelGGL(k_pool_tokens<32>, grid, dim3(kSelectWideThreads), 0, st, ip, tp, n_slots);
+    if (d_idx == 64) launch("k_pool_tokens", k_pool_tokens<64>, grid, dim3(kSelectWideThreads), st, ip, tp, n_slots);
+    else launch("k_pool_tokens", k_pool_tokens<32>, grid, dim3(kSelectWideThreads), st, ip, tp, n_slots);
     return hipGetLastError();
 }
 
@@ -1157,7 +1156,7 @@ hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t st)
     const size_t n = bytes / sizeof(uint32_t);
     if (n == 0) return hipSuccess;
     const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, st, (uint32_t *)ws, n);
+    launch("k_fill_zero", k_fill_zero, dim3(blocks), dim3(256), st, (uint32_t *)ws, n);
     return hipGetLastError();
 }
 

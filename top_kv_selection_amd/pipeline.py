@@ -261,3 +261,47 @@ def algorithmic_ops(cfg: Config) -> dict:
         keys = win + (0 if mode == "swa" else sel)
         out["attend"].append(int(len(layers) * (keys * H * D * 4).sum()))
     return out
+
+
+def kernel_work(cfg: Config) -> dict:
+    """Algorithmic work of one step per kernel of the library, for the
+    rooflines of bench.py: kernel name -> (unit, amount per step), where unit
+    is "bytes" (decode: every input read once and every output written once,
+    as the kernel that moves it) or "int8_ops" / "bf16_flops" (prompts: the
+    indexer scoring and the attention, 2 ops per multiply-add).  Covers the
+    kernels of the decode layer group (block scoring; pool selection and token
+    scoring; token Top-K and attention with the merge of its chunk records)
+    and of prompts whose pools are whole prefixes (dense token Top-K, row
+    attention, window attention)."""
+    S, T, d, B, P, K, W_, H, D = (cfg.n_seq, cfg.ctx, cfg.d_idx, cfg.block, cfg.pool, cfg.top_k,
+                                  cfg.window, cfg.n_heads, cfg.head_dim)
+    esz = 4 if cfg.dtype == "f32" else 2
+    work = {}
+
+    def add(kernel, unit, amount):
+        u, a = work.get(kernel, (unit, 0))
+        work[kernel] = (unit, a + int(amount))
+
+    if cfg.decode:
+        n_q = cfg.n_q
+        t = T - 1
+        n_elig = t // B + 1
+        own = t - (n_elig - 1) * B + 1
+        pool = min(P, n_elig)
+        n_cand = pool * B - (B - own)
+        sel = min(K, n_cand)
+        per_layer = min(W_, t + 1) * 2 * D * esz + 2 * H * D * esz + H * 4
+        for mode, layers in cfg.groups():
+            if mode in ("full", "reindex"):
+                store = n_q * d if (mode == "full" and own == B) else 0
+                add("k_index_blocks", "bytes", n_q * (d + (n_elig - 1) * d + own * d) + store)
+                add("k_pool_tokens", "bytes", n_q * (d + P * 4 + 4 + n_cand * d))
+                add("k_attend_chunks", "bytes",
+                    n_q * (P * 4 + 4 + K * 4 + 4 + sel * 2 * D * esz + len(layers) * per_layer))
+        return work
+    ops = algorithmic_ops(cfg)
+    for (mode, layers), flops in zip(cfg.groups(), ops["attend"]):
+        add("k_attend_window" if mode == "swa" else "k_attend_rows", "bf16_flops", flops)
+    for n in ops["topk_tokens"]:
+        add("k_topk_dense", "int8_ops", n)
+    return work
