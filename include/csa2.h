@@ -270,6 +270,28 @@ int32_t csa2_layer_group(const csa2_cfg *cfg, int32_t mode, int32_t n_layers, in
                          int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* csa2_layer_group without a workspace argument, for callers that cannot
+ * allocate device memory: code under graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine): its scratch is a 16 MiB device
+ * array inside the library (one per GPU, held until the process ends), whose
+ * address is looked up once per device on the first call with that device
+ * current.  Arguments, results and errors are those of csa2_layer_group; a
+ * call whose stages need more than the 16 MiB returns CSA2_E_WORKSPACE
+ * without launching anything (16 MiB holds the decode layer group at batch
+ * 8 and 128K context with room to spare).  The histograms at the head of the
+ * array are cleared by a kernel at the start of every call that selects.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and give undefined
+ * results; calls issued in order on one stream are safe. */
+int32_t csa2_layer_group_static(const csa2_cfg *cfg, int32_t mode, int32_t n_layers, int32_t n_q,
+                                const int8_t *q_idx, const int32_t *q_seq, const int32_t *q_pos,
+                                const int8_t *k_idx, int8_t *k_blk, int32_t blk_update_begin,
+                                int32_t n_seq, int32_t T, const void *q, const void *k_main,
+                                const void *v_main, const void *k_swa, const void *v_swa,
+                                int32_t swa_first, int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt,
+                                int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

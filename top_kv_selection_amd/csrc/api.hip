@@ -61,6 +61,36 @@ bool profile_events(const char *name, hipStream_t st, hipEvent_t &start, hipEven
 }
 }  // namespace csa2
 
+// ---- scratch of csa2_layer_group_static: a file-scope device array (each
+// GPU the library runs on holds its own copy until the process ends).  Host
+// code never uses the array's name as an address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress, taken once per device with that
+// device current, and is what the kernels receive.
+static constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array.
+int32_t static_scratch(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return CSA2_E_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return CSA2_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA2_E_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return CSA2_OK;
+}
+}  // namespace
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -651,6 +681,41 @@ int32_t csa2_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int3
     return layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, blk_update_begin, n_seq, T, q,
                        k_main, v_main, k_swa, v_swa, swa_first, swa_len, blk_ids, blk_cnt, topk, topk_cnt, out,
                        lse, ws, ws_bytes, (hipStream_t)stream, true);
+}
+
+int32_t csa2_layer_group_static(const csa2_cfg *c, int32_t mode, int32_t n_layers, int32_t n_q,
+                                const int8_t *q_idx, const int32_t *q_seq, const int32_t *q_pos,
+                                const int8_t *k_idx, int8_t *k_blk, int32_t blk_update_begin,
+                                int32_t n_seq, int32_t T, const void *q, const void *k_main,
+                                const void *v_main, const void *k_swa, const void *v_swa,
+                                int32_t swa_first, int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt,
+                                int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    void *ws = nullptr;
+    if (int32_t e = static_scratch(&ws)) return e;
+    // every argument, and every stage's room in the scratch, first
+    if (int32_t e = layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, blk_update_begin,
+                                n_seq, T, q, k_main, v_main, k_swa, v_swa, swa_first, swa_len, blk_ids, blk_cnt,
+                                topk, topk_cnt, out, lse, ws, kStaticScratchBytes, st, false))
+        return e;
+    if (n_q == 0) return CSA2_OK;
+    // The array keeps the previous call's contents: the histograms at its
+    // head must start at zero, so they are cleared (with a kernel, which a
+    // graph capture may record) for the calls whose selections use them.
+    const bool selects = mode == CSA2_FULL || mode == CSA2_REINDEX || mode == CSA2_REINDEX_TOKENS;
+    if (selects) {
+        const FusedPlan f = plan_fused(c, n_q, T, n_layers);
+        const bool uses_head = (f.ok && f.head + f.tail <= kStaticScratchBytes) ||
+                               plan_index(n_q, T, c->block, c->pool, c->d_idx).split ||
+                               plan_topk(n_q, T, c->block, c->pool, c->top_k, c->d_idx).split;
+        if (uses_head)
+            if (int32_t e = hip_status(launch_fill_zero(ws, std::min(hist_bytes(n_q), kStaticScratchBytes), st)))
+                return e;
+    }
+    return layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, blk_update_begin, n_seq, T, q,
+                       k_main, v_main, k_swa, v_swa, swa_first, swa_len, blk_ids, blk_cnt, topk, topk_cnt, out,
+                       lse, ws, kStaticScratchBytes, st, true);
 }
 
 }  // extern "C"
