@@ -134,16 +134,24 @@ int32_t csa2_profile_begin(const char *kernel_filter, int32_t max_launches);
 int32_t csa2_profile_end(int32_t *n_timed);
 int32_t csa2_profile_record(int32_t i, char *name, int32_t name_len, float *ms);
 
-/* Bytes of workspace needed by any call below for n_q query rows against
- * caches of T positions and n_layers layers per group call.  Writes *bytes. */
+/* Bytes of workspace for calls of at most n_q query rows, caches of at most T
+ * positions and at most n_layers layers per group call: an upper bound of
+ * every such call's zero-between-calls head plus an upper bound of its
+ * scratch, so one workspace of this size serves any sequence of them in
+ * stream order.  Writes *bytes.  (Plumbing of the library, not a step of the
+ * method.) */
 int32_t csa2_workspace_bytes(const csa2_cfg *cfg, int32_t n_q, int32_t T, int32_t n_layers,
                              size_t *bytes);
 
 /* Zero-fills `bytes` of device memory at `ws` with a kernel (safe to record
- * into a HIP graph). */
+ * into a HIP graph).  `ws` 4-byte aligned, `bytes` a multiple of 4.  (Plumbing,
+ * not a step of the method.) */
 int32_t csa2_workspace_init(void *ws, size_t bytes, void *stream);
 
-/* Block keys (the block-level indexer keys the hierarchical pass scores).
+/* Block keys (the block-level indexer keys the hierarchical pass scores;
+ * "Hierarchical indexer" key fact of the page "DeepSeek V4.1 Flash" and the
+ * forum summary's blocks of candidates; the key of a block is fixed here as
+ * the rounded mean of its k_idx rows).
  * For each sequence s < n_seq and each block j in [blk_begin, blk_end) that
  * is complete ((j+1)*B <= T):
  *     k_blk[s][j][c] = round_half_even(mean over p in [jB, jB+B) of k_idx[s][p][c])
@@ -180,7 +188,11 @@ int32_t csa2_append_tokens(const csa2_cfg *cfg, int32_t n_new, const int32_t *se
                            void *k_main, void *v_main, int8_t *k_blk, int32_t n_seq, int32_t T,
                            void *stream);
 
-/* Hierarchical block pass.  For query row i at position t = q_pos[i] in
+/* Hierarchical block pass ("Hierarchical indexer" key fact of the page
+ * "DeepSeek V4.1 Flash": a block-level pass bounds the candidates an indexer
+ * scores, at most P*B tokens whatever the context length; the forum summary's
+ * hierarchical sparse indexer that narrows candidates down to blocks).
+ * For query row i at position t = q_pos[i] in
  * sequence s = q_seq[i], the eligible blocks are j = 0 .. t/B (each holds at
  * least one visible token).  If there are at most P of them, all are pooled;
  * otherwise the P with the highest block score, ties to the lower block id.
@@ -190,19 +202,26 @@ int32_t csa2_append_tokens(const csa2_cfg *cfg, int32_t n_new, const int32_t *se
  *   q_seq, q_pos : device int32 [n_q]
  *   k_idx   : device int8  [n_seq][T][d_idx]
  *   k_blk   : device int8  [n_seq][T/B][d_idx], blocks < t/B filled
- *   blk_ids : device int32 [n_q][P] out: pooled block ids ascending, then -1
+ *   blk_ids : device int32 [n_q][P] out: pooled block ids ascending, then -1;
+ *             may be NULL when every pool is the whole prefix ((T-1)/B + 1 <=
+ *             P): the pool of row i is then blocks 0 .. blk_cnt[i]-1 and no id
+ *             is stored (CSA2_E_NULL otherwise)
  *   blk_cnt : device int32 [n_q]    out: number of pooled blocks           */
 int32_t csa2_index_blocks(const csa2_cfg *cfg, int32_t n_q, const int8_t *q_idx,
                           const int32_t *q_seq, const int32_t *q_pos, const int8_t *k_idx,
                           const int8_t *k_blk, int32_t n_seq, int32_t T, int32_t *blk_ids,
                           int32_t *blk_cnt, void *ws, size_t ws_bytes, void *stream);
 
-/* Token Top-K.  The candidates of query row i are the visible positions
+/* Token Top-K ("Sparse attention" key fact of the page "DeepSeek V4.1
+ * Flash": each query keeps its Top-K main-KV entries; "Hierarchical indexer":
+ * only the tokens of the pooled blocks are scored).
+ * The candidates of query row i are the visible positions
  * (p <= t) of its pooled blocks.  If there are at most K, all are selected;
  * otherwise the K with the highest token score, ties to the lower position.
  *   blk_ids, blk_cnt : as written by csa2_index_blocks for the same cfg, T and
- *                      queries (when every pool is the whole prefix, i.e.
- *                      (T-1)/B + 1 <= P, they are not read)
+ *                      queries; blk_ids may be NULL when every pool is the
+ *                      whole prefix ((T-1)/B + 1 <= P), pool slot r then
+ *                      holds block r (the many-query kernel reads neither)
  *   topk     : device int32 [n_q][K] out: selected positions ascending, then -1
  *   topk_cnt : device int32 [n_q]    out: number selected                   */
 int32_t csa2_topk_tokens(const csa2_cfg *cfg, int32_t n_q, const int8_t *q_idx,
@@ -213,6 +232,10 @@ int32_t csa2_topk_tokens(const csa2_cfg *cfg, int32_t n_q, const int8_t *q_idx,
 
 /* Sparse attention for a group of n_layers layers that share one index set
  * and one main K/V cache (the layer-group call; n_layers = 1 is one layer).
+ * "Sparse attention" key fact of the page "DeepSeek V4.1 Flash" (each query
+ * attends to its Top-K main entries plus a sliding window) and the mode table
+ * of "CSA2 with cross-layer reuse" (layers that share the main KV and the
+ * indices; every layer has its own Q and its own window K/V).
  * For layer l, query row i, head h: one softmax over
  *   - main entries p in topk[i][0 .. topk_cnt[i]) with k_main/v_main rows of
  *     sequence q_seq[i] (skipped when topk is NULL: a window-only layer), and
@@ -233,7 +256,12 @@ int32_t csa2_attend_group(const csa2_cfg *cfg, int32_t n_layers, int32_t n_q, co
                           const int32_t *topk, const int32_t *topk_cnt, void *out, float *lse,
                           void *ws, size_t ws_bytes, void *stream);
 
-/* One layer: csa2_attend_group with n_layers = 1. */
+/* One layer: csa2_attend_group with n_layers = 1 (same passages).  It takes
+ * no layer mode: in the mode table of "CSA2 with cross-layer reuse" the
+ * three modes attend identically and differ only in where the indices come
+ * from (fresh for Full and Reindex, shared for Reuse), so the caller passes
+ * the indices of whichever layer selected them; csa2_layer_group carries the
+ * mode and does the selection the mode asks for. */
 int32_t csa2_attend(const csa2_cfg *cfg, int32_t n_q, const void *q, const int32_t *q_seq,
                     const int32_t *q_pos, const void *k_main, const void *v_main, int32_t n_seq,
                     int32_t T, const void *k_swa, const void *v_swa, int32_t swa_first,
@@ -260,7 +288,8 @@ int32_t csa2_attend(const csa2_cfg *cfg, int32_t n_q, const void *q, const int32
  *                  Reindex layer that recomputes only the token Top-K
  * blk_ids/blk_cnt/topk/topk_cnt are outputs for FULL/REINDEX, inputs for
  * REUSE; for REINDEX_TOKENS blk_ids/blk_cnt are inputs and topk/topk_cnt
- * outputs.  Shapes as in the calls above. */
+ * outputs.  Shapes as in the calls above; blk_ids may be NULL when every pool
+ * is the whole prefix ((T-1)/B + 1 <= P), as in csa2_index_blocks. */
 int32_t csa2_layer_group(const csa2_cfg *cfg, int32_t mode, int32_t n_layers, int32_t n_q,
                          const int8_t *q_idx, const int32_t *q_seq, const int32_t *q_pos,
                          const int8_t *k_idx, int8_t *k_blk, int32_t blk_update_begin,

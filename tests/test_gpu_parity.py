@@ -65,12 +65,8 @@ def test_decoder_pattern_64k(lib):
     check(lib, W.CONFIGS["decoder_pattern_64k"])
 
 
-def test_prefill_8k_sampled_rows(lib):
-    cfg = W.CONFIGS["prefill_8k"]
-    rng = np.random.default_rng(4)
-    edges = [0, 1, 7, 8, 9, 63, 64, 127, 128, 129, 511, 512, 513, 1023, 4095, 8190, 8191]
-    rows = np.unique(np.concatenate([edges, rng.choice(cfg.n_q, 80, replace=False)]))
-    check(lib, cfg, rows=rows)
+def test_prefill_8k_all_rows(lib):
+    check(lib, W.CONFIGS["prefill_8k"])
 
 
 # ------------------------------------------------------------------ scaled cases
@@ -151,12 +147,8 @@ def test_encoder_pattern_scaled_all_rows(lib):
     check(lib, cfg, seed=50)
 
 
-def test_encoder_prefill_8k_sampled_rows(lib):
-    cfg = W.CONFIGS["encoder_prefill_8k"]
-    rng = np.random.default_rng(6)
-    edges = [0, 1, 7, 8, 127, 128, 1023, 1024, 4095, 8190, 8191]
-    rows = np.unique(np.concatenate([edges, rng.choice(cfg.n_q, 40, replace=False)]))
-    check(lib, cfg, rows=rows)
+def test_encoder_prefill_8k_all_rows(lib):
+    check(lib, W.CONFIGS["encoder_prefill_8k"])
 
 
 def test_decoder_replay_8k(lib):
@@ -251,10 +243,26 @@ def test_prefill_dense_topk_longest_context(lib):
 
 def test_decode_more_blocks_than_one_workgroup_holds(lib):
     """Blocks of 2 at a 40,000-token context: 20,000 eligible blocks, more than
-    the 16,384 keys one selection workgroup keeps in registers, so the pool is
-    chosen by the streaming two-pass path over the workspace keys."""
+    16,384 keys per selection workgroup, so the layer group keeps 32 block keys
+    per thread of its pool selection."""
     cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=2, ctx=40000, block=2, pool=4096, top_k=512)
     check(lib, cfg, seed=34)
+
+
+def test_decode_group_256k_batch_8(lib):
+    """The 128K layer group's shapes (batch 8, Full + 5 Reuse, blocks of 8,
+    pool 2,048, Top-512, window 128) at a 262,144-token context: 32,768
+    eligible blocks per query, the most the fused layer group takes."""
+    check(lib, W.CONFIGS["decode_group_256k"])
+
+
+def test_decode_past_the_fused_limit(lib):
+    """280,000 tokens in blocks of 8 (35,000 eligible blocks, past the fused
+    layer group's 32,768): the block pass, pool selection, token Top-K and
+    attention run as separate launches, and the pool is chosen by the
+    streaming two-pass path over the workspace keys."""
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=2, ctx=280000, layers=("full", "reuse"))
+    check(lib, cfg, seed=35)
 
 
 def test_prefill_window_layer_chunks_and_mixed_tiles(lib):
@@ -462,7 +470,7 @@ def test_fused_layer_group_equals_separate_calls(lib, name, kw):
     torch.cuda.synchronize()
     grp = dw.groups[0]
     lc = dw.lcfg
-    ids = torch.empty_like(dw.blk_ids[0]); cnt = torch.empty_like(dw.blk_cnt[0])
+    ids = torch.empty((cfg.n_q, cfg.pool), dtype=torch.int32, device="cuda"); cnt = torch.empty_like(dw.blk_cnt[0])
     tk = torch.empty_like(dw.topk[0]); tc = torch.empty_like(dw.topk_cnt[0])
     out = torch.empty_like(grp.out); lse = torch.empty_like(grp.lse)
     B.csa2_index_blocks(lc, grp.q_idx, dw.q_seq, dw.q_pos, dw.k_idx, dw.k_blk, ids, cnt, dw.ws)
@@ -470,8 +478,47 @@ def test_fused_layer_group_equals_separate_calls(lib, name, kw):
     B.csa2_attend_group(lc, grp.q, dw.q_seq, dw.q_pos, dw.k_main, dw.v_main, grp.k_swa, grp.v_swa,
                         cfg.swa_first, tk, tc, out, lse, dw.ws)
     torch.cuda.synchronize()
-    assert torch.equal(cnt, dw.blk_cnt[0]) and torch.equal(ids, dw.blk_ids[0])
+    assert torch.equal(cnt, dw.blk_cnt[0])
+    if dw.blk_ids[0] is not None:
+        assert torch.equal(ids, dw.blk_ids[0])
+    else:   # the layer group stored no ids: the standalone pass writes blocks 0 .. cnt-1
+        slots = torch.arange(cfg.pool, device="cuda", dtype=torch.int32)[None, :]
+        assert torch.equal(ids, torch.where(slots < cnt[:, None], slots, torch.full_like(slots, -1)))
     assert torch.equal(tc, dw.topk_cnt[0]) and torch.equal(tk, dw.topk[0])
     assert torch.equal(out, grp.out) and torch.equal(lse, grp.lse)
     ref = oracle.run_layers(wl)
     compare_run(pipeline.outputs(dw), ref, cfg, what="fused")
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_unstored_pool_ids_give_the_same_selection(lib, decode):
+    """Every pool is the whole prefix: a layer group that stores the pool ids
+    and one that stores none (blk_cnt describes the pool) select the same
+    tokens and attend identically; the stored ids are blocks 0 .. cnt-1."""
+    B, pipeline = lib
+    base = W.CONFIGS["decode_full_32k" if decode else "prefill_8k"]
+    kw = dict(n_seq=5, ctx=1500, pool=200, top_k=300, window=50) if decode else \
+        dict(ctx=1500, pool=200, top_k=300, window=50, layers=("full", "reuse"))
+    cfg = W.scaled(base, **kw)
+    print(f"case unstored pool ids decode={decode} n_q={cfg.n_q}", flush=True)
+    wl = W.generate(cfg, seed=37)
+    dw = pipeline.upload(wl)
+    pipeline.build_cache(dw)
+    assert dw.blk_ids[0] is None                    # the pipeline stores none here
+    pipeline.run(dw)
+    torch.cuda.synchronize()
+    grp = dw.groups[0]
+    ids = torch.full((cfg.n_q, cfg.pool), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.empty_like(dw.blk_cnt[0])
+    tk = torch.empty_like(dw.topk[0]); tc = torch.empty_like(dw.topk_cnt[0])
+    out = torch.empty_like(grp.out); lse = torch.empty_like(grp.lse)
+    B.csa2_layer_group(dw.lcfg, "full", grp.q_idx, dw.q_seq, dw.q_pos, dw.k_idx, dw.k_blk,
+                       pipeline.step_update_begin(dw), grp.q, dw.k_main, dw.v_main, grp.k_swa, grp.v_swa,
+                       cfg.swa_first, ids, cnt, tk, tc, out, lse, dw.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt, dw.blk_cnt[0])
+    assert torch.equal(tk, dw.topk[0]) and torch.equal(tc, dw.topk_cnt[0])
+    assert torch.equal(out, grp.out) and torch.equal(lse, grp.lse)
+    slots = torch.arange(cfg.pool, device="cuda", dtype=torch.int32)[None, :]
+    assert torch.equal(ids, torch.where(slots < cnt[:, None], slots, torch.full_like(slots, -1)))
+    compare_run(pipeline.outputs(dw), oracle.run_layers(wl), cfg, what="unstored pool ids")

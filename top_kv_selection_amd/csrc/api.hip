@@ -168,11 +168,12 @@ int32_t do_index(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int3
                  int32_t T, int32_t *blk_ids, int32_t *blk_cnt, void *ws, size_t ws_bytes,
                  hipStream_t st, bool launch, int8_t *k_blk_store = nullptr)
 {
-    if (!q_idx || !q_seq || !q_pos || !k_idx || !k_blk || !blk_ids || !blk_cnt) return CSA2_E_NULL;
+    const SelectPlan pl = plan_index(n_q, T, c->block, c->pool, c->d_idx);
+    // the ids may be left unstored only where every pool is the whole prefix
+    if (!q_idx || !q_seq || !q_pos || !k_idx || !k_blk || !blk_cnt || (!blk_ids && !pl.all)) return CSA2_E_NULL;
     if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(k_blk) || !aligned4(q_seq) ||
         !aligned4(q_pos) || !aligned4(blk_ids) || !aligned4(blk_cnt))
         return CSA2_E_ALIGN;
-    const SelectPlan pl = plan_index(n_q, T, c->block, c->pool, c->d_idx);
     Region r;
     if (int32_t e = carve(ws, ws_bytes, select_head_bytes(n_q, pl.split), pl.key_bytes, r)) return e;
     if (!launch) return CSA2_OK;
@@ -194,7 +195,8 @@ int32_t do_topk(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32
                 size_t ws_bytes, hipStream_t st, bool launch)
 {
     if (c->top_k < 1) return CSA2_E_SHAPE;
-    if (!q_idx || !q_seq || !q_pos || !k_idx || !blk_ids || !blk_cnt || !topk || !topk_cnt)
+    const bool whole_prefix = (long long)(T - 1) / c->block + 1 <= c->pool;
+    if (!q_idx || !q_seq || !q_pos || !k_idx || !blk_cnt || !topk || !topk_cnt || (!blk_ids && !whole_prefix))
         return CSA2_E_NULL;
     if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned4(q_seq) || !aligned4(q_pos) ||
         !aligned4(blk_ids) || !aligned4(blk_cnt) || !aligned4(topk) || !aligned4(topk_cnt))
@@ -280,7 +282,7 @@ FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
     f.idx = plan_index(n_q, T, c->block, c->pool, c->d_idx);
     f.tok = plan_topk(n_q, T, c->block, c->pool, c->top_k, c->d_idx);
     f.att = plan_attend(n_q, n_layers, c->n_heads, c->head_dim, c->top_k, c->window, c->dtype);
-    f.ok = c->top_k >= 1 && f.idx.split && f.tok.split && n_elig_max <= kMaxCandidates && f.att.mfma && !f.att.rows &&
+    f.ok = c->top_k >= 1 && f.idx.split && f.tok.split && n_elig_max <= kFusedEligMax && f.att.mfma && !f.att.rows &&
            (f.att.chunks || f.att.keys_per_split <= kAttendRowChunk) && c->pool <= kFusedPoolLds;
     f.blk_stride = (n_elig_max + 3) / 4 * 4;
     f.tok_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
@@ -325,7 +327,7 @@ bool fused_possible(const csa2_cfg *c, int T)
 //    are whole prefixes keeps no keys;
 //  * chunked attention: records of fewer than kTargetWorkgroups / 2 items;
 //  * fused layer group: block and token keys, token histograms and records of
-//    fewer than kTargetWorkgroups / 2 items, at contexts up to kMaxCandidates
+//    fewer than kTargetWorkgroups / 2 items, at contexts up to kFusedEligMax
 //    blocks.
 size_t scratch_bound(const csa2_cfg *c, int n_q, int T, int n_layers)
 {
@@ -345,7 +347,7 @@ size_t scratch_bound(const csa2_cfg *c, int n_q, int T, int n_layers)
     const long long n_elig_max = (long long)(T - 1) / c->block + 1;
     if (fused_possible(c, T)) {
         const int n_f = std::min(n_q, n_items);
-        const long long blk_stride = (std::min<long long>(n_elig_max, kMaxCandidates) + 3) / 4 * 4;
+        const long long blk_stride = (std::min<long long>(n_elig_max, kFusedEligMax) + 3) / 4 * 4;
         const long long tok_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
         const size_t fused = round_up((size_t)n_f * blk_stride * 4) + round_up((size_t)n_f * tok_stride * 4) +
                              round_up((size_t)n_f * kRadixBins * 4) + records;

@@ -163,10 +163,11 @@ constexpr int kDenseMaxT = 16384;       // longest context of the dense (MFMA ti
 constexpr int kDenseMinQueries = 256;   // queries per call below which the per-query kernels run
 constexpr int kAttendRowChunk = 2048;   // key-list entries one attention workgroup stages at once
 constexpr int kFusedPoolLds = 2048;     // pooled block ids the fused attention keeps in LDS
+constexpr int kFusedEligMax = 32768;    // eligible blocks per query the fused layer group takes (256K tokens at B = 8)
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t st);
 // Layer-group decode: pool selection (from a split block pass's keys and
 // histogram) and token scoring in one launch; ceil(P / pool_tokens_slots)
-// workgroups per query.  Requires n_elig_max <= kLdsKeys and P <= kFusedPoolLds.
+// workgroups per query.  Requires n_elig_max <= kFusedEligMax and P <= kFusedPoolLds.
 int pool_tokens_slots(int n_q, int P, int B);
 hipError_t launch_pool_tokens(const IndexParams &ip, const TopkParams &tp, int d_idx, hipStream_t st);
 

@@ -261,7 +261,8 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
 // Pools when every eligible block of every query fits (n_elig <= P for the
 // longest context): the pool of a query is its blocks 0 .. t/B, so no score
 // is needed.  A grid-stride kernel writes the ids (then -1 padding), 16 bytes
-// per store when the rows allow it, and the counts; a Full layer also stores
+// per store when the rows allow it, unless the caller stores no ids (the
+// count then describes the pool), and the counts; a Full layer also stores
 // the key of the block its query completes.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPoolAllThreads = 256;
@@ -273,7 +274,9 @@ __global__ __launch_bounds__(kPoolAllThreads) void k_pool_all(IndexParams p)
     const size_t stride = (size_t)gridDim.x * kPoolAllThreads;
     const size_t id = (size_t)blockIdx.x * kPoolAllThreads + threadIdx.x;
     const bool vec = (p.P % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.blk_ids) & 15) == 0);
-    if (vec) {
+    if (p.blk_ids == nullptr) {
+        // the pools are not stored: blk_cnt alone describes them
+    } else if (vec) {
         const int P4 = p.P / 4;
         const size_t total = (size_t)p.n_q * P4;
         for (size_t k = id; k < total; k += stride) {
@@ -354,16 +357,18 @@ __device__ void topk_finish(const TopkParams &p, int q, const uint32_t (&k)[IPT]
 {
     const int tid = threadIdx.x, B = p.B;
     const int n_pool = p.blk_cnt[q];
-    const int32_t *pool = p.blk_ids + (size_t)q * p.P;
+    // no stored ids: every pool is the whole prefix, slot r holds block r
+    const bool implicit = p.blk_ids == nullptr;
+    const int32_t *pool = implicit ? nullptr : p.blk_ids + (size_t)q * p.P;
     const bool pool_in_lds = n_pool <= kPoolLds;
     if (pool_in_lds)
-        for (int r = tid; r < n_pool; r += NT) s_pool[r] = pool[r];
+        for (int r = tid; r < n_pool; r += NT) s_pool[r] = implicit ? r : pool[r];
     const Threshold th = threshold_regs<NT, IPT>(k, n_cand, (uint32_t)p.K, s_hist, s_sm);
     int32_t *out = p.topk + (size_t)q * p.K;
     const uint32_t cap = (uint32_t)p.K;
     auto emit = [&](uint32_t slot, int i) {
         const int r = i / B;
-        const int blk = pool_in_lds ? s_pool[r] : pool[r];
+        const int blk = pool_in_lds ? s_pool[r] : (implicit ? r : pool[r]);
         if (slot < cap) out[slot] = blk * B + (i - r * B);
     };
     const uint32_t chosen = compact_regs<NT, IPT>(k, th, emit, s_sm);
@@ -386,7 +391,8 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
     const int B = p.B;
     const int n_pool = p.blk_cnt[q];
     const int n_cand = n_pool * B;                    // <= P*B <= kLdsKeys
-    const int32_t *pool = p.blk_ids + (size_t)q * p.P;
+    const bool implicit = p.blk_ids == nullptr;       // every pool is the whole prefix
+    const int32_t *pool = implicit ? nullptr : p.blk_ids + (size_t)q * p.P;
     // the histogram is cleared now; the barrier that orders the clearing
     // before the first count comes after the first batch's loads are issued
     for (int b = tid; b < kHist2Words; b += NT) s_hist[b] = 0;
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             cl[u] = min(base + u * RPP + tid / LPR, hi_w - 1);
-            blk[u] = pool[cl[u] / B];
+            blk[u] = implicit ? cl[u] / B : pool[cl[u] / B];
         }
         // the query's sequence and count are first used here, so the wait for
         // them stays behind the pool loads (the empty asm keeps the compiler
@@ -473,10 +479,10 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
 constexpr int kPoolTokCand = 512;
 constexpr int kPoolTokMaxWorkgroups = 256;   // one 1,024-thread workgroup per CU
 
-template <int DIDX>
+template <int DIDX, int IPT>
 __global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams ip, TopkParams tp, int n_slots)
 {
-    constexpr int NT = kSelectWideThreads, IPT = kLdsKeys / NT;
+    constexpr int NT = kSelectWideThreads;
     constexpr int LPR = DIDX / 16, RPP = NT / LPR;
     __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
     __shared__ int32_t s_pool[kFusedPoolLds];
@@ -1146,8 +1152,18 @@ hipError_t launch_pool_tokens(const IndexParams &ip, const TopkParams &tp, int d
     if (ip.n_q <= 0) return hipSuccess;
     const int n_slots = pool_tokens_slots(ip.n_q, ip.P, ip.B);
     const dim3 grid((unsigned)(ip.n_q * ceil_div(ip.P, n_slots)));
-    if (d_idx == 64) launch("k_pool_tokens", k_pool_tokens<64>, grid, dim3(kSelectWideThreads), st, ip, tp, n_slots);
-    else launch("k_pool_tokens", k_pool_tokens<32>, grid, dim3(kSelectWideThreads), st, ip, tp, n_slots);
+    // the block keys of a query sit in registers: 16 per thread up to 16,384
+    // eligible blocks, 32 per thread up to kFusedEligMax
+    const bool wide = (long long)(ip.T - 1) / ip.B + 1 > kLdsKeys;
+    constexpr int IPT = kLdsKeys / kSelectWideThreads;
+    static_assert(2 * kLdsKeys == kFusedEligMax, "two register key sets cover the fused limit");
+    if (d_idx == 64) {
+        if (wide) launch("k_pool_tokens", k_pool_tokens<64, 2 * IPT>, grid, dim3(kSelectWideThreads), st, ip, tp, n_slots);
+        else launch("k_pool_tokens", k_pool_tokens<64, IPT>, grid, dim3(kSelectWideThreads), st, ip, tp, n_slots);
+    } else {
+        if (wide) launch("k_pool_tokens", k_pool_tokens<32, 2 * IPT>, grid, dim3(kSelectWideThreads), st, ip, tp, n_slots);
+        else launch("k_pool_tokens", k_pool_tokens<32, IPT>, grid, dim3(kSelectWideThreads), st, ip, tp, n_slots);
+    }
     return hipGetLastError();
 }
 

@@ -62,6 +62,12 @@ class DeviceWorkload:
     ws: torch.Tensor = None
 
 
+def whole_prefix_pools(cfg: Config) -> bool:
+    """Every query's pool is all of its eligible blocks (the longest context
+    has at most P blocks): the library then needs no stored pool ids."""
+    return (cfg.ctx - 1) // cfg.block + 1 <= cfg.pool
+
+
 def group_caches(cfg: Config) -> list:
     """Cache of each layer group: a Full layer opens its own main-KV and
     indexer cache, and the groups after it share that cache until the next
@@ -108,7 +114,10 @@ def upload(wl: Workload, device="cuda", q_idx=None, q=None) -> DeviceWorkload:
             grp.q_idx = _dev(q_idx[layers[0]], device)
             g = len(dw.groups)
             if mode != "reindex_tokens":   # a token-only Reindex group reads the shared pool
-                dw.blk_ids[g] = torch.empty((cfg.n_q, cfg.pool), dtype=torch.int32, device=device)
+                # when every pool is the whole prefix the count describes it
+                # and no ids are stored
+                dw.blk_ids[g] = None if whole_prefix_pools(cfg) else \
+                    torch.empty((cfg.n_q, cfg.pool), dtype=torch.int32, device=device)
                 dw.blk_cnt[g] = torch.empty(cfg.n_q, dtype=torch.int32, device=device)
             dw.topk[g] = torch.empty((cfg.n_q, cfg.top_k), dtype=torch.int32, device=device)
             dw.topk_cnt[g] = torch.empty(cfg.n_q, dtype=torch.int32, device=device)
@@ -173,8 +182,14 @@ def outputs(dw: DeviceWorkload):
             out[layer], lse[layer] = o[j], l[j]
         if g in dw.topk:
             pg = grp.pool_of if grp.mode == "reindex_tokens" else g
+            cnt = dw.blk_cnt[pg].cpu().numpy()
+            if dw.blk_ids[pg] is None:     # unstored: pool slot r holds block r
+                slots = np.arange(dw.cfg.pool, dtype=np.int32)
+                ids = np.where(slots[None, :] < cnt[:, None], slots[None, :], -1).astype(np.int32)
+            else:
+                ids = dw.blk_ids[pg].cpu().numpy()
             index[grp.layers[0]] = {
-                "blk_ids": dw.blk_ids[pg].cpu().numpy(), "blk_cnt": dw.blk_cnt[pg].cpu().numpy(),
+                "blk_ids": ids, "blk_cnt": cnt,
                 "topk": dw.topk[g].cpu().numpy(), "topk_cnt": dw.topk_cnt[g].cpu().numpy()}
     return {"out": out, "lse": lse, "index": index}
 
@@ -196,7 +211,7 @@ def replicate(dw: DeviceWorkload, q_idx=None, q=None) -> DeviceWorkload:
         if grp.q_idx is not None:
             ng.q_idx = grp.q_idx.clone() if q_idx is None else _dev(q_idx[grp.layers[0]], dev)
             if g in dw.blk_ids:
-                new.blk_ids[g] = torch.empty_like(dw.blk_ids[g])
+                new.blk_ids[g] = None if dw.blk_ids[g] is None else torch.empty_like(dw.blk_ids[g])
                 new.blk_cnt[g] = torch.empty_like(dw.blk_cnt[g])
             new.topk[g] = torch.empty_like(dw.topk[g])
             new.topk_cnt[g] = torch.empty_like(dw.topk_cnt[g])

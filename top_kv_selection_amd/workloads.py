@@ -25,6 +25,11 @@ decoder patterns):
 * ``decoder_replay_8k``   the last 128 prompt positions through the decoder
   pattern Full + 3 Reuse, [Reindex + 3 Reuse] x 4
 
+and the 128K layer group's shapes at twice the context ("Hierarchical
+indexer": the candidate cap holds whatever the context length):
+
+* ``decode_group_256k``   batch 8, 256K context, Full + 5 Reuse
+
 Recipe (both sides read identical bytes):
 * ``numpy.random.Generator(PCG64(1000 + config_number))``;
 * draw order: ``k_idx``, each indexing layer's ``q_idx`` (model order), main K,
@@ -142,6 +147,8 @@ CONFIGS = {
                _encoder_pattern()),
         Config("decoder_replay_8k", 7, "bf16", 1, 8192, False, 16, 128, 64, 8, 2048, 512, 128,
                _decoder_pattern(), replay=128),
+        Config("decode_group_256k", 8, "bf16", 8, 262144, True, 16, 128, 64, 8, 2048, 512, 128,
+               (FULL,) + (REUSE,) * 5),
     ]
 }
 
