@@ -273,7 +273,11 @@ int32_t csa2_attend(const csa2_cfg *cfg, int32_t n_q, const void *q, const int32
  * (the mode table of "CSA2 with cross-layer reuse": a Full or Reindex layer
  * followed by the Reuse layers that take its indices).
  *   CSA2_FULL    : csa2_build_block_keys over [blk_update_begin, T/B) (pass
- *                  blk_update_begin >= T/B to skip), csa2_index_blocks,
+ *                  blk_update_begin >= T/B to skip it: the block pass reads
+ *                  the keys of the blocks before each query's own, so skip
+ *                  only when they are current, as in decode, or when every
+ *                  pool is the whole prefix, where no key is read),
+ *                  csa2_index_blocks,
  *                  csa2_topk_tokens, csa2_attend_group; the block pass also
  *                  stores into k_blk the key of every block that a query
  *                  completes ((t+1) % B == 0), so a decode step keeps k_blk

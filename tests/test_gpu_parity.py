@@ -522,3 +522,32 @@ def test_unstored_pool_ids_give_the_same_selection(lib, decode):
     slots = torch.arange(cfg.pool, device="cuda", dtype=torch.int32)[None, :]
     assert torch.equal(ids, torch.where(slots < cnt[:, None], slots, torch.full_like(slots, -1)))
     compare_run(pipeline.outputs(dw), oracle.run_layers(wl), cfg, what="unstored pool ids")
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_layer_group_leaves_every_completed_block_key(lib, decode):
+    """After a Full layer group whose queries complete blocks (every position
+    of a prompt, or the newest token of decode), k_blk holds the key of every
+    complete block, bit-exact, without a bulk block-key launch; a prompt's
+    layer group starts from zeroed block keys."""
+    B, pipeline = lib
+    if decode:
+        cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=4096, pool=64, top_k=128)
+    else:
+        cfg = W.scaled(W.CONFIGS["prefill_8k"], n_seq=2, ctx=1003, pool=200, top_k=100, window=40,
+                       layers=("full", "reuse"))
+    print(f"case completed block keys decode={decode} S={cfg.n_seq} T={cfg.ctx}", flush=True)
+    wl = W.generate(cfg, seed=38)
+    dw = pipeline.upload(wl)
+    nblk = cfg.ctx // cfg.block
+    if decode:
+        pipeline.build_cache(dw, upto_block=nblk - 1)   # the newest token completes the last block
+    assert pipeline.step_update_begin(dw) == nblk     # no bulk rebuild inside the step
+    pipeline.run(dw)
+    torch.cuda.synchronize()
+    got = dw.k_blk.cpu().numpy()
+    for s in range(cfg.n_seq):
+        for j in range(nblk):
+            want = oracle.block_key(wl.k_idx[s], cfg.block, j, cfg.ctx - 1)
+            assert np.array_equal(got[s, j], want), (s, j)
+    compare_run(pipeline.outputs(dw), oracle.run_layers(wl), cfg, what="completed block keys")

@@ -148,11 +148,18 @@ def build_cache(dw: DeviceWorkload, upto_block=None):
 
 
 def step_update_begin(dw: DeviceWorkload) -> int:
-    """First block a Full layer rebuilds in bulk inside a step: prefill builds
-    every block; decode builds none in bulk (the block pass stores the block
-    the newest token completes)."""
+    """First block a Full layer rebuilds in bulk inside a step.  None in
+    decode (earlier steps left every other block's key current, and the block
+    pass stores the block the newest token completes) and in prompts whose
+    every position is a query and whose pools are whole prefixes (the block
+    pass then reads no block key, and stores the key of every block a query
+    completes, i.e. every complete block).  Otherwise every block, before the
+    block pass reads them."""
     T = dw.k_idx.shape[1]
-    return T // dw.cfg.block if dw.cfg.decode else 0
+    cfg = dw.cfg
+    if cfg.decode or (cfg.replay == 0 and whole_prefix_pools(cfg)):
+        return T // cfg.block
+    return 0
 
 
 def run(dw: DeviceWorkload):
