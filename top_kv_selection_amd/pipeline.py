@@ -321,9 +321,23 @@ def kernel_work(cfg: Config) -> dict:
                 add("k_attend_chunks", "bytes",
                     n_q * (P * 4 + 4 + K * 4 + 4 + sel * 2 * D * esz + len(layers) * per_layer))
         return work
+    # prompts: the attention kernel follows the number of (query, layer, head
+    # group) items of a call (few: key-list chunks; a few hundred: one
+    # workgroup per item; many: one wave per item, or the shared-window kernel
+    # for window-only layers), and the token Top-K is the dense MFMA kernel
+    # when every pool is the whole prefix and the call has enough queries
     ops = algorithmic_ops(cfg)
+    hg = max(1, H // 16)
     for (mode, layers), flops in zip(cfg.groups(), ops["attend"]):
-        add("k_attend_window" if mode == "swa" else "k_attend_rows", "bf16_flops", flops)
+        items = cfg.n_q * len(layers) * hg
+        if items < 256:
+            kernel = "k_attend_chunks"
+        elif items < 1024:
+            kernel = "k_attend_mfma"
+        else:
+            kernel = "k_attend_window" if mode == "swa" else "k_attend_rows"
+        add(kernel, "bf16_flops", flops)
+    dense = whole_prefix_pools(cfg) and T <= 16384 and cfg.n_q >= 256
     for n in ops["topk_tokens"]:
-        add("k_topk_dense", "int8_ops", n)
+        add("k_topk_dense" if dense else "k_topk_tokens", "int8_ops", n)
     return work
