@@ -551,3 +551,18 @@ def test_layer_group_leaves_every_completed_block_key(lib, decode):
             want = oracle.block_key(wl.k_idx[s], cfg.block, j, cfg.ctx - 1)
             assert np.array_equal(got[s, j], want), (s, j)
     compare_run(pipeline.outputs(dw), oracle.run_layers(wl), cfg, what="completed block keys")
+
+
+def test_prefill_dense_topk_extreme_scores(lib):
+    """int8 values of -128 (the ABI accepts them): a block of rows and
+    queries of all -128 scores exactly 2^20, the one score in the top bin of
+    the dense Top-K's first pass; the rest of the prompt draws in [-127, 127]
+    and ties are broken by position."""
+    _, pipeline = lib
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=1000, pool=200, top_k=96, window=16, layers=("full",))
+    wl = W.generate(cfg, seed=39)
+    wl.k_idx[0, 100:400] = -128
+    wl.q_idx[0][500:] = -128
+    print(f"case dense Top-K with scores of 2^20: n_q={cfg.n_q}", flush=True)
+    got = run_gpu(pipeline, wl)
+    compare_run(got, oracle.run_layers(wl), cfg, what="extreme scores")

@@ -192,7 +192,8 @@ int32_t do_index(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int3
 int32_t do_topk(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32_t *q_seq,
                 const int32_t *q_pos, const int8_t *k_idx, int32_t T, const int32_t *blk_ids,
                 const int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt, void *ws,
-                size_t ws_bytes, hipStream_t st, bool launch)
+                size_t ws_bytes, hipStream_t st, bool launch, int32_t *pool_cnt_out = nullptr,
+                int8_t *k_blk_store = nullptr)
 {
     if (c->top_k < 1) return CSA2_E_SHAPE;
     const bool whole_prefix = (long long)(T - 1) / c->block + 1 <= c->pool;
@@ -214,6 +215,12 @@ int32_t do_topk(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32
     p.ws_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
     p.ws_hist = r.ctr;
     p.topk = topk; p.topk_cnt = topk_cnt;
+    if (pool_cnt_out) {   // only the dense kernel stands in for the block pass
+        if (!pl.dense || blk_ids) return CSA2_E_SHAPE;
+        p.pool_cnt_out = pool_cnt_out;
+        p.k_blk_store = k_blk_store;
+        p.nblk = T / c->block;
+    }
     return hip_status(launch_topk_tokens(p, pl, c->d_idx, st));
 }
 
@@ -482,12 +489,19 @@ int32_t layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int32_t n
                 return e;
         }
         if (selects) {
+            // A prompt whose pools are whole prefixes and whose pool ids are
+            // not stored: the block pass would only write the counts and the
+            // completed blocks' keys, which the dense token Top-K writes
+            // instead (one launch less).
+            const bool in_topk = !blk_ids && plan_index(n_q, T, c->block, c->pool, c->d_idx).all &&
+                                 plan_topk(n_q, T, c->block, c->pool, c->top_k, c->d_idx).dense;
+            int8_t *store = mode == CSA2_FULL ? k_blk : nullptr;
             if (int32_t e = do_index(c, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, n_seq, T, blk_ids,
-                                     blk_cnt, ws, ws_bytes, st, launch,
-                                     mode == CSA2_FULL ? k_blk : nullptr))
+                                     blk_cnt, ws, ws_bytes, st, launch && !in_topk, store))
                 return e;
             if (int32_t e = do_topk(c, n_q, q_idx, q_seq, q_pos, k_idx, T, blk_ids, blk_cnt, topk,
-                                    topk_cnt, ws, ws_bytes, st, launch))
+                                    topk_cnt, ws, ws_bytes, st, launch, in_topk ? blk_cnt : nullptr,
+                                    in_topk ? store : nullptr))
                 return e;
         }
         if (tokens_only) {   // the shared pool is read, only the token Top-K is fresh

@@ -92,6 +92,13 @@ struct TopkParams {
     int64_t ws_stride;
     uint32_t *ws_hist;
     int32_t *topk, *topk_cnt;
+    // dense token Top-K of a prompt whose pools are whole prefixes and whose
+    // pool ids are not stored: the kernel also writes the pool counts and
+    // (Full layer) the key of every block a query completes, in place of the
+    // block pass (non-null only there)
+    int32_t *pool_cnt_out;
+    int8_t *k_blk_store;
+    int nblk;
 };
 
 struct AttendParams {

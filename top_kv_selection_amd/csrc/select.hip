@@ -600,8 +600,12 @@ __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
 // (-> exact threshold key tau and the number of ties to take) and a third
 // pass builds bitmaps of keys above tau and equal to tau.  An ordered emit
 // over the bitmaps writes the positions ascending, ties lowest position
-// first.  Histogram counts (at most kDenseMaxT) are packed two per 32-bit LDS
-// word and the bitmaps reuse the histogram memory; per-query rows are padded
+// first.  The first pass counts one key bin per 32-bit LDS word: scores lie
+// in [-2^20, 2^20], so only the 1,025 bins 512 .. 1536 of key >> 11 can hold
+// a key, and word w of a row counts bin 512 + w (a count costs a shift, an
+// add and the atomic).  The low-bit histogram of the fallback packs two
+// 16-bit counts (at most kDenseMaxT) per word.  The bitmaps reuse the
+// histogram memory; per-query rows are padded
 // so that the 16 queries of a wave instruction fall in different LDS banks,
 // and a wave owns whole bitmap words, which it writes with plain stores.
 constexpr int kDenseQ = 16;              // queries per workgroup (one MFMA column block)
@@ -610,7 +614,9 @@ constexpr int kDenseUnroll = 8;          // position tiles per wave per load bat
 constexpr int kDenseBatchPos = 16 * kDenseUnroll;
 constexpr int kDenseBatchWords = kDenseBatchPos / 32;
 static_assert(kDenseBatchPos % 32 == 0, "a batch covers whole bitmap words");
-constexpr int kDenseHistWords = kRadixBins / 2 + 8;   // packed histogram words per query (+ bank pad)
+constexpr int kDenseHistWords = kRadixBins / 2 + 8;   // histogram words per query (+ bank pad)
+constexpr int kDenseBin0 = 512;          // key >> 11 of the first occupied first-pass bin
+static_assert(kDenseHistWords >= 1025, "every occupied first-pass bin has a word");
 constexpr int kDenseMapWords = kDenseMaxT / 32 + 4;   // bitmap words per query (+ bank pad)
 constexpr int kDenseList = 128;          // bin-b1 keys per query the two-pass select resolves
 
@@ -658,6 +664,49 @@ __device__ __forceinline__ void find_bin_packed(const uint32_t *h, uint32_t n, i
     const uint64_t found = __builtin_amdgcn_ballot_w64(here);   // exactly one lane when n <= total
     const int src = found ? __builtin_ctzll(found) : 0;
     bin = __builtin_amdgcn_readlane(32 * lane + b, src);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)run, src);
+    in_bin = (uint32_t)__builtin_amdgcn_readlane((int)cb, src);
+}
+
+// The same search over one query's first-pass histogram, one bin per word:
+// word w counts key bin kDenseBin0 + w for w = 0 .. 1024; lane l covers words
+// 16 l .. 16 l + 15, and lane 63 also word 1024 (the top bin, which only a
+// score of exactly 2^20 reaches).  `bin` is returned as a key bin (key >> 11).
+__device__ __forceinline__ void find_bin_words(const uint32_t *h, uint32_t n, int &bin, uint32_t &above,
+                                               uint32_t &in_bin)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t c[16];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(h + 16 * lane + 4 * k);
+        c[4 * k] = v.x; c[4 * k + 1] = v.y; c[4 * k + 2] = v.z; c[4 * k + 3] = v.w;
+    }
+    const uint32_t top = (lane == 63) ? h[1024] : 0u;
+    uint32_t S = top;
+#pragma unroll
+    for (int k = 0; k < 16; k++) S += c[k];
+    const uint32_t incl = wave_incl_scan(S);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t suf = total - incl;   // keys in the bins above this lane's
+    const bool here = suf < n && suf + S >= n;
+    int b = 0;
+    uint32_t run = suf, cb = 0;
+    if (here) {
+        if (run + top >= n) {
+            b = 16;
+            cb = top;
+        } else {
+            run += top;
+            for (int k = 15; k >= 0; k--) {
+                if (run + c[k] >= n) { b = k; cb = c[k]; break; }
+                run += c[k];
+            }
+        }
+    }
+    const uint64_t found = __builtin_amdgcn_ballot_w64(here);   // exactly one lane when n <= total
+    const int src = found ? __builtin_ctzll(found) : 0;
+    bin = kDenseBin0 + __builtin_amdgcn_readlane(16 * lane + b, src);
     above = (uint32_t)__builtin_amdgcn_readlane((int)run, src);
     in_bin = (uint32_t)__builtin_amdgcn_readlane((int)cb, src);
 }
@@ -730,6 +779,21 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
     if (qvalid && 16 * g < DIDX) qb = *reinterpret_cast<const v4i32 *>(p.q_idx + (size_t)qi * DIDX + 16 * g);
     uint32_t *gt_map = s_buf, *eq_map = s_buf + kDenseQ * MW;   // eq_map doubles as the bin-b1 map
 
+    // the block pass's outputs when it is not launched (see TopkParams)
+    if (p.pool_cnt_out != nullptr) {
+        for (int x = tid; x < kDenseQ * DIDX; x += NT) {
+            const int i = q0 + x / DIDX, dd = x % DIDX;
+            if (i >= p.n_q) continue;
+            const int t = p.q_pos[i], jt = t / p.B;
+            if (dd == 0) p.pool_cnt_out[i] = eligible_blocks(t, p.B, p.tail);
+            if (p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk) {
+                const size_t row0 = (size_t)p.q_seq[i] * p.T + (size_t)jt * p.B;
+                p.k_blk_store[((size_t)p.q_seq[i] * p.nblk + jt) * DIDX + dd] =
+                    (int8_t)block_key_dim<DIDX>(p.k_idx + row0 * DIDX, p.B, dd);
+            }
+        }
+    }
+
     auto zero_buf = [&] {
         for (int x = tid * 4; x < kDenseQ * HW; x += NT * 4) *reinterpret_cast<uint4 *>(s_buf + x) = make_uint4(0, 0, 0, 0);
     };
@@ -798,12 +862,11 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
         const bool all_mine = __builtin_amdgcn_ballot_w64(mine) == ~0ull;
 
         // ---- pass 1: top-bit histograms.  With key = score + 2^21, the word
-        // of bin key >> 11 is (score >> 12) + 512 and its half is bit 11 of
-        // the score (the bias does not reach bits below 21).
+        // of bin key >> 11 is (score >> 11) + 1024 - kDenseBin0.
         zero_buf();
         __syncthreads();
-        uint32_t *hrow = s_buf + r16 * HW + (kKeyBias >> (kRadixBits + 1));
-        auto hist_add = [&](int sc) { atomicAdd(&hrow[sc >> (kRadixBits + 1)], ((sc >> kRadixBits) & 1) ? 0x10000u : 1u); };
+        uint32_t *hrow = s_buf + r16 * HW + ((int)(kKeyBias >> kRadixBits) - kDenseBin0);
+        auto hist_add = [&](int sc) { atomicAdd(&hrow[sc >> kRadixBits], 1u); };
         scan([&](int, int pos0, v4i32 d, bool check) {
             if (!check && all_mine) {
 #pragma unroll
@@ -821,7 +884,7 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
             const uint32_t n = (uint32_t)__builtin_amdgcn_readlane(tq, jq) + 1;
             int b1 = -1;                 // fewer candidates than K: every key is taken
             uint32_t gt1 = 0, eq1 = 0;
-            if (n > (uint32_t)K) find_bin_packed(s_buf + jq * HW, (uint32_t)K, b1, gt1, eq1);
+            if (n > (uint32_t)K) find_bin_words(s_buf + jq * HW, (uint32_t)K, b1, gt1, eq1);
             if (lane == 0) {
                 s_b1[jq] = b1;
                 s_gt1[jq] = gt1;
