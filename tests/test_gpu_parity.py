@@ -566,3 +566,24 @@ def test_prefill_dense_topk_extreme_scores(lib):
     print(f"case dense Top-K with scores of 2^20: n_q={cfg.n_q}", flush=True)
     got = run_gpu(pipeline, wl)
     compare_run(got, oracle.run_layers(wl), cfg, what="extreme scores")
+
+
+@pytest.mark.parametrize("kind", ["equal_scores", "zero_strided_rows"])
+def test_prefill_dense_topk_adversarial(lib, kind):
+    """Prompts far from random scores: every key row equal (every query's
+    scores tie, so the K-th key's bin holds far more keys than a per-query
+    list, and the ties are taken lowest position first), and zero rows in
+    every fourth run of 64 positions (a strided sample of the prefix would
+    put the K-th key near score 0, while the prefix's K best lie far above
+    it)."""
+    _, pipeline = lib
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=3000, layers=("full",))
+    wl = W.generate(cfg, seed=40)
+    if kind == "equal_scores":
+        wl.k_idx[0, :] = wl.k_idx[0, 7]
+    else:
+        pos = np.arange(cfg.ctx)
+        wl.k_idx[0, (pos // 64) % 4 == 0] = 0
+    print(f"case dense Top-K adversarial ({kind}): n_q={cfg.n_q} T={cfg.ctx}", flush=True)
+    got = run_gpu(pipeline, wl)
+    compare_run(got, oracle.run_layers(wl), cfg, what=f"adversarial ({kind})")

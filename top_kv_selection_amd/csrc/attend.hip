@@ -532,7 +532,6 @@ constexpr int kRowCodes = 256;          // Top-K row ids staged per wave at once
 constexpr int kTileInst = 1024 + 16;    // bytes per load instruction in a tile
 constexpr int kTileBytes = 8 * kTileInst;
 constexpr float kLazyLog2 = 8.f;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -550,13 +549,6 @@ __device__ __forceinline__ float sum_groups(float x)   // sum over lanes l, l^16
     x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// Orders this wave's LDS accesses in the compiler; the hardware performs one
-// wave's LDS instructions in issue order.
-__device__ __forceinline__ void wave_lds_order()
-{
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base, long long n_rows)
 {

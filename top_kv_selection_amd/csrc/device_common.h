@@ -23,6 +23,7 @@ constexpr int kRadixBits = 11;
 constexpr int kRadixBins = 1 << kRadixBits;
 constexpr uint32_t kRadixMask = kRadixBins - 1;
 constexpr uint32_t kKeyBias = 1u << 21;
+constexpr int kRsrcWord3 = 0x00020000;   // buffer resource word 3: raw buffer, 32-bit data format
 constexpr int kLdsKeys = 16384;            // keys held in LDS by one workgroup
 constexpr int kLdsKeysPadded = kLdsKeys + kLdsKeys / 32;
 // Histograms in LDS also carry one pad word per 32 bins, so that the wave that
@@ -58,6 +59,14 @@ struct GlobalKeys {
     const uint32_t *p;
     __device__ __forceinline__ uint32_t operator()(int i) const { return p[i]; }
 };
+
+// Orders this wave's LDS accesses in the compiler; the hardware performs one
+// wave's LDS instructions in issue order.
+__device__ __forceinline__ void wave_lds_order()
+{
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
 
 // Inclusive prefix sum across the 64 lanes of a wave with DPP moves (row
 // shifts, then row broadcasts), which stay in the VALU instead of the LDS

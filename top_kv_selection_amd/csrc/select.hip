@@ -592,9 +592,11 @@ __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
 // instead of storing its keys:
 //   pass 1: histogram of key >> 11 per query -> threshold bin b1, with gt1
 //           keys above it and eq1 keys in it;
-//   pass 2: bitmaps of the keys above bin b1 and of the keys in bin b1; the
-//           eq1 keys of bin b1 are then scored again one by one and the
-//           K - gt1 best by (key desc, position asc) join the first bitmap.
+//   pass 2: a bitmap of the keys above bin b1, while the eq1 keys of bin b1
+//           go to a per-query list (low key bits and position); a ballot
+//           search over the list's low key bits then finds the K-th key,
+//           the list keys above it join the bitmap and those equal to it a
+//           tie bitmap.
 // When some query has more than kDenseList keys in its bin b1 (many equal
 // scores), pass 2 instead takes a histogram of the low bits inside bin b1
 // (-> exact threshold key tau and the number of ties to take) and a third
@@ -610,7 +612,7 @@ __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
 // and a wave owns whole bitmap words, which it writes with plain stores.
 constexpr int kDenseQ = 16;              // queries per workgroup (one MFMA column block)
 constexpr int kDenseWaves = 8;
-constexpr int kDenseUnroll = 8;          // position tiles per wave per load batch
+constexpr int kDenseUnroll = 4;          // position tiles per wave per load batch
 constexpr int kDenseBatchPos = 16 * kDenseUnroll;
 constexpr int kDenseBatchWords = kDenseBatchPos / 32;
 static_assert(kDenseBatchPos % 32 == 0, "a batch covers whole bitmap words");
@@ -621,14 +623,6 @@ constexpr int kDenseMapWords = kDenseMaxT / 32 + 4;   // bitmap words per query 
 constexpr int kDenseList = 128;          // bin-b1 keys per query the two-pass select resolves
 
 typedef int v4i32 __attribute__((ext_vector_type(4)));
-
-// Orders one wave's LDS accesses in the compiler (the hardware performs a
-// wave's LDS instructions in issue order).
-__device__ __forceinline__ void wave_lds_order_sel()
-{
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
 
 // Threshold search over one query's packed 2048-bin histogram by one wave:
 // the bin b where the count of keys in bins above b is < n <= count in bins
@@ -719,33 +713,6 @@ __device__ __forceinline__ uint32_t or_groups(uint32_t x)   // OR over lanes l, 
     return r[0] | r[1];
 }
 
-// Positions of the set bits of one query's bitmap row, in order: lane l
-// covers words 8l .. 8l+7; fn(rank, position) for every set bit, rank being
-// its index among all set bits of the row.
-template <class Fn>
-__device__ __forceinline__ void for_set_bits(const uint32_t *row, uint32_t (&m)[8], Fn &&fn)
-{
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(row + 8 * lane + 4 * k);
-        m[4 * k] = a.x; m[4 * k + 1] = a.y; m[4 * k + 2] = a.z; m[4 * k + 3] = a.w;
-    }
-    uint32_t c = 0;
-#pragma unroll
-    for (int k = 0; k < 8; k++) c += __builtin_popcount(m[k]);
-    uint32_t r = wave_incl_scan(c) - c;
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-        uint32_t x = m[k];
-        while (x) {
-            const int b = __builtin_ctz(x);
-            x &= x - 1;
-            fn(r++, 256 * lane + 32 * k + b);
-        }
-    }
-}
-
 template <int DIDX>
 __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_topk_dense(TopkParams p)
 {
@@ -753,8 +720,9 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
     constexpr int HW = kDenseHistWords, MW = kDenseMapWords;
     static_assert(2 * kDenseQ * MW <= kDenseQ * HW, "bitmaps reuse the histogram memory");
     __shared__ __attribute__((aligned(16))) uint32_t s_buf[kDenseQ * HW];
-    __shared__ uint32_t s_list[kDenseQ][kDenseList];   // bin-b1 positions, then composite keys
+    __shared__ uint32_t s_list[kDenseQ][kDenseList];   // the keys of bin b1 (see pass 2)
     __shared__ int s_b1[kDenseQ], s_tau[kDenseQ], s_need[kDenseQ];
+    __shared__ uint32_t s_cnt[kDenseQ];
     __shared__ uint32_t s_gt1[kDenseQ], s_eq1[kDenseQ];
 
     const int tid = threadIdx.x;
@@ -777,7 +745,7 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
     const int tq = !qvalid ? -1 : (p.tail == kTailExclude ? (p.q_pos[qi] + 1) / p.B * p.B - 1 : p.q_pos[qi]);
     v4i32 qb = {0, 0, 0, 0};
     if (qvalid && 16 * g < DIDX) qb = *reinterpret_cast<const v4i32 *>(p.q_idx + (size_t)qi * DIDX + 16 * g);
-    uint32_t *gt_map = s_buf, *eq_map = s_buf + kDenseQ * MW;   // eq_map doubles as the bin-b1 map
+    uint32_t *gt_map = s_buf, *eq_map = s_buf + kDenseQ * MW;
 
     // the block pass's outputs when it is not launched (see TopkParams)
     if (p.pool_cnt_out != nullptr) {
@@ -821,29 +789,47 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
         // kDenseBatchPos * gi + 16 u ..; d[ii] is the score of position
         // pos0 + 4g + ii for query column r16, and `check` is false when every
         // position of the tile precedes every query.  A batch's loads are
-        // issued together and unconditionally (rows clamped into the
-        // sequence; the dims a d_idx of 32 lacks meet zeros in q_idx).
+        // issued together and unconditionally, as buffer loads over the
+        // sequence's rows (a position past the sequence reads zeros and is
+        // never counted; the dims a d_idx of 32 lacks meet zeros in q_idx),
+        // and a wave issues the loads of its next batch before it works on
+        // this one, so that a batch costs its arithmetic rather than a
+        // memory round trip.
         const int n_batches = tmax / kDenseBatchPos + 1;
+        const auto rows_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(rows), 0, p.T * DIDX, kRsrcWord3);
         auto scan = [&](auto &&fn, auto &&done) {
             const int part = (16 * g < DIDX) ? 16 * g : 16 * (g & 1);
-            for (int gi = w; gi < n_batches; gi += kDenseWaves) {
-                v4i32 a[kDenseUnroll];
+            auto load = [&](int gi, v4i32 (&a)[kDenseUnroll]) {
+                const int off = (kDenseBatchPos * gi + r16) * DIDX + part;
 #pragma unroll
-                for (int u = 0; u < kDenseUnroll; u++) {
-                    const int pos = min(kDenseBatchPos * gi + 16 * u + r16, p.T - 1);
-                    a[u] = *reinterpret_cast<const v4i32 *>(rows + (size_t)pos * DIDX + part);
-                }
+                for (int u = 0; u < kDenseUnroll; u++)
+                    a[u] = __builtin_bit_cast(v4i32, __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc, off + 16 * u * DIDX, 0, 0));
+            };
+            // every tile of a batch is scored: a tile past the last query
+            // takes the checked path, where no position passes (skipping it
+            // instead would leave a prefetched register unread on one path,
+            // and the compiler then waits for every load at the loop head)
+            auto body = [&](int gi, const v4i32 (&a)[kDenseUnroll]) {
 #pragma unroll
                 for (int u = 0; u < kDenseUnroll; u++) {
                     const int pos0 = kDenseBatchPos * gi + 16 * u;
-                    if (pos0 <= tmax) {
-                        const v4i32 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], qb, v4i32{0, 0, 0, 0}, 0, 0, 0);
-                        if (pos0 + 15 > tmin) fn(u, pos0, d, true);
-                        else fn(u, pos0, d, false);
-                    }
+                    const v4i32 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], qb, v4i32{0, 0, 0, 0}, 0, 0, 0);
+                    if (pos0 + 15 > tmin) fn(u, pos0, d, true);
+                    else fn(u, pos0, d, false);
                 }
                 done(kDenseBatchWords * gi);
+            };
+            int gi = w;
+            if (gi >= n_batches) return;
+            v4i32 a0[kDenseUnroll], a1[kDenseUnroll];
+            load(gi, a0);
+            for (; gi + kDenseWaves < n_batches; gi += 2 * kDenseWaves) {
+                load(gi + kDenseWaves, a1);
+                body(gi, a0);
+                load(gi + 2 * kDenseWaves, a0);   // past the end: read, never used
+                body(gi + kDenseWaves, a1);
             }
+            if (gi < n_batches) body(gi, a0);
         };
         auto nothing = [](int) {};
         // bits of this batch for query column r16 (OR over the lane groups),
@@ -890,6 +876,7 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
                 s_gt1[jq] = gt1;
                 s_eq1[jq] = eq1;
                 s_need[jq] = 0;
+                s_cnt[jq] = 0u;
             }
         }
         __syncthreads();
@@ -898,8 +885,10 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
         zero_buf();
         __syncthreads();
         if (listed) {
-            // ---- pass 2: bitmaps of keys above bin b1 and of keys in bin b1
-            uint32_t gw[kDenseBatchWords] = {}, bw[kDenseBatchWords] = {};
+            // ---- pass 2: bitmap of the keys above bin b1; the keys in bin b1
+            // (at most kDenseList per query) go to the query's list as their
+            // low key bits above (kDenseMaxT - 1 - position)
+            uint32_t gw[kDenseBatchWords] = {};
             // bins as score >> 11 (the bias moves every bin by 1024)
             const int b1s = b1q - (int)(kKeyBias >> kRadixBits);
             const uint32_t lane_bit = 1u << (4 * g);    // position 4g of a 16-position tile
@@ -910,66 +899,54 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
                     // pos0 is a multiple of 16, so the bit of position
                     // pos0 + 4g + ii in its word is 16 (u & 1) + 4g + ii
                     const uint32_t bit = lane_bit << (16 * (u & 1) + ii);
-                    const bool ok = !check || pos0 + 4 * g + ii <= tq;
+                    const int pos = pos0 + 4 * g + ii;
+                    const bool ok = !check || pos <= tq;
                     const int b = d[ii] >> kRadixBits;
                     gw[u >> 1] |= (ok && b > b1s) ? bit : 0u;
-                    bw[u >> 1] |= (ok && b == b1s) ? bit : 0u;
+                    if (ok && b == b1s) {
+                        const uint32_t slot = atomicAdd(&s_cnt[r16], 1u);
+                        if (slot < (uint32_t)kDenseList)
+                            s_list[r16][slot] = ((((uint32_t)d[ii] + kKeyBias) & kRadixMask) << 14) |
+                                                (uint32_t)(kDenseMaxT - 1 - pos);
+                    }
                 }
-            }, [&](int word0) {
-                store_bits(gt_map, word0, gw);
-                store_bits(eq_map, word0, bw);
-            });
+            }, [&](int word0) { store_bits(gt_map, word0, gw); });
             __syncthreads();
-            // bin b1: score its (at most kDenseList) keys again and add the
-            // K - gt1 best by (key desc, position asc) to the first bitmap
+            // bin b1: the threshold tau2 on the low key bits that keeps
+            // need1 = K - gt1 of the list's keys (bit by bit from the top,
+            // counting with ballots); keys above tau2 join the first bitmap,
+            // keys equal to it go to the tie bitmap, from which the emit takes
+            // the first ones in position order
             for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
                 if (!((gmask >> jq) & 1) || s_b1[jq] < 0) continue;
                 const int n_list = (int)s_eq1[jq];
-                const int need1 = K - (int)s_gt1[jq];
-                uint32_t m[8];
-                for_set_bits(eq_map + jq * MW, m, [&](uint32_t r, int pos) {
-                    if (r < (uint32_t)kDenseList) s_list[jq][r] = (uint32_t)pos;
-                });
-                wave_lds_order_sel();
-                const int8_t *qrow = p.q_idx + (size_t)(q0 + jq) * DIDX;
-                int4 qv[DIDX / 16], kv[2][DIDX / 16];
+                const uint32_t need1 = (uint32_t)K - s_gt1[jq];
+                uint32_t lo[2];
                 int pos_e[2];
-#pragma unroll
-                for (int k = 0; k < DIDX / 16; k++) qv[k] = *reinterpret_cast<const int4 *>(qrow + 16 * k);
+                bool v[2];
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const int x = lane + 64 * h;
-                    pos_e[h] = (x < n_list) ? (int)s_list[jq][x] : 0;
-#pragma unroll
-                    for (int k = 0; k < DIDX / 16; k++)
-                        kv[h][k] = *reinterpret_cast<const int4 *>(rows + (size_t)pos_e[h] * DIDX + 16 * k);
+                    v[h] = x < n_list;
+                    const uint32_t c = v[h] ? s_list[jq][x] : 0u;
+                    lo[h] = c >> 14;
+                    pos_e[h] = kDenseMaxT - 1 - (int)(c & 0x3fffu);
                 }
-                // composite key: low 11 key bits above (kDenseMaxT - 1 - position)
-                uint32_t c[2];
+                uint32_t tau2 = 0, above = 0;
+                for (int bit = kRadixBits - 1; bit >= 0; bit--) {
+                    const uint32_t want = (tau2 | (1u << bit)) >> bit;
+                    const uint32_t cnt =
+                        (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v[0] && (lo[0] >> bit) == want)) +
+                        (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v[1] && (lo[1] >> bit) == want));
+                    if (above + cnt >= need1) tau2 |= 1u << bit;
+                    else above += cnt;
+                }
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
-                    int acc = 0;
-#pragma unroll
-                    for (int k = 0; k < DIDX / 16; k++) {
-                        acc = dot4_i8(kv[h][k].x, qv[k].x, acc);
-                        acc = dot4_i8(kv[h][k].y, qv[k].y, acc);
-                        acc = dot4_i8(kv[h][k].z, qv[k].z, acc);
-                        acc = dot4_i8(kv[h][k].w, qv[k].w, acc);
-                    }
-                    const uint32_t low = ((uint32_t)(acc + (int)kKeyBias)) & kRadixMask;
-                    c[h] = (lane + 64 * h < n_list) ? (low << 14) | (uint32_t)(kDenseMaxT - 1 - pos_e[h]) : 0u;
+                    if (v[h] && lo[h] > tau2) atomicOr(&gt_map[jq * MW + (pos_e[h] >> 5)], 1u << (pos_e[h] & 31));
+                    if (v[h] && lo[h] == tau2) atomicOr(&eq_map[jq * MW + (pos_e[h] >> 5)], 1u << (pos_e[h] & 31));
                 }
-                // rank of each entry = entries with a larger composite key
-                int rank[2] = {0, 0};
-                for (int y = 0; y < n_list; y++) {
-                    const uint32_t cy = (uint32_t)__builtin_amdgcn_readlane((int)c[y >> 6], y & 63);
-                    rank[0] += cy > c[0];
-                    rank[1] += cy > c[1];
-                }
-#pragma unroll
-                for (int h = 0; h < 2; h++)
-                    if (lane + 64 * h < n_list && rank[h] < need1)
-                        atomicOr(&gt_map[jq * MW + (pos_e[h] >> 5)], 1u << (pos_e[h] & 31));
+                if (lane == 0) s_need[jq] = (int)(need1 - above);
             }
         } else {
             // ---- pass 2': low-bit histograms inside the threshold bin
@@ -1031,7 +1008,7 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
             const int i = q0 + jq;
             const int n = __builtin_amdgcn_readlane(tq, jq) + 1;
             const int cnt = min(n, K);
-            const int need = s_need[jq];   // ties to take (the third pass only)
+            const int need = s_need[jq];   // ties to take, in position order
             int32_t *out = p.topk + (size_t)i * K;
             const int n_words = (n + 31) / 32;
             uint32_t base = 0, ties = 0;
