@@ -568,6 +568,18 @@ def test_prefill_dense_topk_extreme_scores(lib):
     compare_run(got, oracle.run_layers(wl), cfg, what="extreme scores")
 
 
+@pytest.mark.parametrize("top_k", [700, 1100])
+def test_prefill_dense_topk_wide_k(lib, top_k):
+    """Whole-prefix pools with a Top-K longer than the dense kernel's 512-slot
+    output stage: every query's entries are written in several rounds."""
+    _, pipeline = lib
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=2000, pool=256, top_k=top_k, window=64, layers=("full",))
+    wl = W.generate(cfg, seed=41)
+    print(f"case dense Top-K K={top_k}: n_q={cfg.n_q} T={cfg.ctx}", flush=True)
+    got = run_gpu(pipeline, wl)
+    compare_run(got, oracle.run_layers(wl), cfg, what=f"dense Top-K K={top_k}")
+
+
 @pytest.mark.parametrize("kind", ["equal_scores", "zero_strided_rows"])
 def test_prefill_dense_topk_adversarial(lib, kind):
     """Prompts far from random scores: every key row equal (every query's

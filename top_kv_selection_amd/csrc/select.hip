@@ -602,7 +602,8 @@ __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
 // (-> exact threshold key tau and the number of ties to take) and a third
 // pass builds bitmaps of keys above tau and equal to tau.  An ordered emit
 // over the bitmaps writes the positions ascending, ties lowest position
-// first.  The first pass counts one key bin per 32-bit LDS word: scores lie
+// first, staged in the query's bitmap row and copied out with coalesced
+// stores.  The first pass counts one key bin per 32-bit LDS word: scores lie
 // in [-2^20, 2^20], so only the 1,025 bins 512 .. 1536 of key >> 11 can hold
 // a key, and word w of a row counts bin 512 + w (a count costs a shift, an
 // add and the atomic).  The low-bit histogram of the fallback packs two
@@ -621,6 +622,8 @@ constexpr int kDenseBin0 = 512;          // key >> 11 of the first occupied firs
 static_assert(kDenseHistWords >= 1025, "every occupied first-pass bin has a word");
 constexpr int kDenseMapWords = kDenseMaxT / 32 + 4;   // bitmap words per query (+ bank pad)
 constexpr int kDenseList = 128;          // bin-b1 keys per query the two-pass select resolves
+constexpr int kDenseStage = 512;         // output slots staged in a bitmap row at once
+static_assert(kDenseStage <= kDenseMapWords, "a bitmap row holds the output stage");
 
 typedef int v4i32 __attribute__((ext_vector_type(4)));
 
@@ -1001,46 +1004,77 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
             });
         }
         __syncthreads();
-        // ---- ordered emit, 64 bitmap words (2048 positions) per round: lane l
-        // takes word 64 r + l, so a round costs at most 32 bit steps
+        // ---- ordered emit.  A wave takes its query's bitmap words into
+        // registers (lane l: words 64 r + l), folds in the first `need` tie
+        // bits in position order, and writes the positions in slot order into
+        // the query's bitmap row, which then serves as the output stage:
+        // kDenseStage slots at a time, copied out with coalesced stores.
         for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
             if (!((gmask >> jq) & 1)) continue;
+            uint32_t *row = gt_map + jq * MW;
+            const uint32_t *erow = eq_map + jq * MW;
             const int i = q0 + jq;
             const int n = __builtin_amdgcn_readlane(tq, jq) + 1;
             const int cnt = min(n, K);
             const int need = s_need[jq];   // ties to take, in position order
             int32_t *out = p.topk + (size_t)i * K;
             const int n_words = (n + 31) / 32;
-            uint32_t base = 0, ties = 0;
-            for (int r0 = 0; r0 < n_words; r0 += 64) {
-                const int wd = r0 + lane;
-                uint32_t x = (wd < n_words) ? gt_map[jq * MW + wd] : 0u;
-                if (need > 0) {
-                    // the first `need` keys equal to tau in position order
-                    uint32_t e = (wd < n_words) ? eq_map[jq * MW + wd] : 0u;
+            constexpr int R = (kDenseMaxT / 32 + 63) / 64;
+            uint32_t x[R];
+#pragma unroll
+            for (int r = 0; r < R; r++) x[r] = (64 * r + lane < n_words) ? row[64 * r + lane] : 0u;
+            if (need > 0) {
+                uint32_t ties = 0;
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    if (64 * r >= n_words) break;
+                    uint32_t e = (64 * r + lane < n_words) ? erow[64 * r + lane] : 0u;
                     const uint32_t ec = __builtin_popcount(e);
                     const uint32_t e_incl = wave_incl_scan(ec);
                     int take = min(max(need - (int)(ties + e_incl - ec), 0), (int)ec);
                     while (take > 0) {
                         const uint32_t lsb = e & (0u - e);
-                        x |= lsb;
+                        x[r] |= lsb;
                         e ^= lsb;
                         take--;
                     }
                     ties += (uint32_t)__builtin_amdgcn_readlane((int)e_incl, 63);
                 }
-                const uint32_t sc = __builtin_popcount(x);
-                const uint32_t s_incl = wave_incl_scan(sc);
-                uint32_t slot = base + s_incl - sc;
-                while (x) {
-                    const int b = __builtin_ctz(x);
-                    x &= x - 1;
-                    if (slot < (uint32_t)K) out[slot] = 32 * wd + b;
-                    slot++;
-                }
-                base += (uint32_t)__builtin_amdgcn_readlane((int)s_incl, 63);
             }
-            for (int o = cnt + lane; o < K; o += 64) out[o] = -1;
+            wave_lds_order();   // the row is in registers: it becomes the stage
+            for (int c0 = 0; c0 < K; c0 += kDenseStage) {
+                const int len = min(kDenseStage, K - c0);
+                uint32_t run = 0;   // kept positions in the rounds before
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    if (64 * r >= n_words) break;
+                    const uint32_t sc = __builtin_popcount(x[r]);
+                    const uint32_t incl = wave_incl_scan(sc);
+                    uint32_t xx = x[r], slot = run + incl - sc;
+                    run += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+                    const uint32_t pos0 = (uint32_t)(32 * (64 * r + lane));
+                    if (K <= kDenseStage) {
+                        // one stage holds every slot, and the kept positions
+                        // fill exactly slots 0 .. cnt - 1
+                        uint32_t *dst = row + slot;
+                        while (xx) {
+                            *dst++ = pos0 + (uint32_t)__builtin_ctz(xx);
+                            xx &= xx - 1;
+                        }
+                    } else {
+                        while (xx) {
+                            const int b = __builtin_ctz(xx);
+                            xx &= xx - 1;
+                            if (slot >= (uint32_t)c0 && slot < (uint32_t)(c0 + len)) row[slot - c0] = pos0 + (uint32_t)b;
+                            slot++;
+                        }
+                    }
+                }
+                for (int o = max(cnt, c0) - c0 + lane; o < len; o += 64) row[o] = 0xffffffffu;   // -1: no entry
+                wave_lds_order();
+                for (int o = lane; o < len; o += 64) out[c0 + o] = (int32_t)row[o];
+                wave_lds_order();   // the stage is read before the next slots are written
+            }
             if (lane == 0) p.topk_cnt[i] = cnt;
         }
         __syncthreads();
