@@ -592,11 +592,11 @@ __global__ __launch_bounds__(NT) void k_topk_select(TopkParams p)
 // instead of storing its keys:
 //   pass 1: histogram of key >> 11 per query -> threshold bin b1, with gt1
 //           keys above it and eq1 keys in it;
-//   pass 2: a bitmap of the keys above bin b1, while the eq1 keys of bin b1
-//           go to a per-query list (low key bits and position); a ballot
-//           search over the list's low key bits then finds the K-th key,
-//           the list keys above it join the bitmap and those equal to it a
-//           tie bitmap.
+//   pass 2: bitmaps of the keys above bin b1 and of the keys in bin b1 (plain
+//           compares, no branch per key); the eq1 keys of bin b1 are then
+//           scored again from their rows, and a ballot search over their low
+//           key bits finds the K-th key: the ones above it join the first
+//           bitmap, those equal to it a tie bitmap.
 // When some query has more than kDenseList keys in its bin b1 (many equal
 // scores), pass 2 instead takes a histogram of the low bits inside bin b1
 // (-> exact threshold key tau and the number of ties to take) and a third
@@ -716,6 +716,33 @@ __device__ __forceinline__ uint32_t or_groups(uint32_t x)   // OR over lanes l, 
     return r[0] | r[1];
 }
 
+// Positions of the set bits of one query's bitmap row, in order: lane l
+// covers words 8l .. 8l+7; fn(rank, position) for every set bit, rank being
+// its index among all set bits of the row.
+template <class Fn>
+__device__ __forceinline__ void for_set_bits(const uint32_t *row, uint32_t (&m)[8], Fn &&fn)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(row + 8 * lane + 4 * k);
+        m[4 * k] = a.x; m[4 * k + 1] = a.y; m[4 * k + 2] = a.z; m[4 * k + 3] = a.w;
+    }
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) c += __builtin_popcount(m[k]);
+    uint32_t r = wave_incl_scan(c) - c;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        uint32_t x = m[k];
+        while (x) {
+            const int b = __builtin_ctz(x);
+            x &= x - 1;
+            fn(r++, 256 * lane + 32 * k + b);
+        }
+    }
+}
+
 template <int DIDX>
 __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_topk_dense(TopkParams p)
 {
@@ -723,9 +750,8 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
     constexpr int HW = kDenseHistWords, MW = kDenseMapWords;
     static_assert(2 * kDenseQ * MW <= kDenseQ * HW, "bitmaps reuse the histogram memory");
     __shared__ __attribute__((aligned(16))) uint32_t s_buf[kDenseQ * HW];
-    __shared__ uint32_t s_list[kDenseQ][kDenseList];   // the keys of bin b1 (see pass 2)
+    __shared__ uint32_t s_list[kDenseQ][kDenseList];   // positions of the keys of bin b1
     __shared__ int s_b1[kDenseQ], s_tau[kDenseQ], s_need[kDenseQ];
-    __shared__ uint32_t s_cnt[kDenseQ];
     __shared__ uint32_t s_gt1[kDenseQ], s_eq1[kDenseQ];
 
     const int tid = threadIdx.x;
@@ -879,7 +905,6 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
                 s_gt1[jq] = gt1;
                 s_eq1[jq] = eq1;
                 s_need[jq] = 0;
-                s_cnt[jq] = 0u;
             }
         }
         __syncthreads();
@@ -888,66 +913,92 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
         zero_buf();
         __syncthreads();
         if (listed) {
-            // ---- pass 2: bitmap of the keys above bin b1; the keys in bin b1
-            // (at most kDenseList per query) go to the query's list as their
-            // low key bits above (kDenseMaxT - 1 - position)
-            uint32_t gw[kDenseBatchWords] = {};
-            // bins as score >> 11 (the bias moves every bin by 1024)
+            // ---- pass 2: bitmaps of the keys above bin b1 and of the keys in
+            // bin b1 (plain compares, no branch per key).  A lane's thresholds:
+            // above bin b1 from thr_gt, in bin b1 from thr_lo (bins as
+            // score >> 11: the bias moves every bin by 1024); every key passes
+            // thr_gt when the query keeps all its candidates, and none passes
+            // for a lane outside the group.
+            uint32_t gw[kDenseBatchWords] = {}, bw[kDenseBatchWords] = {};
             const int b1s = b1q - (int)(kKeyBias >> kRadixBits);
+            const int thr_gt = !mine ? INT32_MAX : (b1q < 0 ? INT32_MIN : (b1s + 1) * kRadixBins);
+            const int thr_lo = (!mine || b1q < 0) ? INT32_MAX : b1s * kRadixBins;
             const uint32_t lane_bit = 1u << (4 * g);    // position 4g of a 16-position tile
             scan([&](int u, int pos0, v4i32 d, bool check) {
-                if (!mine) return;
 #pragma unroll
                 for (int ii = 0; ii < 4; ii++) {
                     // pos0 is a multiple of 16, so the bit of position
                     // pos0 + 4g + ii in its word is 16 (u & 1) + 4g + ii
                     const uint32_t bit = lane_bit << (16 * (u & 1) + ii);
-                    const int pos = pos0 + 4 * g + ii;
-                    const bool ok = !check || pos <= tq;
-                    const int b = d[ii] >> kRadixBits;
-                    gw[u >> 1] |= (ok && b > b1s) ? bit : 0u;
-                    if (ok && b == b1s) {
-                        const uint32_t slot = atomicAdd(&s_cnt[r16], 1u);
-                        if (slot < (uint32_t)kDenseList)
-                            s_list[r16][slot] = ((((uint32_t)d[ii] + kKeyBias) & kRadixMask) << 14) |
-                                                (uint32_t)(kDenseMaxT - 1 - pos);
-                    }
+                    const bool ok = !check || pos0 + 4 * g + ii <= tq;
+                    gw[u >> 1] |= (ok && d[ii] >= thr_gt) ? bit : 0u;
+                    bw[u >> 1] |= (ok && d[ii] >= thr_lo && d[ii] < thr_gt) ? bit : 0u;
                 }
-            }, [&](int word0) { store_bits(gt_map, word0, gw); });
+            }, [&](int word0) {
+                store_bits(gt_map, word0, gw);
+                store_bits(eq_map, word0, bw);
+            });
             __syncthreads();
-            // bin b1: the threshold tau2 on the low key bits that keeps
-            // need1 = K - gt1 of the list's keys (bit by bit from the top,
-            // counting with ballots); keys above tau2 join the first bitmap,
-            // keys equal to it go to the tie bitmap, from which the emit takes
-            // the first ones in position order
+            // bin b1: its (at most kDenseList) keys are scored again from
+            // their rows; the threshold tau2 on their low key bits that keeps
+            // need1 = K - gt1 of them is found bit by bit from the top
+            // (counting with ballots); keys above tau2 join the first bitmap,
+            // keys equal to it go to the tie bitmap (the query's bin-b1 row,
+            // cleared once read), from which the emit takes the first ones in
+            // position order
             for (int jq = w; jq < kDenseQ; jq += kDenseWaves) {
                 if (!((gmask >> jq) & 1) || s_b1[jq] < 0) continue;
                 const int n_list = (int)s_eq1[jq];
                 const uint32_t need1 = (uint32_t)K - s_gt1[jq];
-                uint32_t lo[2];
+                uint32_t *erow = eq_map + jq * MW;
+                uint32_t m[8];
+                for_set_bits(erow, m, [&](uint32_t r, int pos) {
+                    if (r < (uint32_t)kDenseList) s_list[jq][r] = (uint32_t)pos;
+                });
+                *reinterpret_cast<uint4 *>(erow + 8 * lane) = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(erow + 8 * lane + 4) = make_uint4(0, 0, 0, 0);
+                wave_lds_order();
+                const int8_t *qrow = p.q_idx + (size_t)(q0 + jq) * DIDX;
+                int4 qv[DIDX / 16], kv[2][DIDX / 16];
                 int pos_e[2];
-                bool v[2];
+                bool vl[2];
+#pragma unroll
+                for (int k = 0; k < DIDX / 16; k++) qv[k] = *reinterpret_cast<const int4 *>(qrow + 16 * k);
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const int x = lane + 64 * h;
-                    v[h] = x < n_list;
-                    const uint32_t c = v[h] ? s_list[jq][x] : 0u;
-                    lo[h] = c >> 14;
-                    pos_e[h] = kDenseMaxT - 1 - (int)(c & 0x3fffu);
+                    vl[h] = x < n_list;
+                    pos_e[h] = vl[h] ? (int)s_list[jq][x] : 0;
+#pragma unroll
+                    for (int k = 0; k < DIDX / 16; k++)
+                        kv[h][k] = *reinterpret_cast<const int4 *>(rows + (size_t)pos_e[h] * DIDX + 16 * k);
+                }
+                uint32_t lo[2];
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    int acc = 0;
+#pragma unroll
+                    for (int k = 0; k < DIDX / 16; k++) {
+                        acc = dot4_i8(kv[h][k].x, qv[k].x, acc);
+                        acc = dot4_i8(kv[h][k].y, qv[k].y, acc);
+                        acc = dot4_i8(kv[h][k].z, qv[k].z, acc);
+                        acc = dot4_i8(kv[h][k].w, qv[k].w, acc);
+                    }
+                    lo[h] = ((uint32_t)(acc + (int)kKeyBias)) & kRadixMask;
                 }
                 uint32_t tau2 = 0, above = 0;
                 for (int bit = kRadixBits - 1; bit >= 0; bit--) {
                     const uint32_t want = (tau2 | (1u << bit)) >> bit;
                     const uint32_t cnt =
-                        (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v[0] && (lo[0] >> bit) == want)) +
-                        (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v[1] && (lo[1] >> bit) == want));
+                        (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(vl[0] && (lo[0] >> bit) == want)) +
+                        (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(vl[1] && (lo[1] >> bit) == want));
                     if (above + cnt >= need1) tau2 |= 1u << bit;
                     else above += cnt;
                 }
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
-                    if (v[h] && lo[h] > tau2) atomicOr(&gt_map[jq * MW + (pos_e[h] >> 5)], 1u << (pos_e[h] & 31));
-                    if (v[h] && lo[h] == tau2) atomicOr(&eq_map[jq * MW + (pos_e[h] >> 5)], 1u << (pos_e[h] & 31));
+                    if (vl[h] && lo[h] > tau2) atomicOr(&gt_map[jq * MW + (pos_e[h] >> 5)], 1u << (pos_e[h] & 31));
+                    if (vl[h] && lo[h] == tau2) atomicOr(&erow[pos_e[h] >> 5], 1u << (pos_e[h] & 31));
                 }
                 if (lane == 0) s_need[jq] = (int)(need1 - above);
             }
