@@ -45,13 +45,8 @@ __device__ __forceinline__ bf16x8_t load_nt_bf16x8(const uint16_t *src)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);   // keep NaN a NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+// round to nearest even (gfx950's v_cvt_pk_bf16_f32; a NaN stays a NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
@@ -964,9 +959,9 @@ __global__ __launch_bounds__(kCkWaves * 64) void k_attend_chunks(AttendParams p)
 //    one sequence at a time; a query's softmax state stays in its wave's
 //    registers across chunks.
 constexpr int kWinWaves = 8;
-constexpr int kWinQPW = 1;               // queries per wave
+constexpr int kWinQPW = 2;               // queries per wave
 constexpr int kWinQ = kWinQPW * kWinWaves;   // queries per workgroup
-constexpr int kWinRows = 136;            // window rows staged at once (8 queries of a 128 window: 135)
+constexpr int kWinRows = 144;            // window rows staged at once (16 queries of a 128 window: 143)
 constexpr int kWinKStride = 272;         // bytes per staged K row
 constexpr int kWinVStride = 288;         // bytes per staged V row
 
@@ -1150,10 +1145,15 @@ void k_attend_window(AttendParams p)
     }
     if (one_seq && (s0 < 0 || hi - lo <= kWinRows)) {
         if (s0 >= 0) stage(s0, lo, hi - lo);
+        // a wave's queries w, w + kWinWaves, ... in turn; the next query's
+        // rows are requested before this one's output stores, so waiting for
+        // them does not wait for the stores
+        State st;
+        if (q0 + w < p.n_q) begin(st, q0 + w);
 #pragma unroll
         for (int half = 0; half < kWinQPW; half++) {
             const int j = w + kWinWaves * half, i = q0 + j;
-            if (i >= p.n_q) continue;
+            if (i >= p.n_q) break;
             int my_r0 = 0, my_nw = 0;
 #pragma unroll
             for (int jj = 0; jj < kWinQ; jj++)
@@ -1161,10 +1161,23 @@ void k_attend_window(AttendParams p)
                     my_r0 = r0[jj];
                     my_nw = nw[jj];
                 }
-            State st;
-            begin(st, i);
             if (my_nw > 0) attend_rows(st, my_r0, my_r0 + my_nw, lo);
+            const bool next = half + 1 < kWinQPW && i + kWinWaves < p.n_q;
+            bf16x8_t qn[4];
+            if (next) {
+                const uint16_t *qrow = (const uint16_t *)p.q + (((size_t)l * p.n_q + i + kWinWaves) * p.H + hg * 16 + r16) * 128;
+#pragma unroll
+                for (int kk = 0; kk < 4; kk++) qn[kk] = load_nt_bf16x8(qrow + kk * 32 + g * 8);
+            }
             finish(st, i);
+            if (next) {
+#pragma unroll
+                for (int kk = 0; kk < 4; kk++) st.qb[kk] = qn[kk];
+#pragma unroll
+                for (int m = 0; m < 8; m++) st.acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                st.m_run = -INFINITY;
+                st.l_part = 0.f;
+            }
         }
         return;
     }
