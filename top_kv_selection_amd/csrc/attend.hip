@@ -523,13 +523,15 @@ __global__ __launch_bounds__(32 * kCombineHeads) void k_attend_combine(AttendPar
 // x, x+8, x+16, x+24 as one 1 KiB run, and the runs are kTileInst bytes
 // apart so that rows of different instructions start in different banks.
 constexpr int kRowWaves = 4;            // waves (items in flight) per workgroup
-constexpr int kRowCodes = 256;          // Top-K row ids staged per wave at once (8 steps)
+constexpr int kRowCodes = 512;          // Top-K row ids staged per wave at once (16 steps)
 constexpr int kTileInst = 1024 + 16;    // bytes per load instruction in a tile
 constexpr int kTileBytes = 8 * kTileInst;
 constexpr float kLazyLog2 = 8.f;
+constexpr int kRowPrefetchLoads = 6;    // last vector loads of the next item's prefetch (2 table + 4 query)
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v4i32 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float max_groups(float x)   // max over lanes l, l^16, l^32, l^48
 {
@@ -559,63 +561,94 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
     // pointers and buffer descriptors) in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-    // Workgroup b runs on XCD b % 8 (round-robin dispatch); each XCD takes a
-    // contiguous range of items, i.e. of neighbouring queries whose windows
-    // overlap, so window rows are shared inside one L2.
+    // Workgroup b runs on XCD b % 8 (round-robin dispatch); the waves of an
+    // XCD take contiguous ranges of items, i.e. of neighbouring queries whose
+    // windows overlap, so window rows are shared inside one L2.  The grid
+    // holds every workgroup at once and each wave walks items wave0,
+    // wave0 + n_waves, ...
     const int per_xcd = gridDim.x / 8;
-    const int item = ((blockIdx.x % 8) * per_xcd + blockIdx.x / 8) * kRowWaves + w;
+    const int wave0 = ((blockIdx.x % 8) * per_xcd + blockIdx.x / 8) * kRowWaves + w;
+    const int n_waves = gridDim.x * kRowWaves;
     const int HG = p.H / 16;
-    if (item >= p.n_q * p.n_layers * HG) return;   // whole wave; no barriers follow
-    const int i = item % p.n_q;
-    const int hg = (item / p.n_q) % HG;
-    const int l = item / (p.n_q * HG);
+    const int n_items = p.n_q * p.n_layers * HG;
+    if (wave0 >= n_items) return;   // whole wave; no barriers follow
 
-    const int s = p.q_seq[i], t = p.q_pos[i];
-    const Window win = window_of(t, p.W, p.swa_first, p.swa_len);
-    const int cnt = p.topk ? p.topk_cnt[i] : 0;
-    const int main_steps = (cnt + 31) / 32;
-    const int n_steps = main_steps + (win.nw + 31) / 32;
-
-    const uint16_t *qrow = (const uint16_t *)p.q + (((size_t)l * p.n_q + i) * p.H + hg * 16 + r16) * 128;
-    const size_t main0 = (size_t)s * p.T * 128, swa0 = ((size_t)l * p.n_seq + s) * p.swa_len * 128;
-    const auto rk_main = rows_rsrc((const uint16_t *)p.k_main + main0, p.T);
-    const auto rv_main = rows_rsrc((const uint16_t *)p.v_main + main0, p.T);
-    const auto rk_swa = rows_rsrc((const uint16_t *)p.k_swa + swa0, p.swa_len);
-    const auto rv_swa = rows_rsrc((const uint16_t *)p.v_swa + swa0, p.swa_len);
-    const int32_t *tk = p.topk ? p.topk + (size_t)i * p.K : nullptr;
-    const int wrow0 = win.w0 - p.swa_first;      // window row of the first window key
     int *codes = s_codes[w];
     uint8_t *ktile = s_tiles[w][0], *vtile = s_tiles[w][1];
 
-    // Top-K row ids kc .. kc + kRowCodes - 1; slots past cnt repeat the last id
-    int kc = 0;
-    auto stage = [&](int k0) {
+    struct Item {
+        int i, hg, l, s, cnt, main_steps, n_steps, wrow0, nw;
+    };
+    // item index -> (query, head group, layer); the query's sequence,
+    // position and Top-K count come from the tables
+    auto item_from = [&](int item, int s, int t, int cnt) {
+        Item it;
+        it.i = item % p.n_q;
+        it.hg = (item / p.n_q) % HG;
+        it.l = item / (p.n_q * HG);
+        it.s = s;
+        const Window win = window_of(t, p.W, p.swa_first, p.swa_len);
+        it.cnt = cnt;
+        it.main_steps = (it.cnt + 31) / 32;
+        it.n_steps = it.main_steps + (win.nw + 31) / 32;
+        it.wrow0 = win.w0 - p.swa_first;
+        it.nw = win.nw;
+        return it;
+    };
+    auto load_q = [&](int item, bf16x8_t (&qb)[4]) {
+        const int i = item % p.n_q, hg = (item / p.n_q) % HG, l = item / (p.n_q * HG);
+        const uint16_t *qrow = (const uint16_t *)p.q + (((size_t)l * p.n_q + i) * p.H + hg * 16 + r16) * 128;
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) qb[kk] = load_nt_bf16x8(qrow + kk * 32 + g * 8);
+    };
+    // Top-K row ids kc .. kc + kRowCodes - 1 into the list (a synchronous
+    // round trip); slots past cnt repeat the last id
+    auto stage = [&](const Item &it, int k0) {
+        const int32_t *tk = p.topk + (size_t)it.i * p.K;
         wave_lds_order();
-        for (int x = lane; x < kRowCodes; x += 64) codes[x] = tk[min(k0 + x, cnt - 1)];
+        for (int x = lane; x < kRowCodes; x += 64) codes[x] = tk[min(k0 + x, it.cnt - 1)];
         wave_lds_order();
     };
-    // The 16 loads of step st: instruction x brings tile rows x + 8a
-    // (a = lane / 16) of K and of V, lane % 16 taking 16 bytes of the row.
-    auto issue_loads = [&](int st) {
+    // the next item's first kRowCodes ids, 8 per lane, as two 16-byte loads
+    // (ids past K read as zero; those past cnt are masked keys)
+    const bool pf_ids = p.topk != nullptr && p.K % 4 == 0;
+    auto load_ids = [&](int i, v4i32 (&cn)[2]) {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(p.topk + (size_t)i * p.K), 0,
+                                                          4 * min(p.K, kRowCodes), kRsrcWord3);
+        cn[0] = __builtin_bit_cast(v4i32, __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * lane, 0, 0));
+        cn[1] = __builtin_bit_cast(v4i32, __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * lane + 16, 0, 0));
+    };
+    auto put_ids = [&](const v4i32 (&cn)[2]) {
+        wave_lds_order();
+        *reinterpret_cast<v4i32 *>(codes + 8 * lane) = cn[0];
+        *reinterpret_cast<v4i32 *>(codes + 8 * lane + 4) = cn[1];
+        wave_lds_order();
+    };
+    // The 16 loads of step st of item it (list position kc staged): load x
+    // brings tile rows x + 8a (a = lane / 16) of K and of V, lane % 16 taking
+    // 16 bytes of the row.
+    auto issue_loads = [&](const Item &it, int st, int &kc) {
         int row[8];
         __amdgpu_buffer_rsrc_t rk, rv;
-        if (st < main_steps) {
+        if (st < it.main_steps) {
             if (32 * st - kc == kRowCodes) {
                 kc = 32 * st;
-                stage(kc);
+                stage(it, kc);
             }
             const int4 c0 = *reinterpret_cast<const int4 *>(codes + 32 * st - kc + 8 * g);
             const int4 c1 = *reinterpret_cast<const int4 *>(codes + 32 * st - kc + 8 * g + 4);
             row[0] = c0.x; row[1] = c0.y; row[2] = c0.z; row[3] = c0.w;
             row[4] = c1.x; row[5] = c1.y; row[6] = c1.z; row[7] = c1.w;
-            rk = rk_main;
-            rv = rv_main;
+            const size_t main0 = (size_t)it.s * p.T * 128;
+            rk = rows_rsrc((const uint16_t *)p.k_main + main0, p.T);
+            rv = rows_rsrc((const uint16_t *)p.v_main + main0, p.T);
         } else {
-            const int r0 = wrow0 + 32 * (st - main_steps) + 8 * g, r_last = wrow0 + win.nw - 1;
+            const int r0 = it.wrow0 + 32 * (st - it.main_steps) + 8 * g, r_last = it.wrow0 + it.nw - 1;
 #pragma unroll
             for (int x = 0; x < 8; x++) row[x] = min(r0 + x, r_last);
-            rk = rk_swa;
-            rv = rv_swa;
+            const size_t swa0 = ((size_t)it.l * p.n_seq + it.s) * p.swa_len * 128;
+            rk = rows_rsrc((const uint16_t *)p.k_swa + swa0, p.swa_len);
+            rv = rows_rsrc((const uint16_t *)p.v_swa + swa0, p.swa_len);
         }
 #pragma unroll
         for (int x = 0; x < 8; x++) {
@@ -625,10 +658,6 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
         }
     };
 
-    bf16x8_t qb[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; kk++) qb[kk] = load_nt_bf16x8(qrow + kk * 32 + g * 8);
-
     // operand addresses in the tiles (per lane; tau, kk, m, h are immediates)
     //   K, A layout: tile row 16 tau + r16, bytes 64 kk + 16 g
     const uint8_t *ka_base = ktile + kTileInst * (r16 & 7) + 256 * (r16 >> 3) + 16 * g;
@@ -637,90 +666,163 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
     const int vrow = 4 * g + (r16 >> 2);
     const uint8_t *va_base = vtile + kTileInst * (vrow & 7) + 256 * (vrow >> 3) + 8 * (r16 & 3);
 
-    float m_run = -INFINITY, l_part = 0.f;
-    f32x4_t acc[8];
-#pragma unroll
-    for (int m = 0; m < 8; m++) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    if (n_steps > 0) {
-        if (main_steps > 0) stage(0);
-        issue_loads(0);
+    // Items one after another.  While an item runs, the next item's table
+    // entries, ids and query rows are loaded (issued right after the loads of
+    // the item's second step, the query rows last, so that step waits for
+    // everything but them), and its first step's rows are requested once the
+    // item's last step has read its operands: only the first item of a wave
+    // waits for its ids, query rows and first rows in turn.
+    auto fence = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    Item cur;
+    {
+        const int i0 = wave0 % p.n_q;
+        cur = item_from(wave0, p.q_seq[i0], p.q_pos[i0], p.topk ? p.topk_cnt[i0] : 0);
     }
-    for (int st = 0; st < n_steps; st++) {
-        const int n_valid = (st < main_steps) ? min(32, cnt - 32 * st) : min(32, win.nw - 32 * (st - main_steps));
-        // this step's rows are in the tiles once the wave's loads are done
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        bf16x8_t ka[2][4], va[8];
-#pragma unroll
-        for (int tau = 0; tau < 2; tau++)
-#pragma unroll
-            for (int kk = 0; kk < 4; kk++)
-                ka[tau][kk] = *reinterpret_cast<const bf16x8_t *>(ka_base + 512 * tau + 64 * kk);
-#pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(va_base + 32 * m));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(va_base + 512 + 32 * m));
-            const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
-                                       __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
-            va[m] = __builtin_bit_cast(bf16x8_t, u);
-        }
-        // the tiles are free once these reads have returned: the next step's
-        // rows are fetched during this step's arithmetic
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (st + 1 < n_steps) issue_loads(st + 1);
+    bf16x8_t qb[4];
+    load_q(wave0, qb);
+    int kc = 0;
+    if (cur.main_steps > 0) stage(cur, 0);
+    if (cur.n_steps > 0) issue_loads(cur, 0, kc);
+    for (int item = wave0;;) {
+        const int next_item = item + n_waves;
+        const bool has_next = next_item < n_items;
+        const int nx_i = next_item % p.n_q;
+        const bool pf = has_next && pf_ids;   // the next item's ids come from the prefetch
+        v4i32 cn[2] = {v4i32{0, 0, 0, 0}, v4i32{0, 0, 0, 0}};
+        bf16x8_t qn[4] = {qb[0], qb[1], qb[2], qb[3]};
+        int nx_s = 0, nx_t = 0, nx_c = 0;
+        Item nxt = cur;
+        bool next_issued = false;
+        auto prefetch = [&]() {
+            if (!has_next) return;
+            fence();
+            if (pf) load_ids(nx_i, cn);
+            if (p.topk) nx_c = p.topk_cnt[nx_i];
+            fence();
+            // exactly kRowPrefetchLoads vector loads, issued last
+            nx_s = p.q_seq[nx_i];
+            nx_t = p.q_pos[nx_i];
+            load_q(next_item, qn);
+            fence();
+        };
+        // the next item's first rows, once this item's ids are no longer read
+        auto start_next = [&]() {
+            if (!has_next) return;
+            nxt = item_from(next_item, __builtin_amdgcn_readfirstlane(nx_s), __builtin_amdgcn_readfirstlane(nx_t),
+                            __builtin_amdgcn_readfirstlane(nx_c));
+            int kc_next = 0;
+            if (nxt.main_steps > 0) {
+                if (pf) put_ids(cn);
+                else stage(nxt, 0);
+            }
+            if (nxt.n_steps > 0) issue_loads(nxt, 0, kc_next);
+            next_issued = true;
+        };
+        // the first wait after the prefetch leaves its loads in flight
+        const int pf_step = (cur.n_steps < 2) ? 0 : 1;
 
-        // S^T = K Q^T: lane holds keys 4g+ii (tile 0) and 16+4g+ii (tile 1) of head r16
-        f32x4_t sk[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        float m_run = -INFINITY, l_part = 0.f;
+        f32x4_t acc[8];
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++)
+        for (int m = 0; m < 8; m++) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (cur.n_steps < 2) prefetch();
+        for (int st = 0; st < cur.n_steps; st++) {
+            const int n_valid = (st < cur.main_steps) ? min(32, cur.cnt - 32 * st)
+                                                      : min(32, cur.nw - 32 * (st - cur.main_steps));
+            // this step's rows are in the tiles once the wave's loads are
+            // done; at step 1 the prefetch issued after them may still run
+            if (st == pf_step && has_next) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRowPrefetchLoads) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            bf16x8_t ka[2][4], va[8];
 #pragma unroll
             for (int tau = 0; tau < 2; tau++)
-                sk[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tau][kk], qb[kk], sk[tau], 0, 0, 0);
-        // softmax terms of this step (log2 domain; the scale is positive, so
-        // the maximum of the raw scores gives the maximum logit)
-        float sc[8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) sc[e] = sk[e >> 2][e & 3];
-        if (n_valid < 32) {
+                for (int kk = 0; kk < 4; kk++)
+                    ka[tau][kk] = *reinterpret_cast<const bf16x8_t *>(ka_base + 512 * tau + 64 * kk);
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-                if (slot_key(g, e) >= n_valid) sc[e] = -INFINITY;
+            for (int m = 0; m < 8; m++) {
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(va_base + 32 * m));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(va_base + 512 + 32 * m));
+                const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                           __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+                va[m] = __builtin_bit_cast(bf16x8_t, u);
+            }
+            // the tiles are free once these reads have returned: the next
+            // step's rows (or the next item's first) are fetched during this
+            // step's arithmetic
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (st + 1 < cur.n_steps) {
+                issue_loads(cur, st + 1, kc);
+                if (st == 0) prefetch();
+            } else {
+                start_next();
+            }
+
+            // S^T = K Q^T: lane holds keys 4g+ii (tile 0) and 16+4g+ii (tile 1) of head r16
+            f32x4_t sk[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+                for (int tau = 0; tau < 2; tau++)
+                    sk[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tau][kk], qb[kk], sk[tau], 0, 0, 0);
+            // softmax terms of this step (log2 domain; the scale is positive, so
+            // the maximum of the raw scores gives the maximum logit)
+            float sc[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) sc[e] = sk[e >> 2][e & 3];
+            if (n_valid < 32) {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    if (slot_key(g, e) >= n_valid) sc[e] = -INFINITY;
+            }
+            const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                                   fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))) * p.scale_log2;
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyLog2)) {
+                const float hmax = max_groups(mx);
+                const float m_new = (hmax > m_run + kLazyLog2) ? hmax : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first finite max
+                l_part *= alpha;
+#pragma unroll
+                for (int m = 0; m < 8; m++) acc[m] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            bf16x8_t pb;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float pr = __builtin_amdgcn_exp2f(fmaf(sc[e], p.scale_log2, -m_use));
+                l_part += pr;
+                pb[e] = (__bf16)pr;
+            }
+            // O^T += V^T P^T over the 8 dim tiles
+#pragma unroll
+            for (int m = 0; m < 8; m++) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb, acc[m], 0, 0, 0);
         }
-        const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                               fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))) * p.scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyLog2)) {
-            const float hmax = max_groups(mx);
-            const float m_new = (hmax > m_run + kLazyLog2) ? hmax : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first finite max
-            l_part *= alpha;
+        if (!next_issued) start_next();
+
+        // acc[m][ii] = O[head r16][dim 16m + 4g + ii] (unnormalised)
+        const float L = sum_groups(l_part);
+        const float inv = 1.f / L;
+        const size_t row_id = ((size_t)cur.l * p.n_q + cur.i) * p.H + cur.hg * 16 + r16;
+        uint16_t *orow = (uint16_t *)p.out + row_id * 128;
 #pragma unroll
-            for (int m = 0; m < 8; m++) acc[m] *= alpha;
-            m_run = m_new;
+        for (int m = 0; m < 8; m++) {
+            const uint32_t lo = (uint32_t)f32_to_bf16(acc[m][0] * inv) | ((uint32_t)f32_to_bf16(acc[m][1] * inv) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(acc[m][2] * inv) | ((uint32_t)f32_to_bf16(acc[m][3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(orow + 16 * m + 4 * g) = make_uint2(lo, hi);
         }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        bf16x8_t pb;
+        if (p.lse && g == 0) p.lse[row_id] = (m_run + log2f(L)) * kLn2;
+
+        if (!has_next) break;
+        item = next_item;
+        cur = nxt;
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const float pr = __builtin_amdgcn_exp2f(fmaf(sc[e], p.scale_log2, -m_use));
-            l_part += pr;
-            pb[e] = (__bf16)pr;
-        }
-        // O^T += V^T P^T over the 8 dim tiles
-#pragma unroll
-        for (int m = 0; m < 8; m++) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb, acc[m], 0, 0, 0);
+        for (int kk = 0; kk < 4; kk++) qb[kk] = qn[kk];
+        kc = 0;
     }
-    // acc[m][ii] = O[head r16][dim 16m + 4g + ii] (unnormalised)
-    const float L = sum_groups(l_part);
-    const float inv = 1.f / L;
-    const size_t row_id = ((size_t)l * p.n_q + i) * p.H + hg * 16 + r16;
-    uint16_t *orow = (uint16_t *)p.out + row_id * 128;
-#pragma unroll
-    for (int m = 0; m < 8; m++) {
-        const uint32_t lo = (uint32_t)f32_to_bf16(acc[m][0] * inv) | ((uint32_t)f32_to_bf16(acc[m][1] * inv) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(acc[m][2] * inv) | ((uint32_t)f32_to_bf16(acc[m][3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(orow + 16 * m + 4 * g) = make_uint2(lo, hi);
-    }
-    if (p.lse && g == 0) p.lse[row_id] = (m_run + log2f(L)) * kLn2;
 }
 
 // ============================================================ chunk kernel
@@ -1273,7 +1375,9 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
     }
     if (pl.rows && !fused_select && rows_fit) {
         const long long items = (long long)p.n_q * p.n_layers * (p.H / 16);
-        const long long n_wg = (items + kRowWaves - 1) / kRowWaves;
+        // every workgroup resident at once (two per CU); the waves loop over
+        // the items
+        const long long n_wg = std::min<long long>((items + kRowWaves - 1) / kRowWaves, kTargetWorkgroups);
         launch("k_attend_rows", k_attend_rows, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kRowWaves * 64), st, p);
         return hipGetLastError();
     }
