@@ -18,7 +18,7 @@
 //    an item's records;
 //  * k_attend_mfma (a few hundred items): one workgroup of 8 waves per item;
 //  * k_attend_rows (many items, as in prefill): one wave per item;
-//  * k_attend_window (window-only layers with many queries): the windows of 8
+//  * k_attend_window (window-only layers with many queries): the windows of 32
 //    neighbouring queries staged in LDS once;
 //  * k_attend_generic (fp32, or any H and D in {64, 128}): one wave per head,
 //    keys in sequence, fp32 online softmax on the vector ALU.
@@ -1060,10 +1060,10 @@ __global__ __launch_bounds__(kCkWaves * 64) void k_attend_chunks(AttendParams p)
 //    wave), each walking the union of its windows in chunks of kWinRows rows,
 //    one sequence at a time; a query's softmax state stays in its wave's
 //    registers across chunks.
-constexpr int kWinWaves = 8;
+constexpr int kWinWaves = 16;
 constexpr int kWinQPW = 2;               // queries per wave
 constexpr int kWinQ = kWinQPW * kWinWaves;   // queries per workgroup
-constexpr int kWinRows = 144;            // window rows staged at once (16 queries of a 128 window: 143)
+constexpr int kWinRows = 160;            // window rows staged at once (32 queries of a 128 window: 159)
 constexpr int kWinKStride = 272;         // bytes per staged K row
 constexpr int kWinVStride = 288;         // bytes per staged V row
 
@@ -1077,17 +1077,14 @@ __device__ __forceinline__ void win_stage(const uint8_t *ksrc, const uint8_t *vs
     constexpr int NT = kWinWaves * 64;
     constexpr int PER = (kWinRows * 16 + NT - 1) / NT;
     const int tid = threadIdx.x;
-    uint4 k0, k1, k2, k3, k4, v0, v1, v2, v3, v4;
-    static_assert(PER == 5, "staging is written out for five 16-byte pieces per thread");
+    static_assert(PER == 3, "staging is written out for three 16-byte pieces per thread");
     auto src = [&](int u) {
         const int x = tid + u * NT;
         return (size_t)(c0 + min(x >> 4, n_rows - 1)) * 256 + 16 * (x & 15);
     };
-    k0 = *reinterpret_cast<const uint4 *>(ksrc + src(0)); v0 = *reinterpret_cast<const uint4 *>(vsrc + src(0));
-    k1 = *reinterpret_cast<const uint4 *>(ksrc + src(1)); v1 = *reinterpret_cast<const uint4 *>(vsrc + src(1));
-    k2 = *reinterpret_cast<const uint4 *>(ksrc + src(2)); v2 = *reinterpret_cast<const uint4 *>(vsrc + src(2));
-    k3 = *reinterpret_cast<const uint4 *>(ksrc + src(3)); v3 = *reinterpret_cast<const uint4 *>(vsrc + src(3));
-    k4 = *reinterpret_cast<const uint4 *>(ksrc + src(4)); v4 = *reinterpret_cast<const uint4 *>(vsrc + src(4));
+    const uint4 k0 = *reinterpret_cast<const uint4 *>(ksrc + src(0)), v0 = *reinterpret_cast<const uint4 *>(vsrc + src(0));
+    const uint4 k1 = *reinterpret_cast<const uint4 *>(ksrc + src(1)), v1 = *reinterpret_cast<const uint4 *>(vsrc + src(1));
+    const uint4 k2 = *reinterpret_cast<const uint4 *>(ksrc + src(2)), v2 = *reinterpret_cast<const uint4 *>(vsrc + src(2));
     __syncthreads();
     auto put = [&](int u, uint4 kv, uint4 vv) {
         const int x = tid + u * NT;
@@ -1100,8 +1097,6 @@ __device__ __forceinline__ void win_stage(const uint8_t *ksrc, const uint8_t *vs
     put(0, k0, v0);
     put(1, k1, v1);
     put(2, k2, v2);
-    put(3, k3, v3);
-    put(4, k4, v4);
     __syncthreads();
 }
 
@@ -1125,19 +1120,31 @@ void k_attend_window(AttendParams p)
     const int hg = (tile / tiles_q) % HG;
     const int l = tile / (tiles_q * HG);
 
-    // the tile's sequences and window rows (uniform loads)
-    int qs[kWinQ], r0[kWinQ], nw[kWinQ];
-#pragma unroll
-    for (int j = 0; j < kWinQ; j++) {
-        qs[j] = -1;
-        r0[j] = nw[j] = 0;
-        if (q0 + j < p.n_q) {
-            const Window win = window_of(p.q_pos[q0 + j], p.W, p.swa_first, p.swa_len);
-            qs[j] = p.q_seq[q0 + j];
-            r0[j] = win.w0 - p.swa_first;
-            nw[j] = win.nw;
-        }
+    // lane j < kWinQ of every wave holds query q0 + j: its sequence (-1 past
+    // n_q), first window row and row count; a query's entries are read with
+    // readlane, the tile's union with ballots and wave reductions
+    static_assert(kWinQ <= 64, "a tile's queries are held one per lane");
+    int ls = -1, lr0 = 0, lnw = 0;
+    if (lane < kWinQ && q0 + lane < p.n_q) {
+        const Window win = window_of(p.q_pos[q0 + lane], p.W, p.swa_first, p.swa_len);
+        ls = p.q_seq[q0 + lane];
+        lr0 = win.w0 - p.swa_first;
+        lnw = win.nw;
     }
+    const bool has_rows = ls >= 0 && lnw > 0;
+    auto at = [&](int v, int j) { return __builtin_amdgcn_readlane(v, j); };
+    // min of lo and max of hi over the lanes of mask
+    auto span_of = [&](uint64_t mask, int &lo, int &hi) {
+        const bool in = (mask >> lane) & 1;
+        int a = in ? lr0 : INT32_MAX, b = in ? lr0 + lnw : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            a = min(a, __shfl_xor(a, o));
+            b = max(b, __shfl_xor(b, o));
+        }
+        lo = __builtin_amdgcn_readfirstlane(a);
+        hi = __builtin_amdgcn_readfirstlane(b);
+    };
     // Stages window rows [c0, c0 + n_rows) of sequence s (all loads first).
     auto stage = [&](int s, int c0, int n_rows) {
         const size_t row0 = ((size_t)l * p.n_seq + s) * p.swa_len;
@@ -1235,15 +1242,13 @@ void k_attend_window(AttendParams p)
     };
 
     // the fast path's condition: one sequence, and the union fits one staging
+    const uint64_t with_rows = __builtin_amdgcn_ballot_w64(has_rows);
     int s0 = -1, lo = INT32_MAX, hi = 0;
     bool one_seq = true;
-#pragma unroll
-    for (int j = 0; j < kWinQ; j++) {
-        if (qs[j] < 0 || nw[j] == 0) continue;
-        if (s0 < 0) s0 = qs[j];
-        one_seq = one_seq && qs[j] == s0;
-        lo = min(lo, r0[j]);
-        hi = max(hi, r0[j] + nw[j]);
+    if (with_rows) {
+        s0 = at(ls, __builtin_ctzll(with_rows));
+        one_seq = __builtin_amdgcn_ballot_w64(has_rows && ls != s0) == 0;
+        span_of(with_rows, lo, hi);
     }
     if (one_seq && (s0 < 0 || hi - lo <= kWinRows)) {
         if (s0 >= 0) stage(s0, lo, hi - lo);
@@ -1256,13 +1261,7 @@ void k_attend_window(AttendParams p)
         for (int half = 0; half < kWinQPW; half++) {
             const int j = w + kWinWaves * half, i = q0 + j;
             if (i >= p.n_q) break;
-            int my_r0 = 0, my_nw = 0;
-#pragma unroll
-            for (int jj = 0; jj < kWinQ; jj++)
-                if (jj == j) {
-                    my_r0 = r0[jj];
-                    my_nw = nw[jj];
-                }
+            const int my_r0 = at(lr0, j), my_nw = at(lnw, j);
             if (my_nw > 0) attend_rows(st, my_r0, my_r0 + my_nw, lo);
             const bool next = half + 1 < kWinQPW && i + kWinWaves < p.n_q;
             bf16x8_t qn[4];
@@ -1284,45 +1283,24 @@ void k_attend_window(AttendParams p)
         return;
     }
     // general path: parts of kWinWaves queries, chunks of kWinRows rows
-    // (unrolled, so that the tile arrays are indexed by constants)
 #pragma unroll
     for (int half = 0; half < kWinQPW; half++) {
         const int j = w + kWinWaves * half, i = q0 + j;
         const bool valid = i < p.n_q;
-        int my_r0 = 0, my_nw = 0;
-#pragma unroll
-        for (int jj = 0; jj < kWinQ; jj++)
-            if (jj == j) {
-                my_r0 = r0[jj];
-                my_nw = nw[jj];
-            }
+        const int my_r0 = at(lr0, j), my_nw = at(lnw, j);
         State st;
         if (valid) begin(st, i);
-        uint32_t remaining = 0;
-#pragma unroll
-        for (int jj = 0; jj < kWinWaves; jj++) {
-            const int k = jj + kWinWaves * half;
-            if (qs[k] >= 0 && nw[k] > 0) remaining |= 1u << jj;
-        }
+        // the part's queries with rows, as lane bits
+        const uint64_t part = (kWinWaves >= 64 ? ~0ull : ((1ull << kWinWaves) - 1)) << (kWinWaves * half);
+        uint64_t remaining = with_rows & part;
         // one sequence at a time; every wave takes the same groups and chunks
         while (remaining) {
-            int s = -1;
-#pragma unroll
-            for (int jj = kWinWaves - 1; jj >= 0; jj--)
-                if ((remaining >> jj) & 1) s = qs[jj + kWinWaves * half];
-            uint32_t gmask = 0;
-            int glo = INT32_MAX, ghi = 0;
-#pragma unroll
-            for (int jj = 0; jj < kWinWaves; jj++) {
-                const int k = jj + kWinWaves * half;
-                if (((remaining >> jj) & 1) && qs[k] == s) {
-                    gmask |= 1u << jj;
-                    glo = min(glo, r0[k]);
-                    ghi = max(ghi, r0[k] + nw[k]);
-                }
-            }
+            const int s = at(ls, __builtin_ctzll(remaining));
+            const uint64_t gmask = __builtin_amdgcn_ballot_w64(has_rows && ls == s) & remaining;
+            int glo, ghi;
+            span_of(gmask, glo, ghi);
             remaining &= ~gmask;
-            const bool mine = valid && ((gmask >> w) & 1);
+            const bool mine = valid && ((gmask >> j) & 1);
             for (int c0 = glo; c0 < ghi; c0 += kWinRows) {
                 const int n_rows = min(kWinRows, ghi - c0);
                 stage(s, c0, n_rows);
