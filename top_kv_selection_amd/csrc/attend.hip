@@ -17,7 +17,8 @@
 //    (item, chunk) writes a (max, sum, acc) record and a second launch merges
 //    an item's records;
 //  * k_attend_mfma (a few hundred items): one workgroup of 8 waves per item;
-//  * k_attend_rows (many items, as in prefill): one wave per item;
+//  * k_attend_rows (many items, as in prefill): one wave per item at a time,
+//    each wave walking up to four items;
 //  * k_attend_window (window-only layers with many queries): the windows of 32
 //    neighbouring queries staged in LDS once;
 //  * k_attend_generic (fp32, or any H and D in {64, 128}): one wave per head,
@@ -524,6 +525,7 @@ __global__ __launch_bounds__(32 * kCombineHeads) void k_attend_combine(AttendPar
 // apart so that rows of different instructions start in different banks.
 constexpr int kRowWaves = 4;            // waves (items in flight) per workgroup
 constexpr int kRowCodes = 512;          // Top-K row ids staged per wave at once (16 steps)
+constexpr int kRowItemsPerWave = 4;     // items a wave walks one after another
 constexpr int kTileInst = 1024 + 16;    // bytes per load instruction in a tile
 constexpr int kTileBytes = 8 * kTileInst;
 constexpr float kLazyLog2 = 8.f;
@@ -561,17 +563,27 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
     // pointers and buffer descriptors) in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-    // Workgroup b runs on XCD b % 8 (round-robin dispatch); the waves of an
-    // XCD take contiguous ranges of items, i.e. of neighbouring queries whose
-    // windows overlap, so window rows are shared inside one L2.  The grid
-    // holds every workgroup at once and each wave walks items wave0,
-    // wave0 + n_waves, ...
+    // Each wave walks at most kRowItemsPerWave items, wave0, wave0 + stride,
+    // ...  Workgroup b runs on XCD b % 8 (round-robin dispatch) and the
+    // items of an XCD are contiguous ranges, so neighbouring queries, whose
+    // windows overlap, share one L2.
+    //  * Calls that fit one round of the grid (the chip's workgroups, each
+    //    wave taking up to kRowItemsPerWave items): wave v of the XCD-ordered
+    //    grid takes items v, v + n_waves, ..., so every wave sees the whole
+    //    range of prefix lengths.
+    //  * Larger calls: workgroup b takes a block of kRowWaves *
+    //    kRowItemsPerWave consecutive items (wave w its items w, w +
+    //    kRowWaves, ...), and the blocks run in rounds that the hardware
+    //    dispatch balances over the CUs.
     const int per_xcd = gridDim.x / 8;
-    const int wave0 = ((blockIdx.x % 8) * per_xcd + blockIdx.x / 8) * kRowWaves + w;
+    const int slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     const int n_waves = gridDim.x * kRowWaves;
+    const int wave0 = p.row_blocks ? slot * kRowWaves * kRowItemsPerWave + w : slot * kRowWaves + w;
+    const int stride = p.row_blocks ? kRowWaves : n_waves;
     const int HG = p.H / 16;
     const int n_items = p.n_q * p.n_layers * HG;
     if (wave0 >= n_items) return;   // whole wave; no barriers follow
+    const int item_end = p.row_blocks ? min(n_items, (slot + 1) * kRowWaves * kRowItemsPerWave) : n_items;
 
     int *codes = s_codes[w];
     uint8_t *ktile = s_tiles[w][0], *vtile = s_tiles[w][1];
@@ -687,8 +699,8 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
     if (cur.main_steps > 0) stage(cur, 0);
     if (cur.n_steps > 0) issue_loads(cur, 0, kc);
     for (int item = wave0;;) {
-        const int next_item = item + n_waves;
-        const bool has_next = next_item < n_items;
+        const int next_item = item + stride;
+        const bool has_next = next_item < item_end;
         const int nx_i = next_item % p.n_q;
         const bool pf = has_next && pf_ids;   // the next item's ids come from the prefetch
         v4i32 cn[2] = {v4i32{0, 0, 0, 0}, v4i32{0, 0, 0, 0}};
@@ -1353,9 +1365,15 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
     }
     if (pl.rows && !fused_select && rows_fit) {
         const long long items = (long long)p.n_q * p.n_layers * (p.H / 16);
-        // every workgroup resident at once (two per CU); the waves loop over
-        // the items
-        const long long n_wg = std::min<long long>((items + kRowWaves - 1) / kRowWaves, kTargetWorkgroups);
+        const long long per_wg = (long long)kRowWaves * kRowItemsPerWave;
+        long long n_wg;
+        if (items <= per_wg * kTargetWorkgroups) {   // one round: waves stride over every item
+            p.row_blocks = 0;
+            n_wg = std::min<long long>((items + kRowWaves - 1) / kRowWaves, kTargetWorkgroups);
+        } else {                                      // blocks of consecutive items, in rounds
+            p.row_blocks = 1;
+            n_wg = (items + per_wg - 1) / per_wg;
+        }
         launch("k_attend_rows", k_attend_rows, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kRowWaves * 64), st, p);
         return hipGetLastError();
     }

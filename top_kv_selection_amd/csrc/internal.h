@@ -114,6 +114,7 @@ struct AttendParams {
     void *out;
     float *lse;
     float *ws_part;         // chunk records [L][n_q][H/16][n_splits] (chunk kernel)
+    int row_blocks;         // row kernel: items in blocks per workgroup (1) or strided over the grid (0)
     // fused token selection (layer-group decode path): the key list comes from
     // the token keys instead of topk, and topk/topk_cnt are written
     const uint32_t *sel_keys;   // [n_q][sel_stride] token keys
