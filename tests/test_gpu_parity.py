@@ -132,6 +132,15 @@ def test_prefill_row_kernel_long_lists(lib):
     check(lib, cfg, seed=29)
 
 
+def test_prefill_row_kernel_blocks_in_rounds(lib):
+    """More (query, layer, head group) items than one round of the row kernel
+    takes (four per wave over the chip's workgroups): the items go in blocks
+    of 16 consecutive ones per workgroup, run in rounds, the last block
+    part-filled (3,001 queries x 3 layers = 9,003 items)."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=3001, layers=("full", "reuse", "reuse"))
+    check(lib, cfg, seed=31)
+
+
 def test_prefill_row_kernel_two_head_groups(lib):
     cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=1100, pool=64, top_k=200, window=128, n_heads=32,
                    layers=("full", "swa"))
