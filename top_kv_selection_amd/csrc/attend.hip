@@ -1081,10 +1081,11 @@ constexpr int kWinVStride = 288;         // bytes per staged V row
 
 // Copies window rows [c0, c0 + n_rows) of K and V (256 bytes each) into the
 // padded LDS rows of the window kernel; every load is issued before the
-// first store, and the stores wait for the workgroup to be done with the
-// previous rows.
+// first store (and before `between`), and the stores wait for the workgroup
+// to be done with the previous rows unless there are none.
+template <typename Between>
 __device__ __forceinline__ void win_stage(const uint8_t *ksrc, const uint8_t *vsrc, int c0, int n_rows,
-                                          uint8_t *s_k, uint8_t *s_v)
+                                          uint8_t *s_k, uint8_t *s_v, bool first_barrier, Between &&between)
 {
     constexpr int NT = kWinWaves * 64;
     constexpr int PER = (kWinRows * 16 + NT - 1) / NT;
@@ -1097,7 +1098,8 @@ __device__ __forceinline__ void win_stage(const uint8_t *ksrc, const uint8_t *vs
     const uint4 k0 = *reinterpret_cast<const uint4 *>(ksrc + src(0)), v0 = *reinterpret_cast<const uint4 *>(vsrc + src(0));
     const uint4 k1 = *reinterpret_cast<const uint4 *>(ksrc + src(1)), v1 = *reinterpret_cast<const uint4 *>(vsrc + src(1));
     const uint4 k2 = *reinterpret_cast<const uint4 *>(ksrc + src(2)), v2 = *reinterpret_cast<const uint4 *>(vsrc + src(2));
-    __syncthreads();
+    between();
+    if (first_barrier) __syncthreads();
     auto put = [&](int u, uint4 kv, uint4 vv) {
         const int x = tid + u * NT;
         const int r = x >> 4, c = x & 15;
@@ -1117,6 +1119,7 @@ void k_attend_window(AttendParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t s_k[kWinRows * kWinKStride];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[kWinRows * kWinVStride];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[kWinWaves][16 * 256];   // each wave's first query rows
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1160,7 +1163,8 @@ void k_attend_window(AttendParams p)
     // Stages window rows [c0, c0 + n_rows) of sequence s (all loads first).
     auto stage = [&](int s, int c0, int n_rows) {
         const size_t row0 = ((size_t)l * p.n_seq + s) * p.swa_len;
-        win_stage((const uint8_t *)p.k_swa + row0 * 256, (const uint8_t *)p.v_swa + row0 * 256, c0, n_rows, s_k, s_v);
+        win_stage((const uint8_t *)p.k_swa + row0 * 256, (const uint8_t *)p.v_swa + row0 * 256, c0, n_rows, s_k, s_v,
+                  true, [] {});
     };
     struct State {
         bf16x8_t qb[4];
@@ -1263,12 +1267,42 @@ void k_attend_window(AttendParams p)
         span_of(with_rows, lo, hi);
     }
     if (one_seq && (s0 < 0 || hi - lo <= kWinRows)) {
-        if (s0 >= 0) stage(s0, lo, hi - lo);
+        // One staging (no earlier rows to protect, so no barrier before its
+        // stores).  The wave's first query rows go straight into its LDS
+        // slot with buffer loads issued after the window loads, so the
+        // barrier after the stores waits for both together and the rows are
+        // then read from LDS.
+        State st;
+        const bool first = q0 + w < p.n_q;
+        auto q_to_lds = [&]() {
+            if (!first) return;
+            const uint16_t *qrow0 = (const uint16_t *)p.q + (((size_t)l * p.n_q + q0 + w) * p.H + hg * 16) * 128;
+            const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(qrow0), 0, 16 * 256, kRsrcWord3);
+#pragma unroll
+            for (int x = 0; x < 4; x++)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void *)(s_q[w] + 1024 * x),
+                                                         16, 1024 * x + 16 * lane, 0, 0, 0);
+        };
+        if (s0 >= 0) {
+            const size_t row0 = ((size_t)l * p.n_seq + s0) * p.swa_len;
+            win_stage((const uint8_t *)p.k_swa + row0 * 256, (const uint8_t *)p.v_swa + row0 * 256, lo, hi - lo, s_k,
+                      s_v, false, q_to_lds);
+        } else {
+            q_to_lds();
+            __syncthreads();
+        }
+        if (first) {
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++)
+                st.qb[kk] = *reinterpret_cast<const bf16x8_t *>(s_q[w] + 256 * r16 + 64 * kk + 16 * g);
+#pragma unroll
+            for (int m = 0; m < 8; m++) st.acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            st.m_run = -INFINITY;
+            st.l_part = 0.f;
+        }
         // a wave's queries w, w + kWinWaves, ... in turn; the next query's
         // rows are requested before this one's output stores, so waiting for
         // them does not wait for the stores
-        State st;
-        if (q0 + w < p.n_q) begin(st, q0 + w);
 #pragma unroll
         for (int half = 0; half < kWinQPW; half++) {
             const int j = w + kWinWaves * half, i = q0 + j;
