@@ -525,7 +525,8 @@ __global__ __launch_bounds__(32 * kCombineHeads) void k_attend_combine(AttendPar
 // apart so that rows of different instructions start in different banks.
 constexpr int kRowWaves = 4;            // waves (items in flight) per workgroup
 constexpr int kRowCodes = 512;          // Top-K row ids staged per wave at once (16 steps)
-constexpr int kRowItemsPerWave = 4;     // items a wave walks one after another
+constexpr int kRowItemsPerWave = 4;     // items a wave walks in a one-round call
+constexpr int kRowBlockItems = 2;        // items a wave walks in a larger call (blocks in rounds)
 constexpr int kTileInst = 1024 + 16;    // bytes per load instruction in a tile
 constexpr int kTileBytes = 8 * kTileInst;
 constexpr float kLazyLog2 = 8.f;
@@ -563,27 +564,27 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
     // pointers and buffer descriptors) in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-    // Each wave walks at most kRowItemsPerWave items, wave0, wave0 + stride,
-    // ...  Workgroup b runs on XCD b % 8 (round-robin dispatch) and the
-    // items of an XCD are contiguous ranges, so neighbouring queries, whose
-    // windows overlap, share one L2.
+    // Each wave walks a few items, wave0, wave0 + stride, ...  Workgroup b
+    // runs on XCD b % 8 (round-robin dispatch) and the items of an XCD are
+    // contiguous ranges, so neighbouring queries, whose windows overlap,
+    // share one L2.
     //  * Calls that fit one round of the grid (the chip's workgroups, each
     //    wave taking up to kRowItemsPerWave items): wave v of the XCD-ordered
     //    grid takes items v, v + n_waves, ..., so every wave sees the whole
     //    range of prefix lengths.
-    //  * Larger calls: workgroup b takes a block of kRowWaves *
-    //    kRowItemsPerWave consecutive items (wave w its items w, w +
-    //    kRowWaves, ...), and the blocks run in rounds that the hardware
-    //    dispatch balances over the CUs.
+    //  * Larger calls: workgroup b takes a block of kRowWaves * kRowBlockItems
+    //    consecutive items (wave w its items w, w + kRowWaves, ...), and the
+    //    blocks run in rounds that the hardware dispatch balances over the
+    //    CUs.
     const int per_xcd = gridDim.x / 8;
     const int slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     const int n_waves = gridDim.x * kRowWaves;
-    const int wave0 = p.row_blocks ? slot * kRowWaves * kRowItemsPerWave + w : slot * kRowWaves + w;
+    const int wave0 = p.row_blocks ? slot * kRowWaves * kRowBlockItems + w : slot * kRowWaves + w;
     const int stride = p.row_blocks ? kRowWaves : n_waves;
     const int HG = p.H / 16;
     const int n_items = p.n_q * p.n_layers * HG;
     if (wave0 >= n_items) return;   // whole wave; no barriers follow
-    const int item_end = p.row_blocks ? min(n_items, (slot + 1) * kRowWaves * kRowItemsPerWave) : n_items;
+    const int item_end = p.row_blocks ? min(n_items, (slot + 1) * kRowWaves * kRowBlockItems) : n_items;
 
     int *codes = s_codes[w];
     uint8_t *ktile = s_tiles[w][0], *vtile = s_tiles[w][1];
@@ -1399,13 +1400,13 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
     }
     if (pl.rows && !fused_select && rows_fit) {
         const long long items = (long long)p.n_q * p.n_layers * (p.H / 16);
-        const long long per_wg = (long long)kRowWaves * kRowItemsPerWave;
         long long n_wg;
-        if (items <= per_wg * kTargetWorkgroups) {   // one round: waves stride over every item
+        if (items <= (long long)kRowWaves * kRowItemsPerWave * kTargetWorkgroups) {   // one round: waves stride over every item
             p.row_blocks = 0;
             n_wg = std::min<long long>((items + kRowWaves - 1) / kRowWaves, kTargetWorkgroups);
         } else {                                      // blocks of consecutive items, in rounds
             p.row_blocks = 1;
+            const long long per_wg = (long long)kRowWaves * kRowBlockItems;
             n_wg = (items + per_wg - 1) / per_wg;
         }
         launch("k_attend_rows", k_attend_rows, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kRowWaves * 64), st, p);
