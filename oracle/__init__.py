@@ -16,7 +16,10 @@ token-only Reindex layer (the page's Reindex "recomputes only the Top-K"
 reading) keeps the pool of the most recent index set and reselects the tokens
 with its own indexer query.
 Sliding-window-only layers (the page's first two encoder layers) attend to the
-window alone.  These sequencing rules are pinned by tests that recompute every
+window alone.  With a compression ratio r (the page's CSA2(ratio, mode), whose
+ratio it leaves undefined) the main-KV and indexer caches hold one entry per r
+tokens, a query sees the entries complete at its token position, and its
+window stays per token (``orc_visible_entries`` states the rule).  These sequencing rules are pinned by tests that recompute every
 layer of small multi-layer workloads from scratch (selection by enumeration,
 attention by fp64 SDPA over the gathered rows).
 """
@@ -65,9 +68,11 @@ def lib():
         L.orc_select_one.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P]
         L.orc_select_batch.restype = i32
         L.orc_select_batch.argtypes = [i32, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
-                                       P, P, P, P]
+                                       i32, P, P, P, P]
         L.orc_topk_batch.restype = i32
-        L.orc_topk_batch.argtypes = [i32, i32, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]
+        L.orc_topk_batch.argtypes = [i32, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, P, P]
+        L.orc_visible_entries.restype = i32
+        L.orc_visible_entries.argtypes = [i32, i32]
         L.orc_attend_batch.restype = i32
         L.orc_attend_batch.argtypes = [i32, i32, P, P, P, P, P, i32, i32, P, P, i32, i32,
                                        P, P, i32, i32, i32, i32, i32, ctypes.c_double, P, P]
@@ -139,10 +144,18 @@ def block_key(k_seq: np.ndarray, B: int, j: int, t: int) -> np.ndarray:
 TAIL_VISIBLE, TAIL_EXCLUDE, TAIL_WHOLE = 0, 1, 2
 
 
-def select(q_idx, q_seq, q_pos, k_idx, B, P, K, threads=None, tail=TAIL_VISIBLE):
+def visible_entries(t: int, ratio: int) -> int:
+    """Main-KV entries a query at token t sees when each entry compresses
+    ``ratio`` consecutive tokens (complete entries only)."""
+    return int(lib().orc_visible_entries(int(t), int(ratio)))
+
+
+def select(q_idx, q_seq, q_pos, k_idx, B, P, K, threads=None, tail=TAIL_VISIBLE, ratio=1):
     """Per query: pooled blocks and Top-K positions (ascending, -1 padded).
     q_idx int8 [n_q][d]; k_idx int8 [S][T][d].  ``tail`` picks the reading of
     the query's partial own block (visible rows / excluded / whole block).
+    ``ratio``: tokens per main-KV entry; q_pos holds token positions, k_idx
+    one row per entry, and the ids returned are entry ids.
     Returns (blk_ids [n_q][P], blk_cnt [n_q], topk [n_q][K], topk_cnt [n_q])."""
     q_idx = np.ascontiguousarray(q_idx, dtype=np.int8)
     k_idx = np.ascontiguousarray(k_idx, dtype=np.int8)
@@ -159,7 +172,7 @@ def select(q_idx, q_seq, q_pos, k_idx, B, P, K, threads=None, tail=TAIL_VISIBLE)
 
     def run(a, b):
         return L.orc_select_batch(int(a), int(b), _ptr(q_idx), _ptr(q_seq), _ptr(q_pos),
-                                  _ptr(k_idx), S, T, d, B, P, K, int(tail), _ptr(blk_ids), _ptr(blk_cnt),
+                                  _ptr(k_idx), S, T, d, B, P, K, int(tail), int(ratio), _ptr(blk_ids), _ptr(blk_cnt),
                                   _ptr(topk), _ptr(topk_cnt))
 
     bad = _parallel(n_q, threads or default_threads(), run)
@@ -168,7 +181,7 @@ def select(q_idx, q_seq, q_pos, k_idx, B, P, K, threads=None, tail=TAIL_VISIBLE)
     return blk_ids, blk_cnt, topk, topk_cnt
 
 
-def topk_given_pool(q_idx, q_seq, q_pos, k_idx, B, K, blk_ids, blk_cnt, threads=None):
+def topk_given_pool(q_idx, q_seq, q_pos, k_idx, B, K, blk_ids, blk_cnt, threads=None, ratio=1):
     """Step 5 alone over given pools: the Reindex variant that keeps the pool
     of the shared index set and reselects only the tokens with its own
     q_idx.  blk_ids [n_q][P] ascending, -1 padded; blk_cnt [n_q].
@@ -189,7 +202,8 @@ def topk_given_pool(q_idx, q_seq, q_pos, k_idx, B, K, blk_ids, blk_cnt, threads=
 
     def run(a, b):
         return L.orc_topk_batch(int(a), int(b), _ptr(q_idx), _ptr(q_seq), _ptr(q_pos), _ptr(k_idx),
-                                T, d, B, P, K, _ptr(blk_ids), _ptr(blk_cnt), _ptr(topk), _ptr(topk_cnt))
+                                T, d, B, P, K, int(ratio), _ptr(blk_ids), _ptr(blk_cnt), _ptr(topk),
+                                _ptr(topk_cnt))
 
     bad = _parallel(n_q, threads or default_threads(), run)
     if bad:
@@ -264,14 +278,14 @@ def run_layers(wl, rows=None, threads=None):
         k_idx, k_main, v_main = wl.cache(max(n_full - 1, 0))
         if mode in ("full", "reindex"):
             sel = select(wl.q_idx[layer][idx], q_seq, q_pos, k_idx, cfg.block, cfg.pool,
-                         cfg.top_k, threads, cfg.tail)
+                         cfg.top_k, threads, cfg.tail, cfg.ratio)
             res["index"][layer] = dict(zip(("blk_ids", "blk_cnt", "topk", "topk_cnt"), sel))
             current = sel
         elif mode == "reindex_tokens":
             if current is None:
                 raise ValueError("a token-only Reindex layer needs an earlier Full/Reindex layer")
             topk, cnt = topk_given_pool(wl.q_idx[layer][idx], q_seq, q_pos, k_idx, cfg.block,
-                                        cfg.top_k, current[0], current[1], threads)
+                                        cfg.top_k, current[0], current[1], threads, cfg.ratio)
             sel = (current[0], current[1], topk, cnt)
             res["index"][layer] = dict(zip(("blk_ids", "blk_cnt", "topk", "topk_cnt"), sel))
             current = sel

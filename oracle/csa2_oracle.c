@@ -15,6 +15,13 @@
  *     Reindex uses its own indexer query over shared keys, Reuse takes the
  *     indices of an earlier layer; every mode has its own main Q and own
  *     sliding-window K/V.
+ *   - the architecture figure's caption on the same page names CSA2(ratio,
+ *     mode) with a compression ratio and defines neither the ratio nor the
+ *     compressor.  Reading (orc_visible_entries): with ratio r, main-KV entry
+ *     j stands for the r tokens j*r .. j*r + r - 1 and exists once its last
+ *     token has arrived; the selection runs over entries, the window keeps one
+ *     row per token.  The entries themselves arrive precomputed, like every
+ *     other K/V row.
  * The pages leave the scores open.  The library fixes them as:
  *   - token score  s_p = <q_idx, k_idx[p]>            (int8 x int8, exact)
  *   - block score  s_j = <q_idx, round(mean of k_idx over block j)>
@@ -159,17 +166,44 @@ int orc_topk_one(const int8_t *q_idx, const int8_t *k_seq, int T, int t, int d, 
     return 0;
 }
 
+/* Main-KV entries a query at token position t sees when every entry
+ * compresses r consecutive tokens: entry j (tokens j*r .. j*r + r - 1) is
+ * complete once (j + 1) * r - 1 <= t, i.e. for j + 1 <= (t + 1) / r, so the
+ * visible entries are 0 .. (t + 1) / r - 1.  With r = 1 every entry is one
+ * token and the count is t + 1.  Returns -1 for r < 1 or t < 0. */
+int orc_visible_entries(int t, int r)
+{
+    if (r < 1 || t < 0) return -1;
+    return (t + 1) / r;
+}
+
+/* No visible entry: an empty selection (every slot -1, counts 0). */
+static void empty_selection(int32_t *ids, int n, int32_t *cnt)
+{
+    for (int i = 0; i < n; i++) ids[i] = -1;
+    *cnt = 0;
+}
+
 /* Token Top-K over given pools (blk_ids rows of P entries, blk_cnt counts)
  * for queries [q_begin, q_end): the Reindex variant that keeps the pool of
- * the shared index set and reruns only the token selection. */
+ * the shared index set and reruns only the token selection.  q_pos holds
+ * token positions; with ratio r the candidates are the visible entries. */
 int orc_topk_batch(int q_begin, int q_end, const int8_t *q_idx, const int32_t *q_seq,
                    const int32_t *q_pos, const int8_t *k_idx, int T, int d, int B, int P, int K,
-                   const int32_t *blk_ids, const int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt)
+                   int ratio, const int32_t *blk_ids, const int32_t *blk_cnt, int32_t *topk,
+                   int32_t *topk_cnt)
 {
     int bad = 0;
     for (int i = q_begin; i < q_end; i++) {
         const int s = q_seq[i];
-        bad += orc_topk_one(q_idx + (size_t)i * d, k_idx + (size_t)s * T * d, T, q_pos[i], d, B,
+        const int n_vis = orc_visible_entries(q_pos[i], ratio);
+        if (n_vis < 0) { bad++; continue; }
+        if (n_vis == 0) {
+            if (blk_cnt[i] != 0) { bad++; continue; }
+            empty_selection(topk + (size_t)i * K, K, topk_cnt + i);
+            continue;
+        }
+        bad += orc_topk_one(q_idx + (size_t)i * d, k_idx + (size_t)s * T * d, T, n_vis - 1, d, B,
                             blk_ids + (size_t)i * P, blk_cnt[i], K, topk + (size_t)i * K, topk_cnt + i) != 0;
     }
     return bad;
@@ -226,17 +260,27 @@ int orc_select_one(const int8_t *q_idx, const int8_t *k_seq, int T, int t,
 }
 
 /* Queries [q_begin, q_end) of a batch.  q_idx [n_q][d]; k_idx [S][T][d];
- * blk_ids [n_q][P]; topk [n_q][K].  Returns the number of failed queries. */
+ * blk_ids [n_q][P]; topk [n_q][K].  q_pos holds token positions; with ratio
+ * r the query selects over its visible main-KV entries (T of them stored per
+ * sequence), its last visible entry taking the place of t above, and a query
+ * that sees no entry selects nothing.  Returns the number of failed queries. */
 int orc_select_batch(int q_begin, int q_end, const int8_t *q_idx,
                      const int32_t *q_seq, const int32_t *q_pos,
                      const int8_t *k_idx, int S, int T, int d, int B, int P, int K, int tail,
-                     int32_t *blk_ids, int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt)
+                     int ratio, int32_t *blk_ids, int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt)
 {
     int bad = 0;
     for (int i = q_begin; i < q_end; i++) {
         int s = q_seq[i];
         if (s < 0 || s >= S) { bad++; continue; }
-        bad += orc_select_one(q_idx + (size_t)i * d, k_idx + (size_t)s * T * d, T, q_pos[i],
+        const int n_vis = orc_visible_entries(q_pos[i], ratio);
+        if (n_vis < 0) { bad++; continue; }
+        if (n_vis == 0) {
+            empty_selection(blk_ids + (size_t)i * P, P, blk_cnt + i);
+            empty_selection(topk + (size_t)i * K, K, topk_cnt + i);
+            continue;
+        }
+        bad += orc_select_one(q_idx + (size_t)i * d, k_idx + (size_t)s * T * d, T, n_vis - 1,
                               d, B, P, K, tail, blk_ids + (size_t)i * P, blk_cnt + i,
                               topk + (size_t)i * K, topk_cnt + i) != 0;
     }

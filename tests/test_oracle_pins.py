@@ -576,3 +576,84 @@ def test_reuse_after_token_only_reindex_takes_its_fresh_topk():
     _assert_index(res["index"][2], tok)
     for layer, sets in ((0, full), (1, full), (2, tok), (3, tok)):
         np.testing.assert_allclose(res["out"][layer], _sdpa_layer(wl, layer, 0, sets), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- compressed main-KV
+# The figure caption of the "DeepSeek V4.1 Flash" page names CSA2(ratio,
+# mode) and leaves the compression undefined.  Reading: main-KV entry j
+# stands for tokens j*r .. j*r + r - 1 and exists once its last token has
+# arrived; selection runs over entries, the window stays per token.  The
+# brute force below finds the visible entries by testing each entry's last
+# token against t, not by the division the oracle uses.
+def _select_compressed_brute(q, k_entries, t, r, B, P, K, tail=0):
+    vis = [j for j in range(len(k_entries)) if j * r + r - 1 <= t]
+    if not vis:
+        return [], []
+    assert vis == list(range(len(vis)))
+    return select_brute(q, k_entries, vis[-1], B, P, K, tail)
+
+
+def test_visible_entries_by_definition():
+    for r in range(1, 7):
+        for t in range(0, 40):
+            want = sum(1 for j in range(64) if j * r + r - 1 <= t)
+            assert oracle.visible_entries(t, r) == want, (r, t)
+
+
+def test_compressed_selection_matches_enumeration():
+    rng = np.random.default_rng(41)
+    for _ in range(300):
+        r = int(rng.integers(2, 5))
+        B = int(rng.choice([2, 4]))
+        n = int(rng.integers(1, 9))            # entries in the cache
+        d = int(rng.integers(1, 4))
+        P = int(rng.integers(1, 5))
+        K = int(rng.integers(1, 4))
+        tail = int(rng.integers(0, 3))
+        k = rng.integers(-3, 4, size=(n, d), dtype=np.int8)
+        q = rng.integers(-3, 4, size=d, dtype=np.int8)
+        t = int(rng.integers(0, n * r + r - 1))  # up to the token before entry n completes
+        blk, bc, tk, tc = oracle.select(q[None], [0], [t], k[None], B, P, K, tail=tail, ratio=r)
+        pool, top = _select_compressed_brute(q, k, t, r, B, P, K, tail)
+        assert list(blk[0, :bc[0]]) == pool, (r, B, n, t, tail)
+        assert (blk[0, bc[0]:] == -1).all()
+        assert list(tk[0, :tc[0]]) == top, (r, B, n, t, tail)
+        assert (tk[0, tc[0]:] == -1).all()
+
+
+def test_compressed_selection_hand_case():
+    """Ratio 4, blocks of 2 entries, pool 1, Top-2; entry scores 1, 2, 5, 4
+    (d = 1, q = 1).  Worked by hand:
+      t = 2 : no entry complete                       -> nothing selected
+      t = 3 : entry 0 (tokens 0..3)                    -> pool [0], Top-K [0]
+      t = 7 : entries 0, 1; block 0 key round(1.5) = 2 -> pool [0], Top-K [0, 1]
+      t = 11: entries 0..2; block 1 holds entry 2 only, key 5 beats 2
+                                                      -> pool [1], Top-K [2]
+      t = 14: still entries 0..2 (entry 3 ends at 15)  -> pool [1], Top-K [2]
+      t = 15: entries 0..3; block 1 key round(4.5) = 4 -> pool [1], Top-K [2, 3]"""
+    k = np.array([[1], [2], [5], [4]], dtype=np.int8)
+    q = np.array([1], dtype=np.int8)
+    want = {2: ([], []), 3: ([0], [0]), 7: ([0], [0, 1]), 11: ([1], [2]), 14: ([1], [2]),
+            15: ([1], [2, 3])}
+    for t, (pool, top) in want.items():
+        blk, bc, tk, tc = oracle.select(q[None], [0], [t], k[None], 2, 1, 2, ratio=4)
+        assert list(blk[0, :bc[0]]) == pool, t
+        assert list(tk[0, :tc[0]]) == top, t
+
+
+def test_compressed_layers_against_scratch():
+    """A compressed prompt (ratio 2, every token a query) through Full, Reuse,
+    window-only: each layer recomputed from scratch (entries by enumeration,
+    fp64 SDPA over the selected entries plus the per-token window).  The
+    first token sees no entry and attends to its window alone."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=21, n_heads=2, head_dim=8, d_idx=32, block=2, pool=3,
+                   top_k=3, window=4, layers=("full", "reuse", "swa"), ratio=2)
+    wl = W.generate(cfg, seed=43)
+    assert wl.k_idx.shape[1] == 10 and wl.k_swa[0].shape[1] == 21
+    res = oracle.run_layers(wl)
+    sets = [_select_compressed_brute(wl.q_idx[0][i], wl.k_idx[0], int(wl.q_pos[i]), 2, cfg.block,
+                                     cfg.pool, cfg.top_k, cfg.tail) for i in range(cfg.n_q)]
+    assert sets[0] == ([], []) and sets[1][1] == [0]
+    _assert_index(res["index"][0], sets)
+    for layer, s in ((0, sets), (1, sets), (2, None)):
+        np.testing.assert_allclose(res["out"][layer], _sdpa_layer(wl, layer, 0, s), rtol=1e-12, atol=1e-12)

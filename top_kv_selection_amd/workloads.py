@@ -71,6 +71,7 @@ class Config:
     layers: tuple            # per-layer mode, model order
     tail: int = TAIL_VISIBLE  # reading of a partial own block (see TAIL_*)
     replay: int = 0          # (not decode) queries are only the last `replay` positions
+    ratio: int = 1           # tokens per main-KV entry (compressed main-KV and indexer caches)
 
     @property
     def seed(self) -> int:
@@ -81,6 +82,12 @@ class Config:
         if self.decode:
             return self.n_seq
         return self.n_seq * (self.replay if self.replay > 0 else self.ctx)
+
+    @property
+    def main_len(self) -> int:
+        """Entries of the main-KV and indexer caches per sequence: one per
+        ``ratio`` tokens, complete groups only."""
+        return self.ctx // self.ratio
 
     @property
     def n_caches(self) -> int:
@@ -173,9 +180,9 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 @dataclasses.dataclass
 class Workload:
     cfg: Config
-    k_idx: np.ndarray          # int8 [S][T][d]
+    k_idx: np.ndarray          # int8 [S][main_len][d]
     q_idx: dict                # layer -> int8 [n_q][d]  (indexing layers only)
-    k_main: np.ndarray         # [S][T][D]  float32 or uint16 (bf16 bits)
+    k_main: np.ndarray         # [S][main_len][D]  float32 or uint16 (bf16 bits)
     v_main: np.ndarray
     q: list                    # per layer [n_q][H][D]
     k_swa: list                # per layer [S][swa_len][D]
@@ -215,7 +222,7 @@ def generate(cfg: Config, seed: Optional[int] = None, int_range=(-127, 127)) -> 
     """Draw one workload in the fixed order stated in the module docstring.
     ``int_range`` narrows the int8 draws (e.g. (-2, 2)) to force many score ties."""
     rng = np.random.Generator(np.random.PCG64(cfg.seed if seed is None else seed))
-    S, T, d, H, D = cfg.n_seq, cfg.ctx, cfg.d_idx, cfg.n_heads, cfg.head_dim
+    S, T, d, H, D = cfg.n_seq, cfg.main_len, cfg.d_idx, cfg.n_heads, cfg.head_dim
     lo, hi = int_range
     k_idx = _ints(rng, (S, T, d), lo, hi)
     q_idx = {i: _ints(rng, (cfg.n_q, d), lo, hi) for i in cfg.index_layers}
