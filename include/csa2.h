@@ -37,7 +37,8 @@
  *     caller's next synchronisation.  Nothing is printed, nothing is thrown.
  *   - Positions: sequence s holds positions 0..T-1 in every cache; a query row
  *     i belongs to sequence q_seq[i] at position q_pos[i] (0 <= q_pos[i] < T)
- *     and sees positions <= q_pos[i] only (the pages: both stacks are causal).
+ *     and sees positions <= q_pos[i] only (the pages: both stacks are causal);
+ *     with a compression ratio the main caches count entries (see csa2_cfg).
  *     Device-side values of q_seq/q_pos are trusted: out-of-range values are
  *     undefined behaviour, not an error code.
  *   - Workspace: `ws` is device memory of at least csa2_workspace_bytes()
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 typedef enum {
     CSA2_OK = 0,
@@ -107,8 +108,20 @@ typedef struct {
     int32_t dtype;     /* csa2_dtype of Q, K, V and the output                    */
     float scale;       /* logit scale; 0 means 1/sqrt(head_dim)                  */
     int32_t tail;      /* csa2_tail reading of a partial own block                */
+    int32_t ratio;     /* tokens per main-KV entry, 0 or 1 .. 256; see below      */
 } csa2_cfg;
-/* Limits: P*B <= 16384 candidates per query (the pages' cap on candidates
+/* Compressed main-KV (the architecture figure of the V4.1 Flash page names
+ * CSA2(ratio, mode) and leaves the ratio undefined; this library reads it so):
+ * with ratio r > 1 the main-KV and indexer caches (k_idx, k_blk, K and V
+ * main) hold one entry per r tokens, entry j standing for tokens j*r ..
+ * j*r + r - 1, made outside the library like every other K/V row.  q_pos
+ * stays a token position; a query at token t sees the complete entries
+ * 0 .. (t + 1) / r - 1 (it needs (t + 1) / r <= T, T counting entries), and
+ * blocks, pool, Top-K ids and k_blk all count entries.  A query with no
+ * complete entry (t < r - 1) selects nothing and attends to its window alone,
+ * so r > 1 needs window >= 1.  The window caches keep one row per token.
+ * Ratio 0 or 1: one entry per token.
+ * Limits: P*B <= 16384 candidates per query (the pages' cap on candidates
  * scored by an indexer); T <= 2^24 positions.
  * Flat Top-K (no block hierarchy): block = 1 and pool = top_k select the K
  * best tokens of the whole prefix directly; the block keys of blocks of one
@@ -182,6 +195,8 @@ int32_t csa2_build_block_keys(const csa2_cfg *cfg, const int8_t *k_idx, int32_t 
  *   k_main/v_main : device [n_seq][T][head_dim]         (in/out)
  *   k_blk       : device int8 [n_seq][T/B][d_idx], or NULL to leave block keys
  *                 to a later csa2_build_block_keys / Full layer group
+ * With compressed main-KV (cfg->ratio > 1) the rows are entries and pos[i] an
+ * entry index: the caller appends entry j once its r tokens have arrived.
  * n_new = 0 launches nothing and accepts empty (NULL) arrays.  No workspace. */
 int32_t csa2_append_tokens(const csa2_cfg *cfg, int32_t n_new, const int32_t *seq, const int32_t *pos,
                            const int8_t *new_k_idx, const void *new_k, const void *new_v, int8_t *k_idx,
@@ -248,7 +263,8 @@ int32_t csa2_topk_tokens(const csa2_cfg *cfg, int32_t n_q, const int8_t *q_idx,
  *   out    : device [n_layers][n_q][H][D]             (dtype) out
  *   lse    : device fp32 [n_layers][n_q][H] out (natural-log normaliser) or NULL
  * Window positions outside [swa_first, swa_first + swa_len) are not attended:
- * callers supply rows covering every query's window. */
+ * callers supply rows covering every query's window.  Window positions are
+ * tokens; with compressed main-KV (ratio r) they may reach T*r + r - 2. */
 int32_t csa2_attend_group(const csa2_cfg *cfg, int32_t n_layers, int32_t n_q, const void *q,
                           const int32_t *q_seq, const int32_t *q_pos, const void *k_main,
                           const void *v_main, int32_t n_seq, int32_t T, const void *k_swa,

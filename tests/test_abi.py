@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(B):
 
 
 def test_abi_version_and_status_strings(B):
-    assert B.csa2_abi_version() == B.ABI_VERSION == 2
+    assert B.csa2_abi_version() == B.ABI_VERSION == 3
     for s in range(9):
         assert B._lib.csa2_status_str(s).decode()
     assert B._lib.csa2_status_str(99).decode() == "unknown status"
@@ -83,6 +83,7 @@ def test_workspace_bytes_grow_with_every_size(B):
     ("d_idx", 48, 4), ("head_dim", 96, 4), ("block", 0, 2), ("block", 17, 2), ("pool", 0, 2),
     ("top_k", -1, 2), ("window", 2000, 2), ("dtype", 7, 3), ("n_heads", 0, 2),
     ("scale", float("nan"), 2), ("scale", -1.0, 2), ("tail", 3, 2), ("tail", -1, 2),
+    ("ratio", -1, 2), ("ratio", 257, 2),
 ])
 def test_bad_config_is_rejected(B, field, value, status):
     c = dataclasses.asdict(B.Cfg())
@@ -98,6 +99,8 @@ def test_pool_times_block_cap_and_empty_selection(B):
     assert f(B.Cfg(pool=2049, block=8)) == 2          # more than 16,384 candidates
     assert f(B.Cfg(pool=2048, block=8, top_k=16385)) == 2
     assert f(B.Cfg(top_k=0, window=0)) == 2            # nothing to attend
+    assert f(B.Cfg(ratio=4, window=0)) == 2            # a query before the first entry would see nothing
+    assert f(B.Cfg(ratio=4, window=1)) == 0
     assert f(B.Cfg(top_k=0, window=128)) == 0          # window only is fine
     assert B._lib.csa2_workspace_bytes(None, 1, 64, 1, ctypes.byref(out)) == 1
 

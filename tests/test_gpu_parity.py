@@ -608,3 +608,81 @@ def test_prefill_dense_topk_adversarial(lib, kind):
     print(f"case dense Top-K adversarial ({kind}): n_q={cfg.n_q} T={cfg.ctx}", flush=True)
     got = run_gpu(pipeline, wl)
     compare_run(got, oracle.run_layers(wl), cfg, what=f"adversarial ({kind})")
+
+
+# ------------------------------------------------------------------ compressed main-KV
+# CSA2(ratio, mode): the main-KV and indexer caches hold one entry per `ratio`
+# tokens (entry j = tokens j*ratio .. j*ratio + ratio - 1), a query at token t
+# selects among the entries complete at t, and its window stays per token.
+def test_compressed_decode_layer_group_128k(lib):
+    """The 128K layer group at ratio 4: 32,768 entries, 4,096 eligible blocks
+    per query through the fused layer group."""
+    check(lib, W.CONFIGS["decode_group_128k_c4"])
+
+
+def test_compressed_decode_ragged_context(lib):
+    """A context that is no multiple of the ratio (the newest tokens form an
+    incomplete entry that only the window holds) nor of the block; ratio 3,
+    pool below the eligible blocks, several workgroups per query."""
+    cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=5, ctx=20002, pool=96, top_k=100, window=37, ratio=3)
+    check(lib, cfg, seed=51)
+
+
+def test_compressed_decode_past_the_fused_limit(lib):
+    """Ratio 2 at 600,000 tokens: 300,000 entries in blocks of 8 (37,500
+    eligible blocks) take the separate launches."""
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=2, ctx=600000, layers=("full", "reuse"), ratio=2)
+    check(lib, cfg, seed=52)
+
+
+@pytest.mark.parametrize("tail", [W.TAIL_VISIBLE, W.TAIL_EXCLUDE, W.TAIL_WHOLE])
+def test_compressed_prefill_block_pass(lib, tail):
+    """Every token of a 1,501-token prompt at ratio 3 (500 entries) with a pool
+    below the eligible blocks: block pass, pool selection and per-query token
+    Top-K over entries; the first two tokens see no entry and attend to their
+    window alone."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=1501, pool=24, top_k=64, window=40,
+                   layers=("full", "reuse", "swa"), ratio=3, tail=tail)
+    check(lib, cfg, seed=53 + tail)
+
+
+@pytest.mark.parametrize("tail", [W.TAIL_VISIBLE, W.TAIL_EXCLUDE, W.TAIL_WHOLE])
+def test_compressed_prefill_whole_prefix_pools(lib, tail):
+    """A 3,001-token prompt at ratio 4 (750 entries): whole-prefix pools, the
+    dense token Top-K over entries and the row attention, four queries per
+    entry."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k_c4"], ctx=3001, tail=tail, layers=("full", "reuse", "swa"))
+    check(lib, cfg, seed=56 + tail)
+
+
+def test_compressed_prefill_8k_all_rows(lib):
+    check(lib, W.CONFIGS["prefill_8k_c4"])
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_compressed_layer_group_leaves_every_completed_block_key(lib, decode):
+    """With compressed caches a Full layer group stores the key of every entry
+    block its queries complete (a block is complete once its last entry is),
+    bit-exact, and leaves the others alone."""
+    B, pipeline = lib
+    if decode:
+        cfg = W.scaled(W.CONFIGS["decode_full_32k"], n_seq=3, ctx=4096, pool=64, top_k=128, ratio=4)
+    else:
+        cfg = W.scaled(W.CONFIGS["prefill_8k"], n_seq=2, ctx=1003, pool=200, top_k=100, window=40,
+                       layers=("full", "reuse"), ratio=3)
+    print(f"case compressed block keys decode={decode} S={cfg.n_seq} T={cfg.ctx} r={cfg.ratio}", flush=True)
+    wl = W.generate(cfg, seed=59)
+    dw = pipeline.upload(wl)
+    n = cfg.main_len
+    nblk = n // cfg.block
+    if decode:
+        pipeline.build_cache(dw, upto_block=nblk - 1)   # the newest entry completes the last block
+    assert pipeline.step_update_begin(dw) == nblk
+    pipeline.run(dw)
+    torch.cuda.synchronize()
+    got = dw.k_blk.cpu().numpy()
+    for s in range(cfg.n_seq):
+        for j in range(nblk):
+            want = oracle.block_key(wl.k_idx[s], cfg.block, j, n - 1)
+            assert np.array_equal(got[s, j], want), (s, j)
+    compare_run(pipeline.outputs(dw), oracle.run_layers(wl), cfg, what="compressed block keys")

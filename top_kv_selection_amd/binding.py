@@ -22,7 +22,7 @@ FULL, REINDEX, REUSE, SWA, REINDEX_TOKENS = 0, 1, 2, 3, 4
 MODES = {"full": FULL, "reindex": REINDEX, "reuse": REUSE, "swa": SWA, "reindex_tokens": REINDEX_TOKENS}
 F32, BF16 = 0, 1
 TAIL_VISIBLE, TAIL_EXCLUDE, TAIL_WHOLE = 0, 1, 2
-ABI_VERSION = 2          # csa2_cfg layout of include/csa2.h
+ABI_VERSION = 3          # csa2_cfg layout of include/csa2.h
 
 STATUS = {0: "CSA2_OK", 1: "CSA2_E_NULL", 2: "CSA2_E_SHAPE", 3: "CSA2_E_DTYPE",
           4: "CSA2_E_UNSUPPORTED", 5: "CSA2_E_ALIGN", 6: "CSA2_E_WORKSPACE", 7: "CSA2_E_HIP",
@@ -44,7 +44,7 @@ class _CCfg(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("pool", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("d_idx", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("tail", ctypes.c_int32)]
+                ("tail", ctypes.c_int32), ("ratio", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -59,10 +59,11 @@ class Cfg:
     dtype: int = BF16
     scale: float = 0.0
     tail: int = 0           # TAIL_VISIBLE / TAIL_EXCLUDE / TAIL_WHOLE
+    ratio: int = 1          # tokens per main-KV entry (compressed main-KV and indexer caches)
 
     def c(self) -> _CCfg:
         return _CCfg(self.block, self.pool, self.top_k, self.window, self.d_idx, self.n_heads,
-                     self.head_dim, self.dtype, float(self.scale), int(self.tail))
+                     self.head_dim, self.dtype, float(self.scale), int(self.tail), int(self.ratio))
 
     @property
     def torch_dtype(self):
@@ -314,7 +315,7 @@ def csa2_layer_group_static(cfg: Cfg, mode, q_idx, q_seq, q_pos, k_idx, k_blk, b
 def cfg_of(wcfg) -> Cfg:
     """Library config from a workload description (top_kv_selection_amd.workloads.Config)."""
     return Cfg(wcfg.block, wcfg.pool, wcfg.top_k, wcfg.window, wcfg.d_idx, wcfg.n_heads, wcfg.head_dim,
-               F32 if wcfg.dtype == "f32" else BF16, 0.0, wcfg.tail)
+               F32 if wcfg.dtype == "f32" else BF16, 0.0, wcfg.tail, wcfg.ratio)
 
 
 def default_scale(head_dim: int) -> float:

@@ -113,6 +113,9 @@ int32_t check_cfg(const csa2_cfg *c)
     if (!(c->scale >= 0.f) || !isfinite(c->scale)) return CSA2_E_SHAPE;
     if (c->tail != CSA2_TAIL_VISIBLE && c->tail != CSA2_TAIL_EXCLUDE && c->tail != CSA2_TAIL_WHOLE)
         return CSA2_E_SHAPE;
+    // compressed main-KV: a query before the first complete entry attends to
+    // its window alone, so a window is required
+    if (c->ratio < 0 || c->ratio > kMaxRatio || (c->ratio > 1 && c->window < 1)) return CSA2_E_SHAPE;
     return CSA2_OK;
 }
 
@@ -181,6 +184,7 @@ int32_t do_index(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int3
     p.q_idx = q_idx; p.q_seq = q_seq; p.q_pos = q_pos; p.k_idx = k_idx; p.k_blk = k_blk;
     p.k_blk_store = k_blk_store;
     p.T = T; p.B = c->block; p.P = c->pool; p.n_q = n_q; p.G = pl.G; p.chunk = pl.chunk; p.tail = c->tail;
+    p.ratio = c->ratio;
     p.nblk = T / c->block;
     p.ws_keys = (uint32_t *)r.data;
     p.ws_stride = ((long long)(T - 1) / c->block + 1 + 3) / 4 * 4;   // rows 16-byte aligned
@@ -210,6 +214,7 @@ int32_t do_topk(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int32
     p.q_idx = q_idx; p.q_seq = q_seq; p.q_pos = q_pos; p.k_idx = k_idx;
     p.blk_ids = blk_ids; p.blk_cnt = blk_cnt;
     p.T = T; p.B = c->block; p.P = c->pool; p.K = c->top_k; p.n_q = n_q; p.G = pl.G; p.tail = c->tail;
+    p.ratio = c->ratio;
     p.chunk = pl.chunk;
     p.ws_keys = (uint32_t *)r.data;
     p.ws_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
@@ -239,7 +244,12 @@ int32_t do_attend(const csa2_cfg *c, int32_t n_layers, int32_t n_q, const void *
     if (has_main && (!k_main || !v_main)) return CSA2_E_NULL;
     if (c->window > 0 && (!k_swa || !v_swa)) return CSA2_E_NULL;
     if (!has_main && c->window < 1) return CSA2_E_SHAPE;
-    if (c->window > 0 && (swa_len < 1 || swa_first < 0 || swa_first >= T || swa_len > T)) return CSA2_E_SHAPE;
+    // tokens a sequence may hold: T, or with compressed main-KV the tokens of
+    // its T entries plus an incomplete group
+    const int per_entry = std::max(c->ratio, 1);
+    const long long n_tok = (long long)T * per_entry + (per_entry - 1);
+    if (c->window > 0 && (swa_len < 1 || swa_first < 0 || swa_first >= n_tok || swa_len > n_tok))
+        return CSA2_E_SHAPE;
     const void *dev16[] = {q, out, k_main, v_main, k_swa, v_swa};
     for (const void *ptr : dev16)
         if (ptr && !aligned16(ptr)) return CSA2_E_ALIGN;
@@ -421,6 +431,7 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     ip.tok_hist_clear = tok_hist;
     ip.T = T; ip.B = c->block; ip.P = c->pool; ip.n_q = n_q; ip.G = f.idx.G; ip.chunk = f.idx.chunk;
     ip.tail = c->tail;
+    ip.ratio = c->ratio;
     ip.nblk = T / c->block;
     ip.ws_keys = blk_keys; ip.ws_stride = f.blk_stride; ip.ws_hist = head;
     ip.blk_ids = blk_ids; ip.blk_cnt = blk_cnt;
@@ -431,6 +442,7 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     tp.q_idx = q_idx; tp.q_seq = q_seq; tp.q_pos = q_pos; tp.k_idx = k_idx;
     tp.blk_ids = blk_ids; tp.blk_cnt = blk_cnt;
     tp.T = T; tp.B = c->block; tp.P = c->pool; tp.K = c->top_k; tp.n_q = n_q; tp.tail = c->tail;
+    tp.ratio = c->ratio;
     tp.G = f.tok.G; tp.chunk = f.tok.chunk;
     tp.ws_keys = tok_keys; tp.ws_stride = f.tok_stride; tp.ws_hist = tok_hist;
     tp.topk = topk; tp.topk_cnt = topk_cnt;

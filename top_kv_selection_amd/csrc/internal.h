@@ -40,13 +40,27 @@ constexpr int kSelectThreads = 512;     // threads of a scoring or many-query se
 constexpr int kSelectWideThreads = 1024; // threads of a one-query-per-workgroup select launch (16 keys each)
 constexpr int kTargetWorkgroups = 512;  // ~2 per CU on a 256-CU MI355X
 constexpr int kMaxCandidates = 16384;   // P*B cap: candidates one query may score
+constexpr int kMaxRatio = 256;          // largest csa2_cfg.ratio (tokens per main-KV entry)
 constexpr int kTailExclude = 1;         // csa2_tail values the kernels test
 constexpr int kTailWhole = 2;
 
-// Blocks eligible for a query at position t: every block holding a visible
-// token, or only the complete ones when a partial own block is excluded.
+// Last main-KV entry a query at token position t sees.  With `ratio` tokens
+// compressed into one entry (the "CSA2(ratio, mode)" of the V4.1 Flash
+// page's architecture figure), entry j stands for tokens j*ratio ..
+// j*ratio + ratio - 1 and exists once the last of them has arrived, so the
+// visible entries are 0 .. (t + 1) / ratio - 1; -1 when none is complete yet.
+// Ratio 1 (or 0, the default) is one entry per token.
+__host__ __device__ inline int main_pos(int t, int ratio)
+{
+    return ratio > 1 ? (t + 1) / ratio - 1 : t;
+}
+
+// Blocks eligible for a query whose last visible entry is t: every block
+// holding a visible entry, or only the complete ones when a partial own block
+// is excluded; none when no entry is visible (t < 0).
 __host__ __device__ inline int eligible_blocks(int t, int B, int tail)
 {
+    if (t < 0) return 0;
     return tail == kTailExclude ? (t + 1) / B : t / B + 1;
 }
 
@@ -75,6 +89,7 @@ struct IndexParams {
     uint32_t *tok_hist_clear;   // non-null (fused layer group): zero [n_q][2048] token histograms
     int T, B, P, n_q, G, chunk, nblk;
     int tail;               // csa2_tail reading of a partial own block
+    int ratio;              // tokens per main-KV entry: q_pos are tokens, the caches entries
     uint32_t *ws_keys;
     int64_t ws_stride;
     uint32_t *ws_hist;      // [n_q][2048] top-11-bit histograms (split launches)
@@ -88,6 +103,7 @@ struct TopkParams {
     const int32_t *blk_ids, *blk_cnt;
     int T, B, P, K, n_q, G, chunk;
     int tail;               // csa2_tail reading of a partial own block
+    int ratio;              // tokens per main-KV entry (see main_pos)
     uint32_t *ws_keys;
     int64_t ws_stride;
     uint32_t *ws_hist;

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     const int q = blockIdx.x / p.G;   // a query's workgroups are consecutive: spread over the XCDs
     const int g = blockIdx.x % p.G;
     const int tid = threadIdx.x, part = tid % LPR;
-    const int s = p.q_seq[q], t = p.q_pos[q];
+    const int s = p.q_seq[q], t = main_pos(p.q_pos[q], p.ratio);   // last visible entry (-1: none)
     const int jt = t / p.B, n_elig = eligible_blocks(t, p.B, p.tail);
     int32_t *ids = p.blk_ids + (size_t)q * p.P;
     // rows averaged into the own block's key: those at positions <= t, or
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     // workgroup whose range holds it, one lane per dimension.  A Full layer
     // also stores the key of a block its query has just completed (t is the
     // block's last position).
-    const bool store_own = p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk;
+    const bool store_own = p.k_blk_store != nullptr && t >= 0 && (t + 1) % p.B == 0 && jt < p.nblk;
     int8_t *own_store = store_own ? p.k_blk_store + ((size_t)s * p.nblk + jt) * DIDX : nullptr;
     const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX;
 
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kPoolAllThreads) void k_pool_all(IndexParams p)
         const size_t total = (size_t)p.n_q * P4;
         for (size_t k = id; k < total; k += stride) {
             const int q = (int)(k / P4), j = 4 * (int)(k % P4);
-            const int n = eligible_blocks(p.q_pos[q], p.B, p.tail);
+            const int n = eligible_blocks(main_pos(p.q_pos[q], p.ratio), p.B, p.tail);
             const int4 v = make_int4(j < n ? j : -1, j + 1 < n ? j + 1 : -1, j + 2 < n ? j + 2 : -1,
                                      j + 3 < n ? j + 3 : -1);
             // nontemporal: the ids are not read again in this step, and
@@ -294,15 +294,15 @@ __global__ __launch_bounds__(kPoolAllThreads) void k_pool_all(IndexParams p)
         const size_t total = (size_t)p.n_q * p.P;
         for (size_t k = id; k < total; k += stride) {
             const int q = (int)(k / p.P), j = (int)(k % p.P);
-            p.blk_ids[k] = (j < eligible_blocks(p.q_pos[q], p.B, p.tail)) ? j : -1;
+            p.blk_ids[k] = (j < eligible_blocks(main_pos(p.q_pos[q], p.ratio), p.B, p.tail)) ? j : -1;
         }
     }
     for (size_t k = id; k < (size_t)p.n_q * DIDX; k += stride) {
         const int q = (int)(k / DIDX), d = (int)(k % DIDX);
-        const int s = p.q_seq[q], t = p.q_pos[q];
+        const int s = p.q_seq[q], t = main_pos(p.q_pos[q], p.ratio);
         const int jt = t / p.B;
         if (d == 0) p.blk_cnt[q] = eligible_blocks(t, p.B, p.tail);
-        if (p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk) {
+        if (p.k_blk_store != nullptr && t >= 0 && (t + 1) % p.B == 0 && jt < p.nblk) {
             const int8_t *own_rows = p.k_idx + ((size_t)s * p.T + (size_t)jt * p.B) * DIDX;
             p.k_blk_store[((size_t)s * p.nblk + jt) * DIDX + d] = (int8_t)block_key_dim<DIDX>(own_rows, p.B, d);
         }
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(NT) void k_index_select(IndexParams p)
     uint32_t k[IPT];
     const bool fits = p.ws_stride <= NT * IPT;
     if (fits) load_keys_global<IPT>(gkeys, (int)p.ws_stride, k);
-    const int t = p.q_pos[q];
+    const int t = main_pos(p.q_pos[q], p.ratio);
     const int n_elig = eligible_blocks(t, p.B, p.tail);
     if (n_elig <= p.P) return;   // handled by the scoring launch (nothing was stored)
     store_hist<NT>(hr, ghist, s_hist);
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
     const int q = blockIdx.x % p.n_q;   // query-fastest: k_topk_select reads a query's keys on its XCD
     const int g = blockIdx.x / p.n_q;
     const int tid = threadIdx.x, part = tid % LPR;
-    const int s = p.q_seq[q], t = p.q_pos[q];
+    const int s = p.q_seq[q], t = main_pos(p.q_pos[q], p.ratio);   // last visible entry
     const int B = p.B;
     const int n_pool = p.blk_cnt[q];
     const int n_cand = n_pool * B;                    // <= P*B <= kLdsKeys
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams 
     uint32_t k[IPT];
     load_keys_global<IPT>(ip.ws_keys + (size_t)q * ip.ws_stride, (int)ip.ws_stride, k);
     const int4 qv = *reinterpret_cast<const int4 *>(tp.q_idx + (size_t)q * DIDX + part * 16);
-    const int s = ip.q_seq[q], t = ip.q_pos[q];
+    const int s = ip.q_seq[q], t = main_pos(ip.q_pos[q], ip.ratio);   // last visible entry
     const int n_elig = eligible_blocks(t, B, ip.tail);
     hist_to_lds<NT>(hr, s_hist);
     // this workgroup's pool slots [s0, s0 + n_slots): s_pool[x] holds slot s0 + x
@@ -768,10 +768,11 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
     const int qi = q0 + r16;
     const bool qvalid = qi < p.n_q;
     const int sq = qvalid ? p.q_seq[qi] : -1;
-    // last candidate position of this lane's query: its position, or with a
-    // partial own block excluded the end of its last complete block (-1: no
-    // candidate)
-    const int tq = !qvalid ? -1 : (p.tail == kTailExclude ? (p.q_pos[qi] + 1) / p.B * p.B - 1 : p.q_pos[qi]);
+    // last candidate entry of this lane's query: its last visible entry, or
+    // with a partial own block excluded the end of its last complete block
+    // (-1: no candidate)
+    const int tv = qvalid ? main_pos(p.q_pos[qi], p.ratio) : -1;
+    const int tq = p.tail == kTailExclude ? (tv + 1) / p.B * p.B - 1 : tv;
     v4i32 qb = {0, 0, 0, 0};
     if (qvalid && 16 * g < DIDX) qb = *reinterpret_cast<const v4i32 *>(p.q_idx + (size_t)qi * DIDX + 16 * g);
     uint32_t *gt_map = s_buf, *eq_map = s_buf + kDenseQ * MW;
@@ -781,9 +782,9 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
         for (int x = tid; x < kDenseQ * DIDX; x += NT) {
             const int i = q0 + x / DIDX, dd = x % DIDX;
             if (i >= p.n_q) continue;
-            const int t = p.q_pos[i], jt = t / p.B;
+            const int t = main_pos(p.q_pos[i], p.ratio), jt = t / p.B;
             if (dd == 0) p.pool_cnt_out[i] = eligible_blocks(t, p.B, p.tail);
-            if (p.k_blk_store != nullptr && (t + 1) % p.B == 0 && jt < p.nblk) {
+            if (p.k_blk_store != nullptr && t >= 0 && (t + 1) % p.B == 0 && jt < p.nblk) {
                 const size_t row0 = (size_t)p.q_seq[i] * p.T + (size_t)jt * p.B;
                 p.k_blk_store[((size_t)p.q_seq[i] * p.nblk + jt) * DIDX + dd] =
                     (int8_t)block_key_dim<DIDX>(p.k_idx + row0 * DIDX, p.B, dd);

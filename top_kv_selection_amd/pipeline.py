@@ -65,7 +65,7 @@ class DeviceWorkload:
 def whole_prefix_pools(cfg: Config) -> bool:
     """Every query's pool is all of its eligible blocks (the longest context
     has at most P blocks): the library then needs no stored pool ids."""
-    return (cfg.ctx - 1) // cfg.block + 1 <= cfg.pool
+    return (cfg.main_len - 1) // cfg.block + 1 <= cfg.pool
 
 
 def group_caches(cfg: Config) -> list:
@@ -235,9 +235,10 @@ def algorithmic_bytes(cfg: Config) -> dict:
                                   cfg.window, cfg.n_heads, cfg.head_dim)
     esz = 4 if cfg.dtype == "f32" else 2
     n_q = cfg.n_q
-    t = T - 1
-    n_elig = t // B + 1
-    own = t - (n_elig - 1) * B + 1                  # visible rows of the query's own block
+    t = T - 1                                       # token position (window)
+    tm = (t + 1) // cfg.ratio - 1                   # last visible main-KV entry (selection)
+    n_elig = tm // B + 1
+    own = tm - (n_elig - 1) * B + 1                 # visible rows of the query's own block
     pool = min(P, n_elig)
     n_cand = pool * B - (B - own)                   # the own block is pooled at most once
     sel = min(K, n_cand)
@@ -266,12 +267,13 @@ def algorithmic_ops(cfg: Config) -> dict:
     S, T, d, B, P, K, W_, H, D = (cfg.n_seq, cfg.ctx, cfg.d_idx, cfg.block, cfg.pool, cfg.top_k,
                                   cfg.window, cfg.n_heads, cfg.head_dim)
     _, q_pos = query_rows(cfg)
-    t = q_pos.astype(np.int64)
-    n_elig = t // B + 1
+    t = q_pos.astype(np.int64)                               # token positions (window)
+    tm = (t + 1) // cfg.ratio - 1                            # last visible main-KV entry (-1: none)
+    n_elig = np.where(tm >= 0, tm // B + 1, 0)
     pool = np.minimum(P, n_elig)
     block_ops = np.where(n_elig > P, n_elig * d * 2, 0)      # no scoring when the pool is the prefix
-    own = t - (n_elig - 1) * B + 1
-    n_cand = pool * B - (B - own)
+    own = np.where(tm >= 0, tm - (n_elig - 1) * B + 1, B)
+    n_cand = np.maximum(pool * B - (B - own), 0)
     sel = np.minimum(K, n_cand)
     win = np.minimum(W_, t + 1)
     out = {"index_blocks": [], "topk_tokens": [], "attend": []}
@@ -306,9 +308,10 @@ def kernel_work(cfg: Config) -> dict:
 
     if cfg.decode:
         n_q = cfg.n_q
-        t = T - 1
-        n_elig = t // B + 1
-        own = t - (n_elig - 1) * B + 1
+        t = T - 1                                   # token position (window)
+        tm = (t + 1) // cfg.ratio - 1               # last visible main-KV entry (selection)
+        n_elig = tm // B + 1
+        own = tm - (n_elig - 1) * B + 1
         pool = min(P, n_elig)
         n_cand = pool * B - (B - own)
         sel = min(K, n_cand)
@@ -337,7 +340,7 @@ def kernel_work(cfg: Config) -> dict:
         else:
             kernel = "k_attend_window" if mode == "swa" else "k_attend_rows"
         add(kernel, "bf16_flops", flops)
-    dense = whole_prefix_pools(cfg) and T <= 16384 and cfg.n_q >= 256
+    dense = whole_prefix_pools(cfg) and cfg.main_len <= 16384 and cfg.n_q >= 256
     for n in ops["topk_tokens"]:
         add("k_topk_dense" if dense else "k_topk_tokens", "int8_ops", n)
     return work

@@ -30,11 +30,20 @@ indexer": the candidate cap holds whatever the context length):
 
 * ``decode_group_256k``   batch 8, 256K context, Full + 5 Reuse
 
+and two workloads with compressed main-KV and indexer caches (the page's
+CSA2(ratio, mode); the ratio is not given there, 4 is an illustration):
+
+* ``decode_group_128k_c4`` the 128K layer group with one entry per 4 tokens
+  (32,768 entries per sequence; the window stays 128 tokens)
+* ``prefill_8k_c4``        the 8K prefill with one entry per 4 tokens
+
 Recipe (both sides read identical bytes):
 * ``numpy.random.Generator(PCG64(1000 + config_number))``;
 * draw order: ``k_idx``, each indexing layer's ``q_idx`` (model order), main K,
   main V, then per layer (model order) Q, sliding-window K, sliding-window V,
   then for every Full layer after the first its own ``k_idx``, main K, main V;
+* main-KV and indexer caches hold ``ctx // ratio`` entries per sequence, the
+  window caches one row per token;
 * int8 values are uniform integers in [-127, 127];
 * real values are standard normal drawn in fp32 and, for bf16 workloads,
   rounded to bf16 with round-to-nearest-even (stored as uint16 bit patterns).
@@ -156,6 +165,10 @@ CONFIGS = {
                _decoder_pattern(), replay=128),
         Config("decode_group_256k", 8, "bf16", 8, 262144, True, 16, 128, 64, 8, 2048, 512, 128,
                (FULL,) + (REUSE,) * 5),
+        Config("decode_group_128k_c4", 9, "bf16", 8, 131072, True, 16, 128, 64, 8, 2048, 512, 128,
+               (FULL,) + (REUSE,) * 5, ratio=4),
+        Config("prefill_8k_c4", 10, "bf16", 1, 8192, False, 16, 128, 64, 8, 2048, 512, 128,
+               (FULL, SWA_ONLY, SWA_ONLY), ratio=4),
     ]
 }
 
