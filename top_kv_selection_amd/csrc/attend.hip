@@ -520,9 +520,20 @@ __global__ __launch_bounds__(32 * kCombineHeads) void k_attend_combine(AttendPar
 //    reduction and no rescale of the accumulators.  The row sum is kept per
 //    lane and reduced across the four lane groups once per item.
 // Tile layout: tile row r (0..31) of a step sits at byte
-// kTileInst * (r % 8) + 256 * (r / 8): load instruction x writes rows
-// x, x+8, x+16, x+24 as one 1 KiB run, and the runs are kTileInst bytes
-// apart so that rows of different instructions start in different banks.
+// inst * (r % 8) + 256 * (r / 8): load instruction x writes rows x, x+8,
+// x+16, x+24 as one 1 KiB run, and the runs are `inst` bytes apart.  The LDS
+// serves 64 banks of 4 bytes per clock, so 256 bytes apart is the same bank:
+//  * V^T reads take 32 bytes of 8 rows (runs 0..7) at once: runs 32 bytes
+//    apart (kRowVInst) put those rows on disjoint banks;
+//  * K reads (A layout) take 16 bytes of 16 rows at once, rows r and r + 8
+//    from one run: runs 16 bytes apart (kRowKInst) spread rows 0..7 over 32
+//    banks, and the rows of odd slots (r / 8 odd) are stored rotated by
+//    128 bytes (chunk c of the row at position (c + 8) % 16 of its slot), so
+//    rows 8..15 take the other 32.  The load of such a row simply fetches its
+//    chunks in that order.
+constexpr int kRowKInst = 1024 + 16;
+constexpr int kRowVInst = 1024 + 32;
+constexpr int kRowTileBytes = 8 * kRowVInst;
 constexpr int kRowWaves = 4;            // waves (items in flight) per workgroup
 constexpr int kRowCodes = 512;          // Top-K row ids staged per wave at once (16 steps)
 constexpr int kRowItemsPerWave = 4;     // items a wave walks in a one-round call
@@ -557,7 +568,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base
 
 __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kRowWaves][2][kTileBytes];   // K, V
+    __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kRowWaves][2][kRowTileBytes];   // K, V
     __shared__ __attribute__((aligned(16))) int s_codes[kRowWaves][kRowCodes];
 
     // the wave index is uniform over the wave: keep it (and the item, its
@@ -663,21 +674,28 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
             rk = rows_rsrc((const uint16_t *)p.k_swa + swa0, p.swa_len);
             rv = rows_rsrc((const uint16_t *)p.v_swa + swa0, p.swa_len);
         }
+        // lane group g fills slot g of each run: K chunks rotated in odd slots
+        const uint32_t koff = (uint32_t)(((r16 + 8 * (g & 1)) & 15) * 16), voff = (uint32_t)r16 * 16u;
 #pragma unroll
         for (int x = 0; x < 8; x++) {
-            const uint32_t off = (uint32_t)row[x] * 256u + (uint32_t)r16 * 16u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(ktile + kTileInst * x), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vtile + kTileInst * x), 16, off, 0, 0, 0);
+            const uint32_t off = (uint32_t)row[x] * 256u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(ktile + kRowKInst * x), 16, off + koff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vtile + kRowVInst * x), 16, off + voff, 0, 0, 0);
         }
     };
 
-    // operand addresses in the tiles (per lane; tau, kk, m, h are immediates)
-    //   K, A layout: tile row 16 tau + r16, bytes 64 kk + 16 g
-    const uint8_t *ka_base = ktile + kTileInst * (r16 & 7) + 256 * (r16 >> 3) + 16 * g;
+    // operand addresses in the tiles (per lane; tau, m, h are immediates)
+    //   K, A layout: tile row 16 tau + r16, row chunk 4 kk + g, which a row
+    //   of an odd slot (r16 >= 8) holds 8 chunks further on
+    const int krot = 8 * (r16 >> 3);
+    const uint8_t *ka_row = ktile + kRowKInst * (r16 & 7) + 256 * (r16 >> 3);
+    const uint8_t *ka_at[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) ka_at[kk] = ka_row + 16 * ((4 * kk + g + krot) & 15);
     //   V^T via the transposing read: lane r16 of group g addresses tile row
     //   16 h + 4 g + r16 / 4, dims 16 m + 4 (r16 % 4) .. +3
     const int vrow = 4 * g + (r16 >> 2);
-    const uint8_t *va_base = vtile + kTileInst * (vrow & 7) + 256 * (vrow >> 3) + 8 * (r16 & 3);
+    const uint8_t *va_base = vtile + kRowVInst * (vrow & 7) + 256 * (vrow >> 3) + 8 * (r16 & 3);
 
     // Items one after another.  While an item runs, the next item's table
     // entries, ids and query rows are loaded (issued right after the loads of
@@ -754,7 +772,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
             for (int tau = 0; tau < 2; tau++)
 #pragma unroll
                 for (int kk = 0; kk < 4; kk++)
-                    ka[tau][kk] = *reinterpret_cast<const bf16x8_t *>(ka_base + 512 * tau + 64 * kk);
+                    ka[tau][kk] = *reinterpret_cast<const bf16x8_t *>(ka_at[kk] + 512 * tau);
 #pragma unroll
             for (int m = 0; m < 8; m++) {
                 const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(va_base + 32 * m));
