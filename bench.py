@@ -276,7 +276,8 @@ def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_sec
         "config": {"workload": name, "batch": cfg.n_seq, "context": cfg.ctx, "layers": "+".join(cfg.layers),
                    "queries_per_step": n_queries, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
                    "d_idx": cfg.d_idx, "block": cfg.block, "pool": cfg.pool, "top_k": cfg.top_k,
-                   "window": cfg.window, "replicas": R, "streams": NS, "parallelism": "none (1 GPU)"},
+                   "window": cfg.window, "ratio": cfg.ratio, "replicas": R, "streams": NS,
+                   "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "roofline_step": step,
         "launch_floor_us": round(floor_us, 3),
