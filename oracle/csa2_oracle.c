@@ -174,7 +174,7 @@ int orc_topk_one(const int8_t *q_idx, const int8_t *k_seq, int T, int t, int d, 
 int orc_visible_entries(int t, int r)
 {
     if (r < 1 || t < 0) return -1;
-    return (t + 1) / r;
+    return (int)(((int64_t)t + 1) / r);   /* t + 1 may exceed INT32_MAX */
 }
 
 /* No visible entry: an empty selection (every slot -1, counts 0). */

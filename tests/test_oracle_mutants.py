@@ -45,8 +45,9 @@ MUTANTS = {
     "normaliser ignores the window": ("for (int i = 0; i < cnt + nw; i++) {\n            logit[i] = exp(logit[i] - m);    /* now the unnormalised weight */\n            z += logit[i];",
                                       "for (int i = 0; i < cnt + nw; i++) {\n            logit[i] = exp(logit[i] - m);    /* now the unnormalised weight */\n            if (i < cnt) z += logit[i];"),
     "lse drops the max": ("lse[h] = m + log(z);", "lse[h] = log(z);"),
-    "compressed entry visible before it completes": ("return (t + 1) / r;", "return t / r + 1;"),
-    "compressed entries one late": ("return (t + 1) / r;", "return t / r;"),
+    "compressed entry visible before it completes": ("return (int)(((int64_t)t + 1) / r);",
+                                                     "return (int)((int64_t)t / r + 1);"),
+    "compressed entries one late": ("return (int)(((int64_t)t + 1) / r);", "return (int)((int64_t)t / r);"),
 }
 
 

@@ -598,6 +598,11 @@ def test_visible_entries_by_definition():
         for t in range(0, 40):
             want = sum(1 for j in range(64) if j * r + r - 1 <= t)
             assert oracle.visible_entries(t, r) == want, (r, t)
+    # the largest int32 position (reachable only with compression: T <= 2^24
+    # entries): entries j with (j + 1) * r <= 2^31
+    t = 2**31 - 1
+    for r in (2, 3, 256):
+        assert oracle.visible_entries(t, r) == 2**31 // r, r
 
 
 def test_compressed_selection_matches_enumeration():

@@ -49,10 +49,11 @@ constexpr int kTailWhole = 2;
 // page's architecture figure), entry j stands for tokens j*ratio ..
 // j*ratio + ratio - 1 and exists once the last of them has arrived, so the
 // visible entries are 0 .. (t + 1) / ratio - 1; -1 when none is complete yet.
-// Ratio 1 (or 0, the default) is one entry per token.
+// Ratio 1 (or 0, the default) is one entry per token.  Token positions are
+// >= 0 and may reach INT32_MAX with large ratios, so t + 1 is taken unsigned.
 __host__ __device__ inline int main_pos(int t, int ratio)
 {
-    return ratio > 1 ? (t + 1) / ratio - 1 : t;
+    return ratio > 1 ? (int)(((uint32_t)t + 1u) / (uint32_t)ratio) - 1 : t;
 }
 
 // Blocks eligible for a query whose last visible entry is t: every block
