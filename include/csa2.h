@@ -169,7 +169,8 @@ int32_t csa2_workspace_init(void *ws, size_t bytes, void *stream);
  * is complete ((j+1)*B <= T):
  *     k_blk[s][j][c] = round_half_even(mean over p in [jB, jB+B) of k_idx[s][p][c])
  *   k_idx : device int8 [n_seq][T][d_idx]
- *   k_blk : device int8 [n_seq][T/B][d_idx]  (only blocks in range are written)
+ *   k_blk : device int8 [n_seq][T/B][d_idx]  (only blocks in range are written;
+ *           NULL allowed when T < B, i.e. no block is complete)
  * A Full layer builds all blocks once (prefill) and, in decode, the block that
  * the newest token completes.  Incomplete blocks are never stored: the
  * selection calls compute the key of a query's own block from k_idx. */
@@ -216,7 +217,8 @@ int32_t csa2_append_tokens(const csa2_cfg *cfg, int32_t n_new, const int32_t *se
  *   q_idx   : device int8  [n_q][d_idx]
  *   q_seq, q_pos : device int32 [n_q]
  *   k_idx   : device int8  [n_seq][T][d_idx]
- *   k_blk   : device int8  [n_seq][T/B][d_idx], blocks < t/B filled
+ *   k_blk   : device int8  [n_seq][T/B][d_idx], blocks < t/B filled (NULL
+ *             allowed when T < B: no block is complete)
  *   blk_ids : device int32 [n_q][P] out: pooled block ids ascending, then -1;
  *             may be NULL when every pool is the whole prefix ((T-1)/B + 1 <=
  *             P): the pool of row i is then blocks 0 .. blk_cnt[i]-1 and no id

@@ -129,6 +129,19 @@ def test_index_blocks_argument_errors(B):
     assert _index_call(B, cfg, T=0) == 2
     assert _index_call(B, cfg, n_q=-1) == 2
     assert _index_call(B, cfg, n_q=0) == 0               # nothing to do, nothing launched
+    # a cache shorter than one block has no block key: k_blk may be NULL
+    # (checked with a misaligned q_seq, which fails right after the pointer
+    # checks, so nothing is launched)
+    assert _index_call(B, cfg, k_blk=None, T=7, q_seq=FAKE + 2) == 5
+    assert _index_call(B, cfg, k_blk=None, T=8, q_seq=FAKE + 2) == 1
+
+
+def test_block_keys_of_a_cache_without_a_complete_block(B):
+    P = ctypes.c_void_p
+    f = lambda T, k_blk: B._lib.csa2_build_block_keys(ctypes.byref(B.Cfg().c()), P(FAKE), 1, T, 0, 1 << 20,
+                                                      P(k_blk), None)
+    assert f(7, None) == 0          # T < B: nothing to write, nothing launched
+    assert f(8, None) == 1
 
 
 def test_layer_group_checks_every_stage_before_launching(B):

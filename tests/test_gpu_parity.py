@@ -635,6 +635,24 @@ def test_compressed_decode_past_the_fused_limit(lib):
     check(lib, cfg, seed=52)
 
 
+def test_compressed_reindex_and_token_only_reindex_decode(lib):
+    """Reindex and token-only Reindex layers over compressed caches (ratio
+    3): fresh pool and Top-K, and a fresh Top-K over the shared pool, each
+    followed by a Reuse layer, in the fused layer group."""
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=3, ctx=24002, pool=256, top_k=300, window=64,
+                   layers=("full", "reuse", "reindex", "reuse", "reindex_tokens", "reuse"), ratio=3)
+    check(lib, cfg, seed=60)
+
+
+def test_compressed_reindex_and_token_only_reindex_prefill(lib):
+    """The same layer kinds over a compressed 1,201-token prompt (ratio 2,
+    pool below the eligible blocks): separate block pass, pool selection and
+    token Top-K launches."""
+    cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=1201, pool=40, top_k=96, window=48,
+                   layers=("full", "reindex", "reuse", "reindex_tokens", "reuse"), ratio=2)
+    check(lib, cfg, seed=61)
+
+
 @pytest.mark.parametrize("tail", [W.TAIL_VISIBLE, W.TAIL_EXCLUDE, W.TAIL_WHOLE])
 def test_compressed_prefill_block_pass(lib, tail):
     """Every token of a 1,501-token prompt at ratio 3 (500 entries) with a pool

@@ -4,8 +4,9 @@ parity.py).  The draws span the sizes the library accepts: blocks of 1 to 16
 tokens, pools smaller or larger than the eligible blocks, Top-K from 0 to
 over 500, windows from 0 to 200, d_idx 32/64, one or two head groups, fp32
 with D = 64 (generic kernel) and bf16 with D = 128, the three tail readings,
-decode batches and prompts, and layer patterns with Reuse, Reindex,
-token-only Reindex, window-only layers and several Full layers; every
+decode batches and prompts, layer patterns with Reuse, Reindex,
+token-only Reindex, window-only layers and several Full layers, and about
+one case in four with compressed main-KV (2 to 8 tokens per entry); every
 fourth case draws int8 values in [-2, 2] so that scores tie often."""
 import numpy as np
 import pytest
@@ -40,11 +41,18 @@ def random_cfg(k: int):
     layers = PATTERNS[int(rng.integers(0, len(PATTERNS)))]
     # a window-only layer, or K = 0, needs a window (W = 0 is rejected there)
     Wn = int(rng.integers(0 if K > 0 and "swa" not in layers else 1, 201))
+    d_idx = int(rng.choice([32, 64]))
+    H = 16 if fp32 else int(rng.choice([16, 32]))
+    tail = int(rng.integers(0, 3))
+    # drawn last, so the draws above stay those of the uncompressed sweep;
+    # compressed main-KV needs a window for queries before the first entry
+    ratio = int(rng.choice([2, 3, 4, 8])) if rng.random() < 0.25 else 1
+    if ratio > 1:
+        Wn = max(Wn, 1)
     return W.scaled(W.CONFIGS["decode_full_32k" if decode else "prefill_8k"],
                     name=f"sweep{k}", n_seq=n_seq, ctx=ctx, block=B, pool=P, top_k=K, window=Wn,
-                    d_idx=int(rng.choice([32, 64])), n_heads=16 if fp32 else int(rng.choice([16, 32])),
-                    head_dim=64 if fp32 else 128, dtype="f32" if fp32 else "bf16", layers=layers,
-                    tail=int(rng.integers(0, 3)))
+                    d_idx=d_idx, n_heads=H, head_dim=64 if fp32 else 128, dtype="f32" if fp32 else "bf16",
+                    layers=layers, tail=tail, ratio=ratio)
 
 
 @pytest.fixture(scope="module")
@@ -54,13 +62,13 @@ def pipeline():
     return pl
 
 
-@pytest.mark.parametrize("k", range(48))
+@pytest.mark.parametrize("k", range(64))
 def test_random_configuration_matches_the_oracle(pipeline, k):
     cfg = random_cfg(k)
     ties = k % 4 == 3                      # narrow int8 draws: long runs of equal scores
     print(f"case {cfg.name}: decode={cfg.decode} S={cfg.n_seq} T={cfg.ctx} B={cfg.block} P={cfg.pool} "
           f"K={cfg.top_k} W={cfg.window} d={cfg.d_idx} H={cfg.n_heads} D={cfg.head_dim} {cfg.dtype} "
-          f"tail={cfg.tail} layers={cfg.layers} ties={ties}", flush=True)
+          f"tail={cfg.tail} ratio={cfg.ratio} layers={cfg.layers} ties={ties}", flush=True)
     wl = W.generate(cfg, seed=9000 + k, int_range=(-2, 2) if ties else (-127, 127))
     dw = pipeline.upload(wl)
     pipeline.build_cache(dw)

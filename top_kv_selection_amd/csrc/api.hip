@@ -173,7 +173,9 @@ int32_t do_index(const csa2_cfg *c, int32_t n_q, const int8_t *q_idx, const int3
 {
     const SelectPlan pl = plan_index(n_q, T, c->block, c->pool, c->d_idx);
     // the ids may be left unstored only where every pool is the whole prefix
-    if (!q_idx || !q_seq || !q_pos || !k_idx || !k_blk || !blk_cnt || (!blk_ids && !pl.all)) return CSA2_E_NULL;
+    // with no complete block (T < B) k_blk is empty and may be NULL: no kernel reads or writes it
+    if (!q_idx || !q_seq || !q_pos || !k_idx || (!k_blk && T / c->block > 0) || !blk_cnt || (!blk_ids && !pl.all))
+        return CSA2_E_NULL;
     if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(k_blk) || !aligned4(q_seq) ||
         !aligned4(q_pos) || !aligned4(blk_ids) || !aligned4(blk_cnt))
         return CSA2_E_ALIGN;
@@ -316,9 +318,9 @@ FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
 int32_t do_block_keys(const csa2_cfg *c, const int8_t *k_idx, int32_t n_seq, int32_t T,
                       int32_t blk_begin, int32_t blk_end, int8_t *k_blk, hipStream_t st, bool launch)
 {
-    if (!k_idx || !k_blk) return CSA2_E_NULL;
+    const int nblk = T / c->block;   // no complete block: k_blk is empty and may be NULL
+    if (!k_idx || (!k_blk && nblk > 0)) return CSA2_E_NULL;
     if (!aligned16(k_idx) || !aligned16(k_blk)) return CSA2_E_ALIGN;
-    const int nblk = T / c->block;
     blk_begin = std::max(blk_begin, 0);
     blk_end = std::min(blk_end, nblk);
     if (!launch || blk_begin >= blk_end) return CSA2_OK;
