@@ -113,12 +113,13 @@ class Config:
 
     @property
     def swa_first(self) -> int:
-        """First position held by the per-layer sliding-window K/V rows."""
-        return self.ctx - self.window if self.decode else 0
+        """First position held by the per-layer sliding-window K/V rows (decode:
+        the last `window` positions, or every position of a shorter context)."""
+        return max(self.ctx - self.window, 0) if self.decode else 0
 
     @property
     def swa_len(self) -> int:
-        return self.window if self.decode else self.ctx
+        return min(self.window, self.ctx) if self.decode else self.ctx
 
     def groups(self):
         """Split the layer list into (mode, [layers]) groups: an indexing or
