@@ -14,9 +14,11 @@ reports it under the key ``prefill``.
 Inputs are resident in HBM before timing starts.  Steps rotate over R device
 replicas of the caches (each with fresh queries) so that the working set of
 consecutive steps is not served from the 256 MB last-level cache.  Steps are
-replayed from HIP graphs (captured through torch on the stream the library
-launches on), each graph replayed once before the timed region, so host
-launch overhead and first-replay costs are not timed.
+replayed from HIP graphs of at least 32 steps (whole cycles over the
+replicas; captured through torch on the stream the library launches on), each
+graph replayed once before the timed region, so host launch overhead and
+first-replay costs are not timed, and the cost of a replay boundary (several
+microseconds) is shared by many steps.
 
 Per-kernel durations come from the library's own timing hook
 (csa2_profile_begin): after the timed region, steps run eagerly on the same
@@ -25,7 +27,8 @@ kernel's execution interval.  ``roofline`` is the kernel of the step with the
 largest time per step, its algorithmic bytes (decode) or operations (prefill)
 per launch over its average duration; ``roofline_step`` is the whole step's
 algorithmic work over the step time.  ``launch_floor_us`` is the time per step
-of a graph holding as many near-empty launches as the step has kernels.
+of graphs as long as the timed ones holding as many near-empty launches per
+step as the step has kernels.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -72,7 +75,10 @@ def measured_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_seconds):
+kGraphSteps = 32    # default steps per replayed graph
+
+
+def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_seconds, graph_steps=None):
     import numpy as np
     import torch
 
@@ -115,25 +121,32 @@ def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_sec
     own = [dws[k * RS:(k + 1) * RS] for k in range(NS)]
     step_graphs = [dict() for _ in range(NS)]
 
+    # steps per graph: whole cycles over the stream's replicas, at least
+    # kGraphSteps (the order of the replicas is the same whatever the graph
+    # length; a replay boundary costs several microseconds, which a graph of
+    # only a few steps would add to each step)
+    G = RS * max(1, -(-(graph_steps or kGraphSteps) // RS))
+
     def graphs_for(n):
-        """Graphs for n steps per stream: full cycles over the stream's replicas
-        plus one shorter tail; every new graph is replayed once."""
+        """Graphs for n steps per stream: graphs of G steps (cycles over the
+        stream's replicas) plus one shorter tail; every new graph is replayed
+        once."""
         for k in range(NS):
-            for m in (RS if n >= RS else 0, n % RS):
+            for m in (G if n >= G else 0, n % G):
                 if m and m not in step_graphs[k]:
-                    step_graphs[k][m] = capture(pipeline.run, own[k][:m], side[k])
+                    step_graphs[k][m] = capture(pipeline.run, [own[k][j % RS] for j in range(m)], side[k])
                     step_graphs[k][m].replay()
         torch.cuda.synchronize()
 
     def run_steps(n_total):
         n = n_total // NS
-        full, rest = divmod(n, RS)
+        full, rest = divmod(n, G)
         main = torch.cuda.current_stream()
         for k in range(NS):
             side[k].wait_stream(main)
             with torch.cuda.stream(side[k]):
                 for _ in range(full):
-                    step_graphs[k][RS].replay()
+                    step_graphs[k][G].replay()
                 if rest:
                     step_graphs[k][rest].replay()
         for k in range(NS):
@@ -176,17 +189,17 @@ def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_sec
         for _ in range(n_empty):
             B.csa2_workspace_init(tiny[:4])
 
-    g_empty = capture(empty_step, list(range(R)))
+    g_empty = capture(empty_step, list(range(G)))   # graphs as long as the step graphs
     g_empty.replay()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = max(1, steps // R)
+    reps = max(1, steps // G)
     s.record()
     for _ in range(reps):
         g_empty.replay()
     e.record()
     torch.cuda.synchronize()
-    floor_us = s.elapsed_time(e) * 1e3 / (reps * R)
+    floor_us = s.elapsed_time(e) * 1e3 / (reps * G)
     log(f"{name}: {n_empty} near-empty launches per step take {floor_us:.2f} us in a graph")
 
     # ---- rooflines
@@ -304,6 +317,9 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="one workload only (default: decode_group_128k, plus prefill_8k under 'prefill')")
     ap.add_argument("--profile-rounds", type=int, default=2, help="eager passes over the replicas with kernel timing")
+    ap.add_argument("--graph-steps", type=int, default=None,
+                    help="steps per replayed graph, rounded up to whole cycles over the replicas "
+                         f"(default {kGraphSteps})")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -340,7 +356,8 @@ def main():
     warmup = args.warmup if args.warmup is not None else (320 if cfg.decode else 20)
     replicas = args.replicas if args.replicas is not None else (32 if cfg.decode else 2)
     cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
-    res = run_workload(main_name, steps, warmup, replicas, args.streams, args.profile_rounds, cpu_s)
+    res = run_workload(main_name, steps, warmup, replicas, args.streams, args.profile_rounds, cpu_s,
+                       args.graph_steps)
 
     extra = {}
     if args.workload is None:
