@@ -46,7 +46,7 @@ METRIC = "sparse-attn queries/sec + achieved HBM GB/s, decode at 128K ctx (1 GPU
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, MI355X
 INT8_PEAK_TOPS = 5000.0
-KERNEL_SOURCES = ["select.hip", "attend.hip", "device_common.h", "internal.h"]
+KERNEL_SOURCES = ["select.hip", "attend.hip", "single.hip", "device_common.h", "internal.h"]
 
 
 def log(msg):
@@ -78,7 +78,8 @@ def measured_traffic(kernel, workload):
 kGraphSteps = 32    # default steps per replayed graph
 
 
-def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_seconds, graph_steps=None):
+def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_seconds, graph_steps=None,
+                 single=False):
     import numpy as np
     import torch
 
@@ -113,8 +114,11 @@ def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_sec
                 fn(dw)
         return g
 
+    def step(dw):                       # one pass of the workload's layer groups
+        pipeline.run(dw, single=single)
+
     for dw in dws:                      # eager pass: every launch checked once
-        pipeline.run(dw)
+        step(dw)
     torch.cuda.synchronize()
     RS = R // NS
     side = [torch.cuda.Stream() for _ in range(NS)]
@@ -134,7 +138,7 @@ def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_sec
         for k in range(NS):
             for m in (G if n >= G else 0, n % G):
                 if m and m not in step_graphs[k]:
-                    step_graphs[k][m] = capture(pipeline.run, [own[k][j % RS] for j in range(m)], side[k])
+                    step_graphs[k][m] = capture(step, [own[k][j % RS] for j in range(m)], side[k])
                     step_graphs[k][m].replay()
         torch.cuda.synchronize()
 
@@ -171,7 +175,7 @@ def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_sec
     n_prof = profile_rounds * R
     B.csa2_profile_begin("", 64 * n_prof)
     for k in range(n_prof):
-        pipeline.run(dws[k % R])
+        step(dws[k % R])
     recs = B.csa2_profile_end()
     per = {}
     for kname, ms in recs:
@@ -204,6 +208,8 @@ def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_sec
 
     # ---- rooflines
     work = pipeline.kernel_work(cfg)   # kernel -> (unit, algorithmic amount per step)
+    if single:   # one kernel does the work of the layer group's four
+        work = {"k_decode_single": ("bytes", sum(a for u, a in work.values() if u == "bytes"))}
     kernels = {}
     for kname, d in sorted(per.items(), key=lambda kv: -kv[1]["ms"]):
         launches_per_step = d["launches"] / n_prof
@@ -290,6 +296,7 @@ def run_workload(name, steps, warmup, replicas, streams, profile_rounds, cpu_sec
                    "queries_per_step": n_queries, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
                    "d_idx": cfg.d_idx, "block": cfg.block, "pool": cfg.pool, "top_k": cfg.top_k,
                    "window": cfg.window, "ratio": cfg.ratio, "replicas": R, "streams": NS,
+                   "single_launch": bool(single),
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "roofline_step": step,
@@ -317,6 +324,8 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="one workload only (default: decode_group_128k, plus prefill_8k under 'prefill')")
     ap.add_argument("--profile-rounds", type=int, default=2, help="eager passes over the replicas with kernel timing")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="run Full/Reindex layer groups through csa2_layer_group_single (one launch each)")
     ap.add_argument("--graph-steps", type=int, default=None,
                     help="steps per replayed graph, rounded up to whole cycles over the replicas "
                          f"(default {kGraphSteps})")
@@ -357,7 +366,7 @@ def main():
     replicas = args.replicas if args.replicas is not None else (32 if cfg.decode else 2)
     cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
     res = run_workload(main_name, steps, warmup, replicas, args.streams, args.profile_rounds, cpu_s,
-                       args.graph_steps)
+                       args.graph_steps, args.single_launch)
 
     extra = {}
     if args.workload is None:

@@ -321,6 +321,34 @@ int32_t csa2_layer_group(const csa2_cfg *cfg, int32_t mode, int32_t n_layers, in
                          int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* csa2_layer_group in one kernel launch (the same operation: the mode table
+ * of "CSA2 with cross-layer reuse" and the "Sparse attention" and
+ * "Hierarchical indexer" key facts of the page "DeepSeek V4.1 Flash"), for a
+ * Full or Reindex group of few decode queries, where csa2_layer_group takes
+ * its four-launch fused path (block scoring; pool selection with token
+ * scoring; token Top-K with chunked attention; merge of the chunk records).
+ * The four stages become phases of one kernel that hand over per query
+ * through counters in the workspace head (zero between calls, left zero).
+ * Arguments, outputs and workspace size are those of csa2_layer_group and
+ * the results are identical to its; a call outside that regime (another mode,
+ * many queries, or an attention plan without key-list chunks) returns
+ * CSA2_E_UNSUPPORTED, a workspace too small for the fused path
+ * CSA2_E_WORKSPACE.  The launch is cooperative (all workgroups resident)
+ * unless the stream is capturing a graph; a capture records an ordinary
+ * launch sized to what the device holds at once, and must not be replayed
+ * while other work occupies the device.  Every wait inside the kernel is
+ * bounded, so a replay that breaks this gives wrong output, not a hang.  On
+ * MI355X the hand-offs cost more than the kernel boundaries they replace, so
+ * csa2_layer_group stays the faster call. */
+int32_t csa2_layer_group_single(const csa2_cfg *cfg, int32_t mode, int32_t n_layers, int32_t n_q,
+                                const int8_t *q_idx, const int32_t *q_seq, const int32_t *q_pos,
+                                const int8_t *k_idx, int8_t *k_blk, int32_t blk_update_begin,
+                                int32_t n_seq, int32_t T, const void *q, const void *k_main,
+                                const void *v_main, const void *k_swa, const void *v_swa,
+                                int32_t swa_first, int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt,
+                                int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *ws,
+                                size_t ws_bytes, void *stream);
+
 /* csa2_layer_group without a workspace argument, for callers that cannot
  * allocate device memory: code under graph capture, tight serving loops,
  * harnesses that forbid allocation.  It allocates nothing (no hipMalloc,

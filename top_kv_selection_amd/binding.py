@@ -31,7 +31,7 @@ STATUS = {0: "CSA2_OK", 1: "CSA2_E_NULL", 2: "CSA2_E_SHAPE", 3: "CSA2_E_DTYPE",
 EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_profile_begin", "csa2_profile_end", "csa2_profile_record",
            "csa2_workspace_bytes", "csa2_workspace_init", "csa2_build_block_keys", "csa2_append_tokens",
            "csa2_index_blocks", "csa2_topk_tokens", "csa2_attend_group", "csa2_attend", "csa2_layer_group",
-           "csa2_layer_group_static"]
+           "csa2_layer_group_single", "csa2_layer_group_static"]
 
 
 class Csa2Error(RuntimeError):
@@ -92,6 +92,8 @@ def _load():
         "csa2_attend": (I, [C, I, P, P, P, P, P, I, I, P, P, I, I, P, P, P, P, P, Z, P]),
         "csa2_layer_group": (I, [C, I, I, I, P, P, P, P, P, I, I, I, P, P, P, P, P, I, I, P, P, P, P,
                                  P, P, P, Z, P]),
+        "csa2_layer_group_single": (I, [C, I, I, I, P, P, P, P, P, I, I, I, P, P, P, P, P, I, I, P, P, P, P,
+                                        P, P, P, Z, P]),
         "csa2_layer_group_static": (I, [C, I, I, I, P, P, P, P, P, I, I, I, P, P, P, P, P, I, I, P, P, P, P,
                                         P, P, P]),
     }
@@ -275,10 +277,12 @@ def csa2_attend(cfg: Cfg, q, q_seq, q_pos, k_main, v_main, k_swa, v_swa, swa_fir
 
 def csa2_layer_group(cfg: Cfg, mode, q_idx, q_seq, q_pos, k_idx, k_blk, blk_update_begin, q, k_main,
                      v_main, k_swa, v_swa, swa_first, blk_ids, blk_cnt, topk, topk_cnt, out, lse=None,
-                     ws=None):
+                     ws=None, single=False):
     """One CSA2 layer group: the first layer's mode (full/reindex/reuse/swa/
     reindex_tokens) picks the selection work; all layers of q [L][n_q][H][D]
-    attend with the shared indices."""
+    attend with the shared indices.  ``single`` calls csa2_layer_group_single
+    (the fused decode group as one launch)."""
+    fn = "csa2_layer_group_single" if single else "csa2_layer_group"
     mode = MODES[mode] if isinstance(mode, str) else int(mode)
     _attend_checks(cfg, q, k_main, v_main, k_swa, v_swa, out, lse, q_seq, q_pos, topk, topk_cnt, ws)
     for t, n, d in ((q_idx, "q_idx", torch.int8), (k_idx, "k_idx", torch.int8), (k_blk, "k_blk", torch.int8),
@@ -287,7 +291,7 @@ def csa2_layer_group(cfg: Cfg, mode, q_idx, q_seq, q_pos, k_idx, k_blk, blk_upda
     L, n_q = q.shape[0], q.shape[1]
     S, T = k_main.shape[0], k_main.shape[1]
     swa_len = k_swa.shape[2] if k_swa is not None else 0
-    _check("csa2_layer_group", _lib.csa2_layer_group(
+    _check(fn, getattr(_lib, fn)(
         ctypes.byref(cfg.c()), mode, L, n_q, _p(q_idx), _p(q_seq), _p(q_pos), _p(k_idx), _p(k_blk),
         int(blk_update_begin), S, T, _p(q), _p(k_main), _p(v_main), _p(k_swa), _p(v_swa), int(swa_first),
         swa_len, _p(blk_ids), _p(blk_cnt), _p(topk), _p(topk_cnt), _p(out), _p(lse), _p(ws),

@@ -305,7 +305,7 @@ FusedPlan plan_fused(const csa2_cfg *c, int n_q, int T, int n_layers)
            (f.att.chunks || f.att.keys_per_split <= kAttendRowChunk) && c->pool <= kFusedPoolLds;
     f.blk_stride = (n_elig_max + 3) / 4 * 4;
     f.tok_stride = ((long long)c->pool * c->block + 3) / 4 * 4;
-    f.head = hist_bytes(n_q);
+    f.head = hist_bytes(n_q) + single_ctr_bytes(n_q);   // block histograms, then the single launch's counters
     size_t off = 0;
     f.blk_off = off;      off += round_up((size_t)n_q * f.blk_stride * 4);
     f.tok_off = off;      off += round_up((size_t)n_q * f.tok_stride * 4);
@@ -388,7 +388,10 @@ size_t head_bound(const csa2_cfg *c, int n_q, int T)
         if (plan_index(n, T, c->block, c->pool, c->d_idx).split ||
             plan_topk(n, T, c->block, c->pool, c->top_k, c->d_idx).split)
             b = std::max(b, hist_bytes(n));
-    if (fused_possible(c, T)) b = std::max(b, hist_bytes(std::min(n_q, kTargetWorkgroups / 2 - 1)));
+    if (fused_possible(c, T)) {
+        const int n_f = std::min(n_q, kTargetWorkgroups / 2 - 1);
+        b = std::max(b, hist_bytes(n_f) + single_ctr_bytes(n_f));
+    }
     return b;
 }
 
@@ -399,8 +402,9 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
                           const void *v_main, const void *k_swa, const void *v_swa,
                           int32_t swa_first, int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt,
                           int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *ws,
-                          size_t ws_bytes, hipStream_t st, const FusedPlan &f, bool launch)
+                          size_t ws_bytes, hipStream_t st, const FusedPlan &f, bool launch, bool single)
 {
+    if (single && !f.att.chunks) return CSA2_E_UNSUPPORTED;
     // the argument checks of the separate stages (nothing launched)
     if (int32_t e = do_index(c, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, n_seq, T, blk_ids, blk_cnt,
                              ws, ws_bytes, st, false))
@@ -437,8 +441,6 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     ip.nblk = T / c->block;
     ip.ws_keys = blk_keys; ip.ws_stride = f.blk_stride; ip.ws_hist = head;
     ip.blk_ids = blk_ids; ip.blk_cnt = blk_cnt;
-    // block scoring (keys and histogram to the workspace)
-    if (int32_t e = hip_status(launch_index_blocks(ip, f.idx, c->d_idx, st, false))) return e;
 
     TopkParams tp{};
     tp.q_idx = q_idx; tp.q_seq = q_seq; tp.q_pos = q_pos; tp.k_idx = k_idx;
@@ -448,10 +450,6 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     tp.G = f.tok.G; tp.chunk = f.tok.chunk;
     tp.ws_keys = tok_keys; tp.ws_stride = f.tok_stride; tp.ws_hist = tok_hist;
     tp.topk = topk; tp.topk_cnt = topk_cnt;
-    // pool selection + token scoring in one launch (each scoring workgroup
-    // redoes the pool selection); the Top-K is taken inside the attention
-    // launch, whose writer also zeroes the block histogram
-    if (int32_t e = hip_status(launch_pool_tokens(ip, tp, c->d_idx, st))) return e;
 
     AttendParams ap{};
     ap.q = q; ap.q_seq = q_seq; ap.q_pos = q_pos; ap.k_main = k_main; ap.v_main = v_main;
@@ -464,6 +462,15 @@ int32_t fused_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int
     ap.sel_keys = tok_keys; ap.sel_stride = f.tok_stride; ap.sel_hist = tok_hist;
     ap.sel_pool = blk_ids; ap.sel_pool_cnt = blk_cnt; ap.sel_B = c->block; ap.sel_P = c->pool;
     ap.topk_out = topk; ap.topk_cnt_out = topk_cnt; ap.blk_hist_clear = head;
+    if (single)
+        return hip_status(launch_decode_single(ip, tp, ap, f.att, c->d_idx,
+                                               (uint32_t *)((char *)head + hist_bytes(n_q)), st));
+    // block scoring (keys and histogram to the workspace)
+    if (int32_t e = hip_status(launch_index_blocks(ip, f.idx, c->d_idx, st, false))) return e;
+    // pool selection + token scoring in one launch (each scoring workgroup
+    // redoes the pool selection); the Top-K is taken inside the attention
+    // launch, whose writer also zeroes the block histogram
+    if (int32_t e = hip_status(launch_pool_tokens(ip, tp, c->d_idx, st))) return e;
     return hip_status(launch_attend(ap, f.att, c->head_dim, c->dtype, st, true));
 }
 
@@ -474,7 +481,8 @@ int32_t layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int32_t n
                     int32_t blk_update_begin, int32_t n_seq, int32_t T, const void *q, const void *k_main,
                     const void *v_main, const void *k_swa, const void *v_swa, int32_t swa_first,
                     int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt, int32_t *topk, int32_t *topk_cnt,
-                    void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t st, bool launch_all)
+                    void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t st, bool launch_all,
+                    bool single = false)
 {
     if (int32_t e = check_cfg(c)) return e;
     if (int32_t e = check_sizes(n_q, n_seq, T)) return e;
@@ -492,8 +500,10 @@ int32_t layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int32_t n
             return fused_layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk,
                                      blk_update_begin, n_seq, T, q, k_main, v_main, k_swa, v_swa,
                                      swa_first, swa_len, blk_ids, blk_cnt, topk, topk_cnt, out, lse,
-                                     ws, ws_bytes, st, f, launch_all);
+                                     ws, ws_bytes, st, f, launch_all, single);
+        if (single && f.ok && ws) return CSA2_E_WORKSPACE;
     }
+    if (single) return CSA2_E_UNSUPPORTED;   // only the fused layer group has a single-launch form
     // every stage is checked before the first launch, then all are launched
     for (int pass = 0; pass < (launch_all ? 2 : 1); pass++) {
         const bool launch = pass == 1;
@@ -711,6 +721,20 @@ int32_t csa2_layer_group(const csa2_cfg *c, int32_t mode, int32_t n_layers, int3
     return layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, blk_update_begin, n_seq, T, q,
                        k_main, v_main, k_swa, v_swa, swa_first, swa_len, blk_ids, blk_cnt, topk, topk_cnt, out,
                        lse, ws, ws_bytes, (hipStream_t)stream, true);
+}
+
+int32_t csa2_layer_group_single(const csa2_cfg *c, int32_t mode, int32_t n_layers, int32_t n_q,
+                                const int8_t *q_idx, const int32_t *q_seq, const int32_t *q_pos,
+                                const int8_t *k_idx, int8_t *k_blk, int32_t blk_update_begin,
+                                int32_t n_seq, int32_t T, const void *q, const void *k_main,
+                                const void *v_main, const void *k_swa, const void *v_swa,
+                                int32_t swa_first, int32_t swa_len, int32_t *blk_ids, int32_t *blk_cnt,
+                                int32_t *topk, int32_t *topk_cnt, void *out, float *lse, void *ws,
+                                size_t ws_bytes, void *stream)
+{
+    return layer_group(c, mode, n_layers, n_q, q_idx, q_seq, q_pos, k_idx, k_blk, blk_update_begin, n_seq, T, q,
+                       k_main, v_main, k_swa, v_swa, swa_first, swa_len, blk_ids, blk_cnt, topk, topk_cnt, out,
+                       lse, ws, ws_bytes, (hipStream_t)stream, true, true);
 }
 
 int32_t csa2_layer_group_static(const csa2_cfg *c, int32_t mode, int32_t n_layers, int32_t n_q,

@@ -194,6 +194,12 @@ hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t st);
 // histogram) and token scoring in one launch; ceil(P / pool_tokens_slots)
 // workgroups per query.  Requires n_elig_max <= kFusedEligMax and P <= kFusedPoolLds.
 int pool_tokens_slots(int n_q, int P, int B);
+// The fused decode layer group as one launch (single.hip): its four phases in
+// one kernel, handing over per query through counters `ctr` (single_ctr_bytes
+// of zeroed workspace, left zeroed).  Needs an attention plan with chunks.
+size_t single_ctr_bytes(int n_q);
+hipError_t launch_decode_single(const IndexParams &ip, const TopkParams &tp, const AttendParams &ap,
+                                const AttendPlan &pl, int d_idx, uint32_t *ctr, hipStream_t st);
 hipError_t launch_pool_tokens(const IndexParams &ip, const TopkParams &tp, int d_idx, hipStream_t st);
 
 }  // namespace csa2

@@ -162,15 +162,17 @@ __global__ __launch_bounds__(64) void k_append_block_keys(AppendParams p)
 constexpr int kUnroll = 4;
 constexpr int kPoolLds = 4096;      // pooled block ids staged in LDS for the emit
 
+// (the body takes its workgroup index, so that the single-launch decode
+// kernel can run it for any of its virtual workgroups)
 template <int NT, int DIDX, bool SPLIT>
-__global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
+__device__ __forceinline__ void index_blocks_body(const IndexParams &p, int bid)
 {
     constexpr int LPR = DIDX / 16, RPP = NT / LPR, IPT = kLdsKeys / NT;
     __shared__ uint32_t s_keys[SPLIT ? 4 : kLdsKeysPadded];
     __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
     __shared__ uint32_t s_sm[NT / 64 + 4];
-    const int q = blockIdx.x / p.G;   // a query's workgroups are consecutive: spread over the XCDs
-    const int g = blockIdx.x % p.G;
+    const int q = bid / p.G;   // a query's workgroups are consecutive: spread over the XCDs
+    const int g = bid % p.G;
     const int tid = threadIdx.x, part = tid % LPR;
     const int s = p.q_seq[q], t = main_pos(p.q_pos[q], p.ratio);   // last visible entry (-1: none)
     const int jt = t / p.B, n_elig = eligible_blocks(t, p.B, p.tail);
@@ -256,6 +258,12 @@ __global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
     const uint32_t chosen = compact_regs<NT, IPT>(k, th, emit, s_sm);
     for (int o = (int)chosen + tid; o < p.P; o += NT) ids[o] = -1;
     if (tid == 0) p.blk_cnt[q] = (int32_t)min(chosen, cap);
+}
+
+template <int NT, int DIDX, bool SPLIT>
+__global__ __launch_bounds__(NT) void k_index_blocks(IndexParams p)
+{
+    index_blocks_body<NT, DIDX, SPLIT>(p, (int)blockIdx.x);
 }
 
 // Pools when every eligible block of every query fits (n_elig <= P for the
@@ -479,16 +487,17 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(TopkParams p)
 constexpr int kPoolTokCand = 512;
 constexpr int kPoolTokMaxWorkgroups = 256;   // one 1,024-thread workgroup per CU
 
+// (G workgroups per query; the body takes its workgroup index)
 template <int DIDX, int IPT>
-__global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams ip, TopkParams tp, int n_slots)
+__device__ __forceinline__ void pool_tokens_body(const IndexParams &ip, const TopkParams &tp, int n_slots, int G,
+                                                 int bid)
 {
     constexpr int NT = kSelectWideThreads;
     constexpr int LPR = DIDX / 16, RPP = NT / LPR;
     __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHist2Words];
     __shared__ int32_t s_pool[kFusedPoolLds];
     __shared__ uint32_t s_sm[NT / 64 + 4];
-    const int G = (int)gridDim.x / ip.n_q;
-    const int q = (int)blockIdx.x / G, g = (int)blockIdx.x % G;
+    const int q = bid / G, g = bid % G;
     const int tid = threadIdx.x, part = tid % LPR;
     const int B = ip.B, P = ip.P;
 
@@ -560,6 +569,12 @@ __global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams 
     }
     lds_barrier();
     flush_hist<NT>(s_hist, tp.ws_hist + (size_t)q * kRadixBins);
+}
+
+template <int DIDX, int IPT>
+__global__ __launch_bounds__(kSelectWideThreads) void k_pool_tokens(IndexParams ip, TopkParams tp, int n_slots)
+{
+    pool_tokens_body<DIDX, IPT>(ip, tp, n_slots, (int)gridDim.x / ip.n_q, (int)blockIdx.x);
 }
 
 template <int NT>

@@ -162,8 +162,9 @@ def step_update_begin(dw: DeviceWorkload) -> int:
     return 0
 
 
-def run(dw: DeviceWorkload):
-    """One pass of every layer group, in model order."""
+def run(dw: DeviceWorkload, single: bool = False):
+    """One pass of every layer group, in model order.  ``single``: Full and
+    Reindex groups go through csa2_layer_group_single (one launch each)."""
     begin = step_update_begin(dw)
     for g, grp in enumerate(dw.groups):
         src = grp.index_of
@@ -174,7 +175,7 @@ def run(dw: DeviceWorkload):
             dw.lcfg, grp.mode, grp.q_idx, dw.q_seq, dw.q_pos, k_idx, k_blk, begin, grp.q,
             k_main, v_main, grp.k_swa, grp.v_swa, dw.cfg.swa_first,
             dw.blk_ids.get(pool), dw.blk_cnt.get(pool), dw.topk.get(idx), dw.topk_cnt.get(idx),
-            grp.out, grp.lse, dw.ws)
+            grp.out, grp.lse, dw.ws, single=single and grp.mode in ("full", "reindex"))
 
 
 def outputs(dw: DeviceWorkload):
