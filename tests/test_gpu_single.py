@@ -73,3 +73,32 @@ def test_single_launch_refuses_other_regimes(lib):
     with pytest.raises(B.Csa2Error) as e:
         pipeline.run(dw, single=True)
     assert e.value.status == 4
+
+
+def test_single_launch_in_a_graph(lib):
+    """Captured in a graph (an ordinary launch of the single kernel), replayed
+    three times with eager work and synchronisation between the replays:
+    every replay equals the eager call bitwise, so the counters are left zero
+    by every replay too."""
+    B, pipeline = lib
+    cfg = W.scaled(W.CONFIGS["decode_group_128k"], n_seq=4, ctx=40000, layers=("full", "reuse", "reuse"))
+    print(f"case single launch in a graph S={cfg.n_seq} T={cfg.ctx}", flush=True)
+    wl = W.generate(cfg, seed=72)
+    dw = pipeline.upload(wl)
+    pipeline.build_cache(dw)
+    pipeline.run(dw, single=True)
+    torch.cuda.synchronize()
+    eager = _flat(pipeline.outputs(dw))
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        pipeline.run(dw, single=True)
+    for rep in range(3):
+        for grp in dw.groups:            # eager work between replays: clobber the outputs
+            grp.out.zero_()
+            grp.lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(_flat(pipeline.outputs(dw)), eager):
+            assert np.array_equal(a, b), f"replay {rep} differs from the eager call"
