@@ -111,7 +111,8 @@ def test_decode_fewer_candidates_than_k(lib):
 
 def test_prefill_scaled_all_rows(lib):
     """Every position of a 700-token prompt: own partial blocks, pool active
-    past 8*64 tokens, K larger than the prefix for early rows."""
+    past 8*64 tokens, K larger than the prefix for early rows; the window-only
+    layer's 700 items take the row kernel (too few for the shared-window one)."""
     cfg = W.scaled(W.CONFIGS["prefill_8k"], ctx=700, pool=64, top_k=96, window=40,
                    layers=("full", "reuse", "swa"))
     check(lib, cfg, seed=25)
@@ -158,6 +159,14 @@ def test_encoder_pattern_scaled_all_rows(lib):
 
 def test_encoder_prefill_8k_all_rows(lib):
     check(lib, W.CONFIGS["encoder_prefill_8k"])
+
+
+def test_one_round_of_attention_workgroups(lib):
+    """256 (query, layer) items, one round of one attention workgroup per
+    item (the MFMA kernel): 64 replayed prompt positions through Full + 3
+    Reuse.  One item more takes the row kernel (the replay test below)."""
+    cfg = W.scaled(W.CONFIGS["decoder_replay_8k"], replay=64, layers=("full", "reuse", "reuse", "reuse"))
+    check(lib, cfg, seed=62)
 
 
 def test_decoder_replay_8k(lib):
@@ -463,9 +472,9 @@ def test_full_mode_stores_the_block_a_query_completes(lib):
     ("decode_full_32k", dict(n_seq=3, ctx=5001, pool=300, top_k=700, window=100)),
     ("decode_full_32k", dict(n_seq=2, ctx=900, pool=2048)),            # pool covers every block
     ("decode_group_128k", dict(n_seq=3, ctx=12000, pool=256, layers=("reindex", "reuse"))),
-    # 48 queries x 6 layers: enough items for one attention workgroup per
-    # (query, layer) instead of key-list chunks
-    ("decode_group_128k", dict(n_seq=48, ctx=3000, pool=128)),
+    # 42 queries x 6 layers = 252 items: the most the chunked attention of
+    # the fused layer group takes
+    ("decode_group_128k", dict(n_seq=42, ctx=3000, pool=128)),
 ])
 def test_fused_layer_group_equals_separate_calls(lib, name, kw):
     """The layer-group call (fused decode launches) and the separate calls

@@ -1430,7 +1430,8 @@ hipError_t launch_attend(const AttendParams &p0, const AttendPlan &pl, int D, in
     if (p0.n_q <= 0 || p0.n_layers <= 0) return hipSuccess;
     AttendParams p = p0;
     const bool rows_fit = (long long)p.T * 256 < INT32_MAX && (long long)p.swa_len * 256 < INT32_MAX;
-    if (pl.rows && !fused_select && p0.topk == nullptr) {
+    if (pl.rows && !fused_select && p0.topk == nullptr &&
+        (long long)p.n_q * p.n_layers * (p.H / 16) >= kWinItemsMin) {
         // window-only layer with many queries: shared windows in LDS
         const long long n_wg = (long long)((p.n_q + kWinQ - 1) / kWinQ) * (p.H / 16) * p.n_layers;
         launch("k_attend_window", k_attend_window, dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(kWinWaves * 64), st, p);

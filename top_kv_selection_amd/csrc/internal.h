@@ -183,7 +183,12 @@ hipError_t launch_topk_tokens(const TopkParams &p, const SelectPlan &plan, int d
 hipError_t launch_attend(const AttendParams &p, const AttendPlan &plan, int D, int dtype,
                          hipStream_t st, bool fused_select = false);
 
-constexpr int kRowItemsMin = 1024;      // (query, layer, head group) items that take the row kernel
+// (query, layer, head group) items that take the row kernel: more than one
+// round of the one-workgroup-per-item MFMA kernel (a workgroup per CU), whose
+// second round doubles its time (384 items: 310.9 against 222.9 us per replay
+// step; at 256 items the MFMA kernel is 1.5-3 % faster)
+constexpr int kRowItemsMin = kTargetWorkgroups / 2 + 1;
+constexpr int kWinItemsMin = 1024;      // window-only items that take the shared-window kernel (32 queries a workgroup)
 constexpr int kDenseMaxT = 16384;       // longest context of the dense (MFMA tile) token Top-K
 constexpr int kDenseMinQueries = 256;   // queries per call below which the per-query kernels run
 constexpr int kAttendRowChunk = 2048;   // key-list entries one attention workgroup stages at once

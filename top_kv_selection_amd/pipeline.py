@@ -326,9 +326,9 @@ def kernel_work(cfg: Config) -> dict:
                     n_q * (P * 4 + 4 + K * 4 + 4 + sel * 2 * D * esz + len(layers) * per_layer))
         return work
     # prompts: the attention kernel follows the number of (query, layer, head
-    # group) items of a call (few: key-list chunks; a few hundred: one
-    # workgroup per item; many: one wave per item, or the shared-window kernel
-    # for window-only layers), and the token Top-K is the dense MFMA kernel
+    # group) items of a call (fewer than 256: key-list chunks; 256: one
+    # workgroup per item; more: one wave per item, or the shared-window kernel
+    # for window-only layers of 1,024 items or more), and the token Top-K is the dense MFMA kernel
     # when every pool is the whole prefix and the call has enough queries
     ops = algorithmic_ops(cfg)
     hg = max(1, H // 16)
@@ -336,10 +336,12 @@ def kernel_work(cfg: Config) -> dict:
         items = cfg.n_q * len(layers) * hg
         if items < 256:
             kernel = "k_attend_chunks"
-        elif items < 1024:
+        elif items == 256:
             kernel = "k_attend_mfma"
+        elif mode == "swa" and items >= 1024:
+            kernel = "k_attend_window"
         else:
-            kernel = "k_attend_window" if mode == "swa" else "k_attend_rows"
+            kernel = "k_attend_rows"
         add(kernel, "bf16_flops", flops)
     dense = whole_prefix_pools(cfg) and cfg.main_len <= 16384 and cfg.n_q >= 256
     for n in ops["topk_tokens"]:
