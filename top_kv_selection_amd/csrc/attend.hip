@@ -39,6 +39,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // each query row once, and keeping those rows out of L2 and the MALL leaves
 // room for the K/V rows that other workgroups gather again.
 typedef int i32x4_nt __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));   // 8-byte nontemporal store
 __device__ __forceinline__ bf16x8_t load_nt_bf16x8(const uint16_t *src)
 {
     return __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(reinterpret_cast<const i32x4_nt *>(src)));
@@ -589,21 +590,22 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
     // Each wave walks a few items, wave0, wave0 + stride, ...  Workgroup b
-    // runs on XCD b % 8 (round-robin dispatch) and the items of an XCD are
-    // contiguous ranges, so neighbouring queries, whose windows overlap,
-    // share one L2.
+    // runs on XCD b % 8 (round-robin dispatch).
     //  * Calls that fit one round of the grid (the chip's workgroups, each
-    //    wave taking up to kRowItemsPerWave items): wave v of the XCD-ordered
-    //    grid takes items v, v + n_waves, ..., so every wave sees the whole
-    //    range of prefix lengths.
+    //    wave taking up to kRowItemsPerWave items): wave v = 4 b + w takes
+    //    items v, v + n_waves, ..., so every wave sees the whole range of
+    //    prefix lengths, and the short early prefixes of a prompt are dealt
+    //    to every XCD in turn rather than all to the first (whose waves
+    //    would then finish early while the others still run).
     //  * Larger calls: workgroup b takes a block of kRowWaves * kRowBlockItems
-    //    consecutive items (wave w its items w, w + kRowWaves, ...), and the
-    //    blocks run in rounds that the hardware dispatch balances over the
-    //    CUs.
+    //    consecutive items (wave w its items w, w + kRowWaves, ...), the
+    //    blocks of an XCD contiguous so that neighbouring queries, whose
+    //    windows overlap, share one L2, and the blocks run in rounds that
+    //    the hardware dispatch balances over the CUs.
     const int per_xcd = gridDim.x / 8;
     const int slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     const int n_waves = gridDim.x * kRowWaves;
-    const int wave0 = p.row_blocks ? slot * kRowWaves * kRowBlockItems + w : slot * kRowWaves + w;
+    const int wave0 = p.row_blocks ? slot * kRowWaves * kRowBlockItems + w : (int)blockIdx.x * kRowWaves + w;
     const int stride = p.row_blocks ? kRowWaves : n_waves;
     const int HG = p.H / 16;
     const int n_items = p.n_q * p.n_layers * HG;
@@ -850,13 +852,15 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
         // acc[m][ii] = O[head r16][dim 16m + 4g + ii] (unnormalised)
         const float L = sum_groups(l_part);
         const float inv = 1.f / L;
+        // nontemporal stores: the output is written once, and keeping it out
+        // of L2 leaves room for the K/V rows other waves gather
         const size_t row_id = ((size_t)cur.l * p.n_q + cur.i) * p.H + cur.hg * 16 + r16;
         uint16_t *orow = (uint16_t *)p.out + row_id * 128;
 #pragma unroll
         for (int m = 0; m < 8; m++) {
             const uint32_t lo = (uint32_t)f32_to_bf16(acc[m][0] * inv) | ((uint32_t)f32_to_bf16(acc[m][1] * inv) << 16);
             const uint32_t hi = (uint32_t)f32_to_bf16(acc[m][2] * inv) | ((uint32_t)f32_to_bf16(acc[m][3] * inv) << 16);
-            *reinterpret_cast<uint2 *>(orow + 16 * m + 4 * g) = make_uint2(lo, hi);
+            __builtin_nontemporal_store(u32x2_nt{lo, hi}, reinterpret_cast<u32x2_nt *>(orow + 16 * m + 4 * g));
         }
         if (p.lse && g == 0) p.lse[row_id] = (m_run + log2f(L)) * kLn2;
 
