@@ -39,7 +39,6 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // each query row once, and keeping those rows out of L2 and the MALL leaves
 // room for the K/V rows that other workgroups gather again.
 typedef int i32x4_nt __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));   // 8-byte nontemporal store
 __device__ __forceinline__ bf16x8_t load_nt_bf16x8(const uint16_t *src)
 {
     return __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(reinterpret_cast<const i32x4_nt *>(src)));
@@ -856,11 +855,25 @@ __global__ __launch_bounds__(kRowWaves * 64) void k_attend_rows(AttendParams p)
         // of L2 leaves room for the K/V rows other waves gather
         const size_t row_id = ((size_t)cur.l * p.n_q + cur.i) * p.H + cur.hg * 16 + r16;
         uint16_t *orow = (uint16_t *)p.out + row_id * 128;
+        // Lanes of groups g and g ^ 1 swap halves (v_permlane16_swap swaps the
+        // odd 16-lane rows of its first operand with the even rows of its
+        // second), so that each lane holds 8 consecutive dims, of dim tile 2j
+        // (even g) or 2j + 1 (odd g), and each store writes 64 contiguous
+        // bytes of every row.
 #pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const uint32_t lo = (uint32_t)f32_to_bf16(acc[m][0] * inv) | ((uint32_t)f32_to_bf16(acc[m][1] * inv) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16(acc[m][2] * inv) | ((uint32_t)f32_to_bf16(acc[m][3] * inv) << 16);
-            __builtin_nontemporal_store(u32x2_nt{lo, hi}, reinterpret_cast<u32x2_nt *>(orow + 16 * m + 4 * g));
+        for (int j = 0; j < 4; j++) {
+            uint32_t lo[2], hi[2];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int m = 2 * j + h;
+                lo[h] = (uint32_t)f32_to_bf16(acc[m][0] * inv) | ((uint32_t)f32_to_bf16(acc[m][1] * inv) << 16);
+                hi[h] = (uint32_t)f32_to_bf16(acc[m][2] * inv) | ((uint32_t)f32_to_bf16(acc[m][3] * inv) << 16);
+            }
+            const auto sl = __builtin_amdgcn_permlane16_swap(lo[0], lo[1], false, false);
+            const auto sh = __builtin_amdgcn_permlane16_swap(hi[0], hi[1], false, false);
+            const int dim0 = 16 * (2 * j + (g & 1)) + 4 * (g & ~1);
+            __builtin_nontemporal_store(i32x4_nt{(int)sl[0], (int)sh[0], (int)sl[1], (int)sh[1]},
+                                        reinterpret_cast<i32x4_nt *>(orow + dim0));
         }
         if (p.lse && g == 0) p.lse[row_id] = (m_run + log2f(L)) * kLn2;
 
@@ -1162,7 +1175,7 @@ void k_attend_window(AttendParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t s_k[kWinRows * kWinKStride];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[kWinRows * kWinVStride];
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[kWinWaves][16 * 256];   // each wave's first query rows
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[kWinWaves][16 * 256];   // each wave's first query rows, then its output rows
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1289,15 +1302,25 @@ void k_attend_window(AttendParams p)
     auto finish = [&](State &st, int i) {
         const float L = sum_groups(st.l_part);
         const float inv = 1.f / L;
-        const size_t row_id = ((size_t)l * p.n_q + i) * p.H + hg * 16 + r16;
-        uint16_t *orow = (uint16_t *)p.out + row_id * 128;
+        // The item's 16 output rows are contiguous (4 KB).  They go through
+        // the wave's query-row slot, which the first query's rows have left,
+        // so that each store writes four whole rows (1 KB), nontemporally
+        // (written once, they need no room in L2; with 32-byte pieces per
+        // row, nontemporal stores were slower).
+        const size_t row0 = ((size_t)l * p.n_q + i) * p.H + hg * 16;
+        uint8_t *so = s_q[w];
+        wave_lds_order();
 #pragma unroll
         for (int m = 0; m < 8; m++) {
             const uint32_t lo2 = (uint32_t)f32_to_bf16(st.acc[m][0] * inv) | ((uint32_t)f32_to_bf16(st.acc[m][1] * inv) << 16);
             const uint32_t hi2 = (uint32_t)f32_to_bf16(st.acc[m][2] * inv) | ((uint32_t)f32_to_bf16(st.acc[m][3] * inv) << 16);
-            *reinterpret_cast<uint2 *>(orow + 16 * m + 4 * g) = make_uint2(lo2, hi2);
+            *reinterpret_cast<uint2 *>(so + 256 * r16 + 32 * m + 8 * g) = make_uint2(lo2, hi2);
         }
-        if (p.lse && g == 0) p.lse[row_id] = (st.m_run + log2f(L)) * kLn2;
+        wave_lds_order();
+        uint8_t *obase = (uint8_t *)p.out + row0 * 256;
+#pragma unroll
+        for (int x = 0; x < 4; x++) __builtin_nontemporal_store(*reinterpret_cast<const i32x4_nt *>(so + 1024 * x + 16 * lane), reinterpret_cast<i32x4_nt *>(obase + 1024 * x + 16 * lane));
+        if (p.lse && g == 0) p.lse[row0 + r16] = (st.m_run + log2f(L)) * kLn2;
     };
 
     // the fast path's condition: one sequence, and the union fits one staging
