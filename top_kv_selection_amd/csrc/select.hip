@@ -1139,7 +1139,15 @@ __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_e
                 }
                 for (int o = max(cnt, c0) - c0 + lane; o < len; o += 64) row[o] = 0xffffffffu;   // -1: no entry
                 wave_lds_order();
-                for (int o = lane; o < len; o += 64) out[c0 + o] = (int32_t)row[o];
+                if ((K & 3) == 0 && (len & 3) == 0 && ((uintptr_t)p.topk & 15) == 0) {
+                    // 16 bytes a lane, nontemporal: the ids are read once, by
+                    // the attention, and need no room in L2 meanwhile
+                    for (int o = 4 * lane; o < len; o += 256)
+                        __builtin_nontemporal_store(*reinterpret_cast<const v4i32 *>(row + o),
+                                                    reinterpret_cast<v4i32 *>(out + c0 + o));
+                } else {
+                    for (int o = lane; o < len; o += 64) out[c0 + o] = (int32_t)row[o];
+                }
                 wave_lds_order();   // the stage is read before the next slots are written
             }
             if (lane == 0) p.topk_cnt[i] = cnt;
