@@ -11,16 +11,17 @@
 // has (bf16, D = 128); all of them run S^T = K Q^T and O^T += V^T P^T on
 // v_mfma_f32_16x16x32_bf16 with 16 heads as the MFMA N dimension and an fp32
 // online softmax (one head per lane column):
-//  * k_attend_chunks + k_attend_combine (few items, as in decode): the key
-//    lists are cut into 64-key chunks taken by different workgroups; a main
-//    chunk's rows are brought into LDS once for every layer of a group; each
-//    (item, chunk) writes a (max, sum, acc) record and a second launch merges
-//    an item's records;
-//  * k_attend_mfma (a few hundred items): one workgroup of 8 waves per item;
-//  * k_attend_rows (many items, as in prefill): one wave per item at a time,
+//  * k_attend_chunks + k_attend_combine (fewer than 256 items, as in
+//    decode): the key lists are cut into 64-key chunks taken by different
+//    workgroups; a main chunk's rows are brought into LDS once for every
+//    layer of a group; each (item, chunk) writes a (max, sum, acc) record and
+//    a second launch merges an item's records;
+//  * k_attend_mfma (256 items, one round of a workgroup per CU): one
+//    workgroup of 8 waves per item;
+//  * k_attend_rows (more items, as in prefill): one wave per item at a time,
 //    each wave walking up to four items;
-//  * k_attend_window (window-only layers with many queries): the windows of 32
-//    neighbouring queries staged in LDS once;
+//  * k_attend_window (window-only layers of 1,024 items or more): the windows
+//    of 32 neighbouring queries staged in LDS once;
 //  * k_attend_generic (fp32, or any H and D in {64, 128}): one wave per head,
 //    keys in sequence, fp32 online softmax on the vector ALU.
 #include <math.h>
