@@ -1320,7 +1320,9 @@ void k_attend_window(AttendParams p)
         wave_lds_order();
         uint8_t *obase = (uint8_t *)p.out + row0 * 256;
 #pragma unroll
-        for (int x = 0; x < 4; x++) __builtin_nontemporal_store(*reinterpret_cast<const i32x4_nt *>(so + 1024 * x + 16 * lane), reinterpret_cast<i32x4_nt *>(obase + 1024 * x + 16 * lane));
+        for (int x = 0; x < 4; x++)
+            __builtin_nontemporal_store(*reinterpret_cast<const i32x4_nt *>(so + 1024 * x + 16 * lane),
+                                        reinterpret_cast<i32x4_nt *>(obase + 1024 * x + 16 * lane));
         if (p.lse && g == 0) p.lse[row0 + r16] = (st.m_run + log2f(L)) * kLn2;
     };
 
